@@ -1,0 +1,375 @@
+/*
+ * oracle.c -- the decode step written out as its plain definition.
+ *
+ * TEST INFRASTRUCTURE (see oracle.h): used by the test suite, the smoke check
+ * and the benchmark's CPU baseline only.
+ *
+ * The step follows the forward() walkthrough of the "run.c 逐行解讀" page
+ * (§4, steps 1, 2a-2h and 3), cross-checked against the transformer() function
+ * of the "run.c" page and the Attention / TransformerBlock / FeedForward layers
+ * of the "LLaMA implemented in R Tensorflow and Keras" page.  Readings where the
+ * pages leave a point open:
+ *   - RMSNorm eps is added to mean(x^2) inside the square root.
+ *   - RoPE rotates adjacent pairs (2j, 2j+1) of each head by pos*theta^(-2j/hs);
+ *     q is rotated in every head, k in its n_kv_heads heads.
+ *   - query head h reads key/value head floor(h*n_kv/n_heads), i.e. the page's
+ *     h / kv_mul with kv_mul = n_heads/n_kv_heads taken as a real ratio.
+ *   - argmax returns the lowest index among equal maxima (strict '>' scan).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef ORACLE_PAGE_LITERAL
+typedef float acc_t;
+#define ACC_SQRT sqrtf
+#define ACC_EXP expf
+#else
+typedef double acc_t;
+#define ACC_SQRT sqrt
+#define ACC_EXP exp
+#endif
+
+int oracle_page_literal(void) {
+#ifdef ORACLE_PAGE_LITERAL
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+static int config_ok(const oracle_config* c) {
+    if (!c) return 0;
+    if (c->dim <= 0 || c->hidden_dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->vocab_size <= 0 || c->seq_len <= 0)
+        return 0;
+    if (c->dim % c->n_heads) return 0;
+    if ((c->dim / c->n_heads) % 2) return 0;
+    if (c->n_kv_heads > c->n_heads) return 0;
+    if (((int64_t)c->dim * c->n_kv_heads) % c->n_heads) return 0;
+    return 1;
+}
+
+static int64_t kv_dim_of(const oracle_config* c) { return (int64_t)c->dim * c->n_kv_heads / c->n_heads; }
+
+/* Per-tensor pointers into the blob ("run.c 逐行解讀" §3, memory_map_weights:
+ * the tensors follow one another, offsets kept in 64 bits). */
+typedef struct {
+    const float *emb, *rms_att, *wq, *wk, *wv, *wo, *rms_ffn, *w1, *w2, *w3, *rms_final, *wcls;
+} weights_t;
+
+static int64_t map_weights(const oracle_config* c, const oracle_options* o, const float* blob, weights_t* w) {
+    const int64_t d = c->dim, h = c->hidden_dim, L = c->n_layers, V = c->vocab_size, kv = kv_dim_of(c);
+    int64_t off = 0;
+    weights_t t;
+#define TAKE(field, count) t.field = blob ? blob + off : NULL; off += (count);
+    TAKE(emb, V * d);
+    TAKE(rms_att, L * d);
+    TAKE(wq, L * d * d);
+    TAKE(wk, L * kv * d);
+    TAKE(wv, L * kv * d);
+    TAKE(wo, L * d * d);
+    TAKE(rms_ffn, L * d);
+    TAKE(w1, L * h * d);
+    TAKE(w2, L * d * h);
+    TAKE(w3, L * h * d);
+    TAKE(rms_final, d);
+    if (o->shared_classifier) {
+        t.wcls = t.emb;
+    } else {
+        TAKE(wcls, V * d);
+    }
+#undef TAKE
+    if (w) *w = t;
+    return off;
+}
+
+int64_t oracle_blob_floats(const oracle_config* c, const oracle_options* o) {
+    if (!config_ok(c) || !o) return -1;
+    return map_weights(c, o, NULL, NULL);
+}
+
+/* RMSNorm: "run.c 逐行解讀" §4 RMSNorm, weight * x / sqrt(mean(x^2) + eps);
+ * same as rmsnorm() of the "run.c" page. */
+void oracle_rmsnorm(float* out, const float* x, const float* g, int n, double eps) {
+    acc_t ss = 0;
+    for (int j = 0; j < n; ++j) ss += (acc_t)x[j] * (acc_t)x[j];
+    ss /= (acc_t)n;
+    ss += (acc_t)eps;
+    acc_t r = (acc_t)1 / ACC_SQRT(ss);
+    for (int j = 0; j < n; ++j) out[j] = (float)((acc_t)g[j] * (r * (acc_t)x[j]));
+}
+
+/* Matrix-vector product: "run.c 逐行解讀" §4 Matmul, W(d,n) @ x(n) -> out(d),
+ * element (i, j) of W at w[i*n + j]. */
+void oracle_matvec(float* out, const float* w, const float* x, int d, int n) {
+    for (int i = 0; i < d; ++i) {
+        const float* row = w + (int64_t)i * n;
+        acc_t s = 0;
+        for (int j = 0; j < n; ++j) s += (acc_t)row[j] * (acc_t)x[j];
+        out[i] = (float)s;
+    }
+}
+
+/* RoPE: "run.c 逐行解讀" §4 step 2d.  Within each head the element at offset
+ * 2j pairs with 2j+1; the pair turns by pos * freq with
+ * freq = 1 / theta^(2j / head_size), as the complex product (v0 + i v1) e^{i pos freq}. */
+void oracle_rope(float* v, int n_heads, int head_size, int pos, double theta) {
+    for (int h = 0; h < n_heads; ++h) {
+        float* vh = v + (int64_t)h * head_size;
+        for (int i = 0; i < head_size; i += 2) {
+#ifdef ORACLE_PAGE_LITERAL
+            float freq = 1.0f / powf((float)theta, (float)i / (float)head_size);
+            float ang = (float)pos * freq;
+            float fcr = cosf(ang), fci = sinf(ang);
+#else
+            double freq = 1.0 / pow(theta, (double)i / (double)head_size);
+            double ang = (double)pos * freq;
+            double fcr = cos(ang), fci = sin(ang);
+#endif
+            acc_t v0 = vh[i], v1 = vh[i + 1];
+            vh[i] = (float)(v0 * fcr - v1 * fci);
+            vh[i + 1] = (float)(v0 * fci + v1 * fcr);
+        }
+    }
+}
+
+int oracle_kv_head(int h, int n_heads, int n_kv_heads) { return (int)(((int64_t)h * n_kv_heads) / n_heads); }
+
+/* Causal multi-head attention with grouped KV heads: "run.c 逐行解讀" §4
+ * step 2e.  For every query head: scores q.k_t / sqrt(head_size) for t = 0..pos,
+ * softmax with the maximum subtracted (§4 Softmax), then the weighted sum of
+ * the value rows. */
+void oracle_attention(float* out, const float* q, const float* kc, const float* vc, int n_heads,
+                      int n_kv_heads, int head_size, int pos) {
+    const int64_t kv_dim = (int64_t)head_size * n_kv_heads;
+    acc_t* att = (acc_t*)malloc(sizeof(acc_t) * (size_t)(pos + 1));
+    for (int h = 0; h < n_heads; ++h) {
+        const int g = oracle_kv_head(h, n_heads, n_kv_heads);
+        const float* qh = q + (int64_t)h * head_size;
+        for (int t = 0; t <= pos; ++t) {
+            const float* k = kc + (int64_t)t * kv_dim + (int64_t)g * head_size;
+            acc_t s = 0;
+            for (int i = 0; i < head_size; ++i) s += (acc_t)qh[i] * (acc_t)k[i];
+            att[t] = s / ACC_SQRT((acc_t)head_size);
+        }
+        acc_t m = att[0];
+        for (int t = 1; t <= pos; ++t)
+            if (att[t] > m) m = att[t];
+        acc_t sum = 0;
+        for (int t = 0; t <= pos; ++t) {
+            att[t] = ACC_EXP(att[t] - m);
+            sum += att[t];
+        }
+        for (int t = 0; t <= pos; ++t) att[t] /= sum;
+        for (int i = 0; i < head_size; ++i) {
+            acc_t acc = 0;
+            for (int t = 0; t <= pos; ++t)
+                acc += att[t] * (acc_t)vc[(int64_t)t * kv_dim + (int64_t)g * head_size + i];
+            out[(int64_t)h * head_size + i] = (float)acc;
+        }
+    }
+    free(att);
+}
+
+/* SwiGLU gate: "run.c 逐行解讀" §4 step 2h, silu(u) = u * (1 / (1 + e^-u)),
+ * multiplied element-wise by the w3 branch. */
+void oracle_swiglu(float* hb, const float* h1, const float* h3, int n) {
+    for (int i = 0; i < n; ++i) {
+        acc_t u = h1[i];
+        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));
+        u *= (acc_t)h3[i];
+        hb[i] = (float)u;
+    }
+}
+
+/* Greedy choice: argmax() of the "run.c" page, a strict '>' scan. */
+int oracle_argmax(const float* v, int n) {
+    int best = 0;
+    float bv = v[0];
+    for (int i = 1; i < n; ++i)
+        if (v[i] > bv) {
+            bv = v[i];
+            best = i;
+        }
+    return best;
+}
+
+static void add_into(float* x, const float* y, int n) {
+    for (int i = 0; i < n; ++i) x[i] = (float)((acc_t)x[i] + (acc_t)y[i]);
+}
+
+/* One decode step: "run.c 逐行解讀" §4 forward(), steps 1 to 3. */
+int oracle_forward(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
+                   float* vcache, int token, int pos, float* logits) {
+    if (!config_ok(c) || !o || !blob || !kcache || !vcache || !logits) return -1;
+    if (token < 0 || token >= c->vocab_size || pos < 0 || pos >= c->seq_len) return -1;
+    weights_t w;
+    map_weights(c, o, blob, &w);
+    const int dim = c->dim, hidden = c->hidden_dim, H = c->n_heads, KV = c->n_kv_heads;
+    const int hs = dim / H, kv_dim = (int)kv_dim_of(c), S = c->seq_len;
+    float* x = (float*)malloc(sizeof(float) * (size_t)dim);
+    float* xb = (float*)malloc(sizeof(float) * (size_t)dim);
+    float* xb2 = (float*)malloc(sizeof(float) * (size_t)dim);
+    float* q = (float*)malloc(sizeof(float) * (size_t)dim);
+    float* hb = (float*)malloc(sizeof(float) * (size_t)hidden);
+    float* hb2 = (float*)malloc(sizeof(float) * (size_t)hidden);
+
+    /* step 1: embedding row of the token */
+    memcpy(x, w.emb + (int64_t)token * dim, sizeof(float) * (size_t)dim);
+
+    for (int l = 0; l < c->n_layers; ++l) {
+        const int64_t lw = (int64_t)l;
+        /* 2a: attention RMSNorm */
+        oracle_rmsnorm(xb, x, w.rms_att + lw * dim, dim, o->norm_eps);
+        /* 2b: k and v of this position live in cache row pos */
+        float* kc = kcache + lw * S * kv_dim;
+        float* vc = vcache + lw * S * kv_dim;
+        float* krow = kc + (int64_t)pos * kv_dim;
+        float* vrow = vc + (int64_t)pos * kv_dim;
+        /* 2c: projections */
+        oracle_matvec(q, w.wq + lw * dim * dim, xb, dim, dim);
+        oracle_matvec(krow, w.wk + lw * kv_dim * dim, xb, kv_dim, dim);
+        oracle_matvec(vrow, w.wv + lw * kv_dim * dim, xb, kv_dim, dim);
+        /* 2d: RoPE on all query heads and on the key heads */
+        oracle_rope(q, H, hs, pos, o->rope_theta);
+        oracle_rope(krow, KV, hs, pos, o->rope_theta);
+        /* 2e: attention over rows 0..pos */
+        oracle_attention(xb, q, kc, vc, H, KV, hs, pos);
+        /* 2f: output projection and residual */
+        oracle_matvec(xb2, w.wo + lw * dim * dim, xb, dim, dim);
+        add_into(x, xb2, dim);
+        /* 2g: FFN RMSNorm */
+        oracle_rmsnorm(xb, x, w.rms_ffn + lw * dim, dim, o->norm_eps);
+        /* 2h: SwiGLU FFN and residual */
+        oracle_matvec(hb, w.w1 + lw * hidden * dim, xb, hidden, dim);
+        oracle_matvec(hb2, w.w3 + lw * hidden * dim, xb, hidden, dim);
+        oracle_swiglu(hb, hb, hb2, hidden);
+        oracle_matvec(xb, w.w2 + lw * dim * hidden, hb, dim, hidden);
+        add_into(x, xb, dim);
+    }
+    /* step 3: final RMSNorm and classifier */
+    oracle_rmsnorm(x, x, w.rms_final, dim, o->norm_eps);
+    oracle_matvec(logits, w.wcls, x, c->vocab_size, dim);
+
+    free(x);
+    free(xb);
+    free(xb2);
+    free(q);
+    free(hb);
+    free(hb2);
+    return 0;
+}
+
+/* Greedy generation: the decode loop of the "run.c" page at temperature 0
+ * (the argmax of each step's logits is the next input token). */
+int oracle_generate(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
+                    float* vcache, int token, int pos, int n, int32_t* tokens_out, float* logits_out) {
+    if (!config_ok(c) || n < 0 || pos < 0 || (int64_t)pos + n > c->seq_len || !tokens_out) return -1;
+    float* logits = (float*)malloc(sizeof(float) * (size_t)c->vocab_size);
+    int rc = 0;
+    for (int i = 0; i < n && rc == 0; ++i) {
+        rc = oracle_forward(c, o, blob, kcache, vcache, token, pos + i, logits);
+        if (rc) break;
+        token = oracle_argmax(logits, c->vocab_size);
+        tokens_out[i] = token;
+        if (logits_out) memcpy(logits_out + (int64_t)i * c->vocab_size, logits, sizeof(float) * (size_t)c->vocab_size);
+    }
+    free(logits);
+    return rc;
+}
+
+/* Full-prefix recompute with no cache, in the style of TransformerDecoder$call
+ * of the R/Keras page: every layer runs over all T = p+1 positions at once and
+ * the scores get the additive causal mask of make_mask (-inf where the key
+ * index exceeds the query index) before the softmax. */
+int oracle_bruteforce(const oracle_config* c, const oracle_options* o, const float* blob,
+                      const int32_t* tokens, int p, float* logits) {
+    if (!config_ok(c) || !o || !blob || !tokens || !logits || p < 0 || p >= c->seq_len) return -1;
+    for (int t = 0; t <= p; ++t)
+        if (tokens[t] < 0 || tokens[t] >= c->vocab_size) return -1;
+    weights_t w;
+    map_weights(c, o, blob, &w);
+    const int dim = c->dim, hidden = c->hidden_dim, H = c->n_heads, KV = c->n_kv_heads;
+    const int hs = dim / H, kv_dim = (int)kv_dim_of(c), T = p + 1;
+    float* X = (float*)malloc(sizeof(float) * (size_t)T * dim);
+    float* XB = (float*)malloc(sizeof(float) * (size_t)T * dim);
+    float* Q = (float*)malloc(sizeof(float) * (size_t)T * dim);
+    float* K = (float*)malloc(sizeof(float) * (size_t)T * kv_dim);
+    float* Vv = (float*)malloc(sizeof(float) * (size_t)T * kv_dim);
+    float* A = (float*)malloc(sizeof(float) * (size_t)T * dim);
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)dim);
+    float* h1 = (float*)malloc(sizeof(float) * (size_t)hidden);
+    float* h3 = (float*)malloc(sizeof(float) * (size_t)hidden);
+    acc_t* sc = (acc_t*)malloc(sizeof(acc_t) * (size_t)T);
+
+    for (int t = 0; t < T; ++t) memcpy(X + (int64_t)t * dim, w.emb + (int64_t)tokens[t] * dim, sizeof(float) * (size_t)dim);
+
+    for (int l = 0; l < c->n_layers; ++l) {
+        const int64_t lw = l;
+        for (int t = 0; t < T; ++t) {
+            float* xb = XB + (int64_t)t * dim;
+            oracle_rmsnorm(xb, X + (int64_t)t * dim, w.rms_att + lw * dim, dim, o->norm_eps);
+            oracle_matvec(Q + (int64_t)t * dim, w.wq + lw * dim * dim, xb, dim, dim);
+            oracle_matvec(K + (int64_t)t * kv_dim, w.wk + lw * kv_dim * dim, xb, kv_dim, dim);
+            oracle_matvec(Vv + (int64_t)t * kv_dim, w.wv + lw * kv_dim * dim, xb, kv_dim, dim);
+            oracle_rope(Q + (int64_t)t * dim, H, hs, t, o->rope_theta);
+            oracle_rope(K + (int64_t)t * kv_dim, KV, hs, t, o->rope_theta);
+        }
+        /* scores (query i, key j) over the whole T x T square, plus the mask */
+        for (int h = 0; h < H; ++h) {
+            const int g = oracle_kv_head(h, H, KV);
+            for (int i = 0; i < T; ++i) {
+                const float* qi = Q + (int64_t)i * dim + (int64_t)h * hs;
+                for (int j = 0; j < T; ++j) {
+                    const float* kj = K + (int64_t)j * kv_dim + (int64_t)g * hs;
+                    acc_t s = 0;
+                    for (int e = 0; e < hs; ++e) s += (acc_t)qi[e] * (acc_t)kj[e];
+                    s /= ACC_SQRT((acc_t)hs);
+                    sc[j] = s + (i < j ? (acc_t)-INFINITY : (acc_t)0);
+                }
+                acc_t m = sc[0];
+                for (int j = 1; j < T; ++j)
+                    if (sc[j] > m) m = sc[j];
+                acc_t sum = 0;
+                for (int j = 0; j < T; ++j) {
+                    sc[j] = ACC_EXP(sc[j] - m);
+                    sum += sc[j];
+                }
+                for (int e = 0; e < hs; ++e) {
+                    acc_t acc = 0;
+                    for (int j = 0; j < T; ++j) acc += (sc[j] / sum) * (acc_t)Vv[(int64_t)j * kv_dim + (int64_t)g * hs + e];
+                    A[(int64_t)i * dim + (int64_t)h * hs + e] = (float)acc;
+                }
+            }
+        }
+        for (int t = 0; t < T; ++t) {
+            float* x = X + (int64_t)t * dim;
+            oracle_matvec(tmp, w.wo + lw * dim * dim, A + (int64_t)t * dim, dim, dim);
+            add_into(x, tmp, dim);
+            oracle_rmsnorm(tmp, x, w.rms_ffn + lw * dim, dim, o->norm_eps);
+            oracle_matvec(h1, w.w1 + lw * hidden * dim, tmp, hidden, dim);
+            oracle_matvec(h3, w.w3 + lw * hidden * dim, tmp, hidden, dim);
+            oracle_swiglu(h1, h1, h3, hidden);
+            oracle_matvec(tmp, w.w2 + lw * dim * hidden, h1, dim, hidden);
+            add_into(x, tmp, dim);
+        }
+    }
+    float* xl = X + (int64_t)p * dim;
+    oracle_rmsnorm(xl, xl, w.rms_final, dim, o->norm_eps);
+    oracle_matvec(logits, w.wcls, xl, c->vocab_size, dim);
+
+    free(X);
+    free(XB);
+    free(Q);
+    free(K);
+    free(Vv);
+    free(A);
+    free(tmp);
+    free(h1);
+    free(h3);
+    free(sc);
+    return 0;
+}

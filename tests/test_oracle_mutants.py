@@ -1,0 +1,56 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of ``oracle/oracle.c`` (on the CPU, in a
+temporary directory), builds it, and runs the pin suite against the mutant:
+the suite must fail.  A mutation that the pins let through would mean the
+oracle is not pinned against that mistake.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "causal_range_off_by_one": ("for (int t = 0; t <= pos; ++t) {\n            const float* k", "for (int t = 0; t < pos; ++t) {\n            const float* k"),
+    "attention_scale_dropped": ("att[t] = s / ACC_SQRT((acc_t)head_size);", "att[t] = s;"),
+    "rmsnorm_eps_dropped": ("ss += (acc_t)eps;", ""),
+    "rmsnorm_sum_not_mean": ("ss /= (acc_t)n;", ""),
+    "rope_sign_flipped": ("vh[i] = (float)(v0 * fcr - v1 * fci);", "vh[i] = (float)(v0 * fcr + v1 * fci);"),
+    "rope_frequency_index": ("double freq = 1.0 / pow(theta, (double)i / (double)head_size);",
+                             "double freq = 1.0 / pow(theta, (double)(i / 2) / (double)head_size);"),
+    "swiglu_branches_swapped": ("acc_t u = h1[i];\n        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));\n        u *= (acc_t)h3[i];",
+                                "acc_t u = h3[i];\n        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));\n        u *= (acc_t)h1[i];"),
+    "attention_residual_overwrites": ("add_into(x, xb2, dim);", "memcpy(x, xb2, sizeof(float) * (size_t)dim);"),
+    "ffn_residual_dropped": ("oracle_matvec(xb, w.w2 + lw * dim * hidden, hb, dim, hidden);\n        add_into(x, xb, dim);",
+                             "oracle_matvec(xb, w.w2 + lw * dim * hidden, hb, dim, hidden);"),
+    "kv_head_integer_kv_mul": ("return (int)(((int64_t)h * n_kv_heads) / n_heads);",
+                               "return h / (n_heads / n_kv_heads) < n_kv_heads ? h / (n_heads / n_kv_heads) : n_kv_heads - 1;"),
+    "matvec_transposed": ("for (int j = 0; j < n; ++j) s += (acc_t)row[j] * (acc_t)x[j];",
+                          "for (int j = 0; j < n; ++j) s += (acc_t)w[(int64_t)j * d + i] * (acc_t)x[j];"),
+    "argmax_last_maximum": ("if (v[i] > bv) {", "if (v[i] >= bv) {"),
+    "key_rope_skipped": ("oracle_rope(krow, KV, hs, pos, o->rope_theta);", ""),
+    "ffn_norm_uses_attention_gain": ("oracle_rmsnorm(xb, x, w.rms_ffn + lw * dim, dim, o->norm_eps);",
+                                     "oracle_rmsnorm(xb, x, w.rms_att + lw * dim, dim, o->norm_eps);"),
+    "softmax_max_not_subtracted_wrongly": ("att[t] = ACC_EXP(att[t] - m);", "att[t] = ACC_EXP(att[t] + m);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared",
+                    "-I", os.path.join(ROOT, "oracle"), str(mut), "-o", str(so), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
