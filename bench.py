@@ -1,0 +1,263 @@
+"""Benchmark of the single-token Llama-2 decode step on one MI355X.
+
+Workload (default): the Llama-2-7B-shaped model (dim 4096, hidden 11008, 32
+layers, 32 query / 32 kv heads, vocab 32000, seq_len 2048, fp32, seeded random
+weights), greedy decode from token 1 at position 0.  One step = one decode
+token: every kernel of the path (q/k/v + RoPE + cache append, attention, wo +
+residual, w1/w3 SwiGLU, w2 + residual per layer; classifier + argmax) runs
+once.  The weights are resident in HBM before the timed region starts.
+
+Output: one JSON line with decode tokens/s, achieved HBM GB/s (algorithmic
+bytes read per token / time), the roofline of the dominant kernel (its average
+launch duration measured with HIP events on the library's stream over a pass
+of the same workload) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def bytes_per_token(c, pos: int) -> int:
+    """Algorithmic bytes read by one decode step at position pos: every weight
+    once (layer matrices and gains, the whole classifier, one embedding row, the
+    final gain) plus the key and value rows 0..pos of every layer."""
+    kv = c.dim * c.n_kv_heads // c.n_heads
+    per_layer = 2 * c.dim * c.dim + 2 * kv * c.dim + 3 * c.dim * c.hidden_dim + 2 * c.dim
+    floats = c.n_layers * per_layer + c.vocab_size * c.dim + 2 * c.dim
+    return 4 * floats + 4 * 2 * c.n_layers * (pos + 1) * kv
+
+
+def kernel_bytes(c, kind: str, pos_list) -> float:
+    """Algorithmic bytes moved per launch of one kernel kind, averaged over the
+    positions of the pass (only attention depends on the position)."""
+    d, h, V = c.dim, c.hidden_dim, c.vocab_size
+    kv = d * c.n_kv_heads // c.n_heads
+    if kind == "qkv_rope_append":  # Wq, Wk, Wv + x + gain; q and the cache row written
+        return 4.0 * ((d + 2 * kv) * d + 2 * d + d + 2 * kv)
+    if kind == "wo_residual":  # Wo + xb + x read and written
+        return 4.0 * (d * d + d + 2 * d)
+    if kind == "w1w3_swiglu":  # W1, W3 + x + gain; hb written
+        return 4.0 * (2 * h * d + 2 * d + h)
+    if kind == "w2_residual":  # W2 + hb + x read and written
+        return 4.0 * (d * h + h + 2 * d)
+    if kind == "classifier_argmax":  # Wcls + x + gain; logits written
+        return 4.0 * (V * d + 2 * d + V)
+    if kind == "attention":  # q, key and value rows 0..pos of one layer, output
+        mean_rows = sum(p + 1 for p in pos_list) / len(pos_list)
+        return 4.0 * (2 * d + 2 * kv * mean_rows)
+    raise KeyError(kind)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("ld_kernels.hip", "ld_runtime.hip", "ld_internal.h"):
+        with open(os.path.join(ROOT, "llama_transformer_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def windows_for(seq_len: int, steps: int, width: int = 16):
+    """Chunk boundaries of the timed generation: 16-step windows at the start,
+    around position 511 and at the end, so per-position rates come from the same
+    timed pass."""
+    marks = {0, min(width, steps)}
+    if steps > 520:
+        marks |= {504, 520}
+    if steps > 2 * width:
+        marks |= {steps - width, steps}
+    marks.add(steps)
+    b = sorted(m for m in marks if 0 <= m <= steps)
+    return list(zip(b[:-1], b[1:]))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default: seq_len)")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps before the timed pass")
+    ap.add_argument("--config", default="llama7b", help="workload: tiny, stories15m, gqa_small, llama7b, llama70b_8l")
+    ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=2, help="oracle decode steps timed for the CPU baseline")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode step is not sharded across GPUs in this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import llama_transformer_decode_amd as pkg
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    S = cfg.seq_len
+    steps = args.steps or S
+    warm = max(0, args.warmup)
+
+    t = time.time()
+    blob = synth.make_blob(cfg)
+    t_gen = time.time() - t
+    t = time.time()
+    weights = torch.from_numpy(blob).to("cuda:0")
+    torch.cuda.synchronize()
+    t_up = time.time() - t
+    print(f"# {cfg.name}: {blob.nbytes / 1e9:.2f} GB of weights generated in {t_gen:.1f} s, uploaded in {t_up:.1f} s",
+          file=sys.stderr, flush=True)
+
+    model = pkg.Model(cfg, weights, graph=not args.no_graph)
+    # warm-up: instantiates the per-token graph and touches every kernel
+    if warm:
+        model.generate(1, 0, min(warm, S))
+    model.reset()
+    torch.cuda.synchronize()
+
+    # ---- timed region: greedy decode of `steps` tokens from token 1 at pos 0 ----
+    chunks = []
+    done, tok, t_total = 0, 1, 0.0
+    while done < steps:
+        n_pass = min(S, steps - done)
+        if done:
+            model.reset()
+        for a, b in windows_for(S, n_pass):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            toks = model.generate(tok, a, b - a)
+            t1 = time.perf_counter()
+            tok = int(toks[-1])
+            chunks.append((a, b, t1 - t0))
+            t_total += t1 - t0
+        done += n_pass
+        tok = 1
+    torch.cuda.synchronize()
+
+    total_bytes = sum(bytes_per_token(cfg, p) for a, b, _ in chunks for p in range(a, b))
+    tok_s = steps / t_total
+    gbps = total_bytes / t_total / 1e9
+    per_pos = {}
+    for a, b, dt in chunks:
+        if b - a <= 16:
+            key = f"pos_{a}_{b - 1}"
+            byt = sum(bytes_per_token(cfg, p) for p in range(a, b))
+            per_pos[key] = {"tok_s": round((b - a) / dt, 2), "GBps": round(byt / dt / 1e9, 1),
+                            "frac_of_peak": round(byt / dt / 1e9 / HBM_PEAK_GBPS, 4)}
+    print(f"# timed {steps} steps in {t_total:.3f} s: {tok_s:.1f} tok/s, {gbps:.0f} GB/s", file=sys.stderr,
+          flush=True)
+
+    # ---- kernel durations: the same workload, every launch bracketed by HIP events ----
+    roofline = None
+    kernels = None
+    if not args.no_kernel_timing:
+        model.reset()
+        n_prof = min(steps, S)
+        stats = model.profile(1, 0, n_prof)
+        pos_list = list(range(n_prof))
+        kernels = {}
+        for s in stats:
+            if s["launches"]:
+                avg_ms = s["total_ms"] / s["launches"]
+                byt = kernel_bytes(cfg, s["name"], pos_list)
+                kernels[s["name"]] = {"launches": s["launches"], "avg_us": round(avg_ms * 1e3, 2),
+                                      "bytes_per_launch": int(byt), "GBps": round(byt / (avg_ms * 1e-3) / 1e9, 1),
+                                      "share_of_time": round(s["total_ms"], 3)}
+        tot = sum(k["share_of_time"] for k in kernels.values())
+        for k in kernels.values():
+            k["share_of_time"] = round(k["share_of_time"] / tot, 4)
+        dom = max(kernels, key=lambda k: kernels[k]["share_of_time"])
+        kd = kernels[dom]
+        traffic = load_traffic(dom, cfg.name)
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "bytes_per_launch": kd["bytes_per_launch"], "avg_us": kd["avg_us"]}
+        print(f"# kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+
+    model.close()
+    del weights
+    torch.cuda.empty_cache()
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cache = oracle.KVCache(cfg)
+        n_cpu = max(1, min(args.cpu_steps, S))
+        t0 = time.perf_counter()
+        tok = 1
+        for p in range(n_cpu):
+            logits = oracle.forward(cfg, blob, cache, tok, p)
+            tok = oracle.argmax(logits)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(n_cpu / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_cpu} greedy decode steps (positions 0-{n_cpu - 1}) of the {cfg.name} workload, "
+                         f"single-threaded C oracle with double accumulation, {dt:.1f} s",
+               "GBps": round(sum(bytes_per_token(cfg, p) for p in range(n_cpu)) / dt / 1e9, 2),
+               "host_cores_available": os.cpu_count()}
+
+    line = {
+        "metric": "batch-1 decode tokens/sec + achieved HBM GB/s as % of MI355X peak",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(1e3 * t_total / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: greedy decode of {steps} tokens from token 1 at position 0, batch 1, "
+                               f"dim {cfg.dim}, hidden {cfg.hidden_dim}, {cfg.n_layers} layers, "
+                               f"{cfg.n_heads}/{cfg.n_kv_heads} heads, vocab {cfg.vocab_size}, "
+                               f"seq_len {cfg.seq_len}, fp32 N(0,0.02) weights (seed {cfg.seed})",
+                   "global_batch": 1, "seq_len": cfg.seq_len, "parallelism": "single-gpu",
+                   "graph_replay": not args.no_graph},
+        "hbm_GBps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_token_pos0": bytes_per_token(cfg, 0),
+        "per_position": per_pos,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

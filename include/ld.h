@@ -1,0 +1,198 @@
+/*
+ * ld.h -- C ABI of the MI355X (gfx950) single-token Llama-2 decode library.
+ *
+ * The library runs one decode step of a Llama-2 decoder at batch 1 in fp32:
+ * embedding lookup, per layer RMSNorm, q/k/v projections, RoPE, KV-cache
+ * append, causal grouped-query attention, output projection + residual,
+ * RMSNorm, SwiGLU FFN + residual; then the final RMSNorm, classifier logits
+ * and the greedy argmax.  The step is the forward() walkthrough of the
+ * "run.c 逐行解讀" page (§4, steps 1, 2a-2h, 3) and transformer() of the
+ * "run.c" page; the interface follows those pages: Config is the create
+ * argument, the Transformer aggregate becomes an opaque handle, forward(token,
+ * pos) returns logits, and the greedy loop is the generate loop of "run.c"
+ * at temperature 0.
+ *
+ * Conventions for every call:
+ *   - Every call returns an int status: LD_OK (0) or a negative LD_E_* code.
+ *     No call aborts the process or lets a C++ exception escape.
+ *   - Pointers named d_* are device pointers (HIP device memory, e.g. the
+ *     storage of a torch CUDA tensor); h_* are host pointers.
+ *   - A model may be used by one host thread at a time.
+ *   - Matrices are fp32, row-major (out, in): element (i, j) at w[i*in + j]
+ *     ("run.c", matmul).
+ */
+#ifndef LD_H
+#define LD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model shape: the Config struct of the "run.c" page (seven int32 fields in
+ * this order).  kv_dim = dim * n_kv_heads / n_heads ("run.c 逐行解讀", §3).
+ * Validity (else LD_E_CONFIG): every field > 0; dim % n_heads == 0; head_size
+ * = dim / n_heads even; n_kv_heads <= n_heads; dim * n_kv_heads % n_heads == 0;
+ * dim, hidden_dim and kv_dim multiples of 4.  Supported by the kernels (else
+ * LD_E_UNSUPPORTED): head_size in {16, 32, 48, 64, 80, 96, 128, 256}; at most 8
+ * query heads per kv head; dim and hidden_dim <= 32768. */
+typedef struct ld_config {
+    int32_t dim;
+    int32_t hidden_dim;
+    int32_t n_layers;
+    int32_t n_heads;
+    int32_t n_kv_heads;
+    int32_t vocab_size;
+    int32_t seq_len;
+} ld_config;
+
+/* Options.  norm_eps is added to mean(x^2) inside the RMSNorm square root
+ * (1e-5 on the "run.c" page).  rope_theta is the RoPE base (10000).
+ * shared_classifier = 1 makes the classifier the embedding table ("run.c"
+ * transformer(); "run.c 逐行解讀" §2 wcls may share the embedding), 0 reads a
+ * separate wcls from the end of the blob.  flags: LD_OPT_* bits. */
+typedef struct ld_options {
+    float norm_eps;
+    float rope_theta;
+    int32_t shared_classifier;
+    int32_t flags;
+} ld_options;
+
+/* Replay-free mode: launch every kernel of a step directly instead of
+ * replaying the captured per-token HIP graph.  Results are bit-identical. */
+#define LD_OPT_NO_GRAPH 1
+
+typedef struct ld_model ld_model;
+
+enum {
+    LD_OK = 0,
+    LD_E_NULL = -1,        /* a required pointer argument is NULL */
+    LD_E_CONFIG = -2,      /* the config or options are invalid (see ld_config) */
+    LD_E_SIZE = -3,        /* the weight blob has the wrong size */
+    LD_E_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+    LD_E_RANGE = -5,       /* token, pos or a step count is out of range */
+    LD_E_OOM = -6,         /* a device allocation failed */
+    LD_E_HIP = -7,         /* a HIP runtime call failed */
+    LD_E_UNSUPPORTED = -8  /* valid shape that the compiled kernels do not cover */
+};
+
+/* Size in bytes of the weight blob for (cfg, opt).  The blob is fp32,
+ * contiguous, no padding, tensors in this order (checkpoint order of the
+ * "run.c" page, checkpoint_init_weights, with the grouped-query shapes and the
+ * separate classifier of "run.c 逐行解讀" §2; no RoPE tables):
+ *   E (V,dim) | rms_att (L,dim) | wq (L,dim,dim) | wk (L,kv_dim,dim) |
+ *   wv (L,kv_dim,dim) | wo (L,dim,dim) | rms_ffn (L,dim) | w1 (L,hidden,dim) |
+ *   w2 (L,dim,hidden) | w3 (L,hidden,dim) | rms_final (dim) |
+ *   [wcls (V,dim) when shared_classifier == 0]
+ * Needs no GPU.  Errors: LD_E_NULL, LD_E_CONFIG. */
+int ld_weights_size(const ld_config* cfg, const ld_options* opt, size_t* bytes_out);
+
+/* Create a model over a device weight blob.
+ *   d_weights: device memory holding the blob (layout above), 16-byte aligned,
+ *              exactly ld_weights_size bytes.  Borrowed, never written; it must
+ *              stay valid until ld_destroy.
+ *   hip_stream: the caller's hipStream_t (NULL = the null stream).  Work of a
+ *              call starts after the work already queued on it, and later work
+ *              queued on it starts after the call's work.
+ * The library allocates and owns the KV caches (zeroed), the activations, the
+ * logits and the per-token graph.  Errors: LD_E_NULL, LD_E_CONFIG,
+ * LD_E_UNSUPPORTED, LD_E_SIZE, LD_E_ALIGN, LD_E_OOM, LD_E_HIP. */
+int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights, size_t bytes,
+              void* hip_stream, ld_model** out);
+
+/* Zero both KV caches (the calloc'd state of the pages).  Asynchronous. */
+int ld_reset(ld_model* m);
+
+/* One decode step at (token, pos): writes KV-cache row pos of every layer,
+ * attends over rows 0..pos (never reads a row above pos) and leaves the logits
+ * (vocab_size floats, library-owned device memory) at *d_logits_out, valid
+ * until the next call on this model and ready in stream order.  Asynchronous.
+ * Needs 0 <= token < vocab_size and 0 <= pos < seq_len, else LD_E_RANGE. */
+int ld_forward(ld_model* m, int32_t token, int32_t pos, const float** d_logits_out);
+
+/* Lowest index holding the maximum of the last step's logits (the strict '>'
+ * scan of argmax() on the "run.c" page).  Synchronous. */
+int ld_argmax_last(ld_model* m, int32_t* h_token_out);
+
+/* Greedy generation: for i = 0..n_steps-1, logits = forward(tok_i, pos + i),
+ * tok_{i+1} = argmax(logits), h_tokens_out[i] = tok_{i+1}; tok_0 = token.
+ * No stop token.  Needs pos + n_steps <= seq_len (else LD_E_RANGE).
+ * h_tokens_out: caller-owned host array of n_steps int32.  Synchronous. */
+int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, int32_t* h_tokens_out);
+
+/* Device pointers of the key and value caches, each (n_layers, seq_len,
+ * kv_dim) fp32 row-major, and their size in floats.  The caller may read or
+ * overwrite them between calls (e.g. to install a cache prefix). */
+int ld_kv_cache(ld_model* m, float** d_key_out, float** d_value_out, size_t* floats_out);
+
+/* Free everything the model owns.  NULL is accepted. */
+void ld_destroy(ld_model* m);
+
+/* Text for a status code; never NULL. */
+const char* ld_strerror(int status);
+
+/* Text naming the HIP call and error behind the calling thread's most recent
+ * LD_E_HIP or LD_E_OOM ("" if none); never NULL. */
+const char* ld_last_error_detail(void);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing.  Runs n_steps greedy decode steps from (token, pos) with
+ * every kernel launched directly and bracketed by HIP events on the model's
+ * stream, and reports per kernel kind the launch count and the summed event
+ * time.  Kinds: "qkv_rope_append", "attention", "wo_residual",
+ * "w1w3_swiglu", "w2_residual", "classifier_argmax".  stats must hold
+ * max_stats entries; *n_stats_out receives the number filled.  Synchronous.
+ */
+typedef struct ld_kernel_stat {
+    char name[32];
+    int32_t launches;
+    double total_ms;
+} ld_kernel_stat;
+
+int ld_profile_steps(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, ld_kernel_stat* stats,
+                     int32_t max_stats, int32_t* n_stats_out);
+
+/* ---------------------------------------------------------------------------
+ * Single kernels of the step, for testing each against its definition.  Each
+ * runs the same kernel the model uses, on hip_stream (NULL = null stream),
+ * allocates its own temporaries and returns after the stream has synchronised.
+ * Shapes follow the ld_config rules (n and rows multiples of 4, n <= 32768).
+ */
+
+/* d_out(rows) = W(rows, n) . x'(n), x' = g * x / sqrt(mean(x^2) + eps) when
+ * d_g != NULL ("run.c 逐行解讀" §4 RMSNorm and Matmul), x' = x when d_g == NULL. */
+int ld_op_rmsnorm_gemv(const float* d_x, const float* d_g, float eps, const float* d_w, int32_t rows,
+                       int32_t n, float* d_out, void* hip_stream);
+
+/* d_x(rows) += W(rows, n) . d_in(n)  (§4 steps 2f and 2h: projection + residual). */
+int ld_op_gemv_residual(const float* d_in, const float* d_w, int32_t rows, int32_t n, float* d_x,
+                        void* hip_stream);
+
+/* d_hb(hidden) = silu(W1 . x') * (W3 . x'), x' = RMSNorm(x) with gain g
+ * (§4 steps 2g-2h). */
+int ld_op_swiglu(const float* d_x, const float* d_g, float eps, const float* d_w1, const float* d_w3,
+                 int32_t hidden, int32_t n, float* d_hb, void* hip_stream);
+
+/* q = Wq x', k = Wk x', v = Wv x' with x' = RMSNorm(x, g), then RoPE at pos on
+ * the n_heads heads of q and the n_kv_heads heads of k (§4 steps 2a-2d).
+ * q: dim floats; k, v: kv_dim floats. */
+int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d_wq, const float* d_wk,
+                   const float* d_wv, int32_t dim, int32_t n_heads, int32_t n_kv_heads, int32_t pos,
+                   float theta, float* d_q, float* d_k, float* d_v, void* hip_stream);
+
+/* Causal GQA attention of one layer at pos (§4 step 2e): d_q (n_heads *
+ * head_size), d_kc / d_vc (at least pos+1 rows of kv_dim floats), d_out
+ * (n_heads * head_size).  Query head h reads kv head floor(h*n_kv/n_heads). */
+int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
+                    int32_t n_kv_heads, int32_t head_size, int32_t pos, float* d_out, void* hip_stream);
+
+/* Lowest index of the maximum of d_v[0..n) ("run.c", argmax). */
+int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LD_H */

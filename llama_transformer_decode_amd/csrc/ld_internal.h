@@ -1,0 +1,103 @@
+// Internal interface between the kernels (ld_kernels.hip) and the runtime
+// (ld_runtime.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ld {
+
+// Per-step scalars kept in device memory so that one captured graph serves
+// every position: the classifier kernel writes `next` and advances
+// (token, pos) for the following step.
+struct StepState {
+    int32_t token;
+    int32_t pos;
+    int32_t next;
+    int32_t pad;
+};
+
+// Kinds of the matrix-vector kernel family.  All read one fp32 row-major
+// weight matrix (or a pair / triple of them) once and differ in the prologue
+// (optional RMSNorm of x) and the epilogue.
+enum GemvKind : int {
+    K_PLAIN = 0,   // out[r] = W x'
+    K_RESID = 1,   // x_resid[r] += W in
+    K_QKV = 2,     // [Wq;Wk;Wv] x', RoPE on q and k, k/v into cache row pos
+    K_SWIGLU = 3,  // hb[e] = silu(W1 x')[e] * (W3 x')[e]
+    K_CLS = 4,     // logits[r] = Wcls x', then the greedy argmax
+};
+
+// Launch geometry: `nt` threads per block, each holding `nx` float4 of x;
+// `rpi` weight rows per iteration; `units` row groups split evenly over `grid`
+// blocks.
+struct GemvPlan {
+    int kind;
+    int nt;
+    int nx;
+    int rpi;
+    int units;
+    int grid;
+};
+
+struct GemvParams {
+    const float* x;        // input vector, n floats
+    const float* emb;      // K_QKV at layer 0: x := emb[token] and x_resid := emb[token]
+    float* x_resid;        // residual stream (K_RESID target, K_QKV layer-0 copy)
+    const float* gain;     // RMSNorm gain, nullptr = no normalisation
+    float eps;
+    int n;                 // input length (floats)
+    int rows;              // output elements (K_SWIGLU: hidden units)
+    int units;             // row groups
+    const float* w0;       // weights: K_QKV wq; K_SWIGLU w1; else W
+    const float* w1;       // K_QKV wk; K_SWIGLU w3
+    const float* w2;       // K_QKV wv
+    int seg1;              // K_QKV: first k row (dim)
+    int seg2;              // K_QKV: first v row (dim + kv_dim)
+    float* out;            // K_PLAIN out, K_QKV q, K_SWIGLU hb, K_CLS logits
+    float* kc;             // K_QKV: key cache of the layer
+    float* vc;             // K_QKV: value cache of the layer
+    int kv_stride;         // K_QKV: floats between cache rows (kv_dim; 0 = single row)
+    int head_size;
+    const float2* rope;    // K_QKV: (position, head_size/2) -> (cos, sin)
+    StepState* state;
+    float2* best;          // K_CLS: per-block (value, index bits)
+};
+
+struct AttnParams {
+    const float* q;        // n_heads * head_size
+    const float* kc;       // this layer's key cache, rows of kv_dim
+    const float* vc;
+    float* out;            // n_heads * head_size
+    float2* part_ml;       // (n_heads, nsplit) running max and sum
+    float* part_acc;       // (n_heads, nsplit, head_size) unnormalised outputs
+    const StepState* state;
+    int n_heads;
+    int n_kv_heads;
+    int kv_dim;
+    int nsplit;            // grid.y
+    int chunk;             // keys per split (set by the launcher)
+};
+
+// Plans and launchers.  Return hipSuccess, or hipErrorInvalidValue for a
+// shape outside the compiled kernels.
+hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan);
+hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s);
+
+int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)
+int attn_splits(int head_size, int seq_len, int n_kv_heads);  // grid.y of the attention kernel
+hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention + merge
+
+hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
+// argmax of v: per-block bests, then the final reduction into st->next
+hipError_t argmax_launch(const float* v, int n, float2* best, int nblocks, StepState* st, hipStream_t s);
+// final reduction of the classifier's per-block bests: st->next, tokens_out[pos], advance (token, pos)
+hipError_t argmax_final_launch(const float2* best, int nblocks, StepState* st, int32_t* tokens_out, hipStream_t s);
+int argmax_blocks(int n);
+
+constexpr int kAttnThreads = 256;
+constexpr int kMaxGroup = 8;   // query heads per kv head
+constexpr int kMaxN = 32768;   // longest input vector of a matrix-vector kernel
+
+}  // namespace ld

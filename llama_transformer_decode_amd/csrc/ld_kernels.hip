@@ -1,0 +1,832 @@
+// ld_kernels.hip -- gfx950 (CDNA4) kernels of the single-token Llama-2 decode
+// step, fp32, batch 1.
+//
+// The step is the forward() walkthrough of the "run.c 逐行解讀" page (§4):
+// RMSNorm, q/k/v matmuls, RoPE, KV-cache write, grouped-query attention,
+// output matmul + residual, FFN RMSNorm, SwiGLU, down matmul + residual, final
+// RMSNorm, classifier, and the greedy argmax of the "run.c" page.
+//
+// At batch 1 every weight is used once per token for one multiply-add, so the
+// step is bound by HBM bandwidth (0.5 flop per byte).  The matrix-vector
+// kernels therefore stream each weight row once with 128-bit loads and keep
+// the input vector in registers; there is no MFMA here because nothing is a
+// dense contraction.
+#include "ld_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+namespace ld {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions with DPP.  Each step adds a permuted copy of the
+// register: neighbours in a quad, the quads of a half row, the halves of a row
+// (16 lanes), then row 0 into row 1 and row 2 into row 3 (row_bcast:15), then
+// rows 0-1 into rows 2-3 (row_bcast:31).  Lane 63 ends with the total, which
+// is read back as a wave-uniform value.  Called with all 64 lanes active.
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float old, float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+constexpr int kQuadSwap1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<kQuadSwap1>(0.f, v);
+    v += dpp<kQuadSwap2>(0.f, v);
+    v += dpp<kRowHalfMirror>(0.f, v);
+    v += dpp<kRowMirror>(0.f, v);
+    v += dpp<kRowBcast15, 0xa>(0.f, v);
+    v += dpp<kRowBcast31, 0xc>(0.f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<kQuadSwap1>(-INFINITY, v));
+    v = fmaxf(v, dpp<kQuadSwap2>(-INFINITY, v));
+    v = fmaxf(v, dpp<kRowHalfMirror>(-INFINITY, v));
+    v = fmaxf(v, dpp<kRowMirror>(-INFINITY, v));
+    v = fmaxf(v, dpp<kRowBcast15, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp<kRowBcast31, 0xc>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float dot4(float4 a, float4 b, float acc) {
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
+    return acc;
+}
+
+// Greedy order of the "run.c" argmax: larger value first, and among equal
+// values the lower index (its strict '>' scan keeps the first maximum).
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float ov = __shfl_xor(v, off);
+        const int oi = __shfl_xor(i, off);
+        if (better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+// Block-wide best over (v, i); the result is valid in every thread.
+template <int NT>
+__device__ void block_best(float& v, int& i) {
+    constexpr int NW = NT / 64;
+    __shared__ float sv[NW];
+    __shared__ int si[NW];
+    wave_best(v, i);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sv[wave] = v;
+        si[wave] = i;
+    }
+    __syncthreads();
+    v = sv[0];
+    i = si[0];
+    for (int w = 1; w < NW; ++w)
+        if (better(sv[w], si[w], v, i)) {
+            v = sv[w];
+            i = si[w];
+        }
+}
+
+// The greedy choice in two launches: every block writes its best (value,
+// index) pair, then one block reduces the pairs and writes the next token.
+// Cross-block hand-off at a kernel boundary costs far less on this chip than a
+// device-scope fence inside a kernel (which writes back and invalidates L2).
+template <int NT>
+__device__ void publish_best(float bv, int bi, float2* best) {
+    block_best<NT>(bv, bi);
+    if (threadIdx.x == 0) best[blockIdx.x] = make_float2(bv, __int_as_float(bi));
+}
+
+constexpr int kArgmaxThreads = 256;
+
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_final_kernel(const float2* best, int nblocks,
+                                                                      StepState* st, int32_t* tokens_out) {
+    float v = -INFINITY;
+    int i = INT_MAX;
+#pragma unroll 4
+    for (int b = threadIdx.x; b < nblocks; b += kArgmaxThreads) {
+        const float2 e = best[b];
+        const int ei = __float_as_int(e.y);
+        if (better(e.x, ei, v, i)) {
+            v = e.x;
+            i = ei;
+        }
+    }
+    block_best<kArgmaxThreads>(v, i);
+    if (threadIdx.x == 0) {
+        if (i == INT_MAX) i = 0;  // every value was NaN
+        const int pos = st->pos;
+        st->next = i;
+        if (tokens_out) tokens_out[pos] = i;
+        st->token = i;
+        st->pos = pos + 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-vector family.
+//
+// A block of NT threads owns a contiguous range of row groups.  Thread t holds
+// float4 number t + k*NT of the input vector (k < NX) in registers for the
+// whole block, so x (and its RMSNorm) is read and computed once per block.
+// Per iteration the block streams RPI weight rows: every thread issues RPI*NX
+// independent 16-byte loads (coalesced: consecutive threads read consecutive
+// 16 bytes of a row), multiplies with its x slice, and the row sums are
+// reduced with DPP inside each wave and through LDS across waves.  The LDS
+// slots are double-buffered so one barrier per iteration suffices.
+//
+// The weights do not depend on x, so their loads are issued early: the first
+// row group's before the x prologue (load, RMSNorm), and each next group's as
+// soon as the current group's products are formed, so that they are in flight
+// during the reduction, the barrier and the epilogue.
+
+#ifndef LD_NT_LOADS
+#define LD_NT_LOADS 1  // weight loads carry the non-temporal hint (each is used once)
+#endif
+
+typedef float native_float4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_w(const float4* p) {
+#if LD_NT_LOADS
+    const native_float4 v = __builtin_nontemporal_load(reinterpret_cast<const native_float4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
+}
+
+// Rows of row group u.  K_SWIGLU interleaves w1 and w3 rows of the same
+// hidden unit; K_QKV walks the three matrices wq | wk | wv as one.
+template <int RPI, int KIND>
+__device__ __forceinline__ void group_rows(const GemvParams& p, int u, const float* (&wr)[RPI]) {
+    const size_t n = (size_t)p.n;
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) {
+        if constexpr (KIND == K_SWIGLU) {
+            const int e = min(u * (RPI / 2) + r / 2, p.rows - 1);
+            wr[r] = ((r & 1) ? p.w1 : p.w0) + (size_t)e * n;
+        } else if constexpr (KIND == K_QKV) {
+            const int row = min(u * RPI + r, p.rows - 1);
+            wr[r] = row < p.seg1   ? p.w0 + (size_t)row * n
+                    : row < p.seg2 ? p.w1 + (size_t)(row - p.seg1) * n
+                                   : p.w2 + (size_t)(row - p.seg2) * n;
+        } else {
+            const int row = min(u * RPI + r, p.rows - 1);
+            wr[r] = p.w0 + (size_t)row * n;
+        }
+    }
+}
+
+__device__ __forceinline__ float4 zero_unless(bool keep, float4 v) {
+    return make_float4(keep ? v.x : 0.f, keep ? v.y : 0.f, keep ? v.z : 0.f, keep ? v.w : 0.f);
+}
+
+// Lanes past the end of a row load the row's last float4 again (always in
+// bounds) and multiply it by their x slice, which is zero there: the weight
+// loads stay unconditional and need no select, so none of them is waited for
+// before its use.  (With finite weights the extra products are exactly 0; a
+// non-finite weight in the last float4 of a row makes the row non-finite
+// either way.)
+template <int NT, int NX, int RPI, int KIND>
+__device__ __forceinline__ void load_group(const GemvParams& p, int u, int n4, float4 (&w)[RPI][NX]) {
+    const float* wr[RPI];
+    group_rows<RPI, KIND>(p, u, wr);
+#pragma unroll
+    for (int k = 0; k < NX; ++k) {
+        const int at = min((int)threadIdx.x + k * NT, n4 - 1);
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) w[r][k] = load_w(reinterpret_cast<const float4*>(wr[r]) + at);
+    }
+}
+
+template <int NT, int NX, int RPI, int KIND>
+__global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
+    constexpr int NW = NT / 64;
+    __shared__ float red[2][NW][RPI];
+    __shared__ float ss_part[NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n4 = p.n >> 2;
+
+    // row groups of this block (an even split of p.units over the grid)
+    const int u0 = (int)(((long long)blockIdx.x * p.units) / gridDim.x);
+    const int u1 = (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    float4 w[RPI][NX];
+    if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
+
+    int pos = 0, token = 0;
+    if constexpr (KIND == K_QKV || KIND == K_CLS) {
+        pos = p.state->pos;
+        token = p.state->token;
+    }
+
+    // ---- prologue: x (layer 0 of the q/k/v kernel reads the embedding row) ----
+    const float* xsrc = p.x;
+    if constexpr (KIND == K_QKV) {
+        if (p.emb) xsrc = p.emb + (size_t)token * (size_t)p.n;
+    }
+    const float4* x4 = reinterpret_cast<const float4*>(xsrc);
+    float4 xr[NX];
+#pragma unroll
+    for (int k = 0; k < NX; ++k) {
+        const int idx = tid + k * NT;
+        xr[k] = zero_unless(idx < n4, x4[min(idx, n4 - 1)]);
+    }
+    if constexpr (KIND == K_QKV) {
+        if (p.emb && blockIdx.x == 0) {
+            float4* xo = reinterpret_cast<float4*>(p.x_resid);
+#pragma unroll
+            for (int k = 0; k < NX; ++k) {
+                const int idx = tid + k * NT;
+                if (idx < n4) xo[idx] = xr[k];
+            }
+        }
+    }
+    // RMSNorm: x' = g * (x * 1/sqrt(mean(x^2) + eps))
+    if (p.gain) {
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < NX; ++k) ss = dot4(xr[k], xr[k], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) ss_part[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) tot += ss_part[w2];
+        const float r = 1.0f / sqrtf(tot / (float)p.n + p.eps);
+        const float4* g4 = reinterpret_cast<const float4*>(p.gain);
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+            const int idx = tid + k * NT;
+            const float4 g = zero_unless(idx < n4, g4[min(idx, n4 - 1)]);
+            xr[k] = make_float4(g.x * (r * xr[k].x), g.y * (r * xr[k].y), g.z * (r * xr[k].z), g.w * (r * xr[k].w));
+        }
+    }
+
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    int buf = 0;
+    for (int u = u0; u < u1; ++u) {
+        float acc[RPI];
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) {
+            acc[r] = 0.f;
+#pragma unroll
+            for (int k = 0; k < NX; ++k) acc[r] = dot4(w[r][k], xr[k], acc[r]);
+        }
+        // keep the next group's loads after these products: hoisting them
+        // would hold two groups of weights in registers at once
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < u1) load_group<NT, NX, RPI, KIND>(p, u + 1, n4, w);
+#pragma unroll
+        for (int r = 0; r < RPI; ++r) acc[r] = wave_sum(acc[r]);
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) red[buf][wave][r] = acc[r];
+        }
+        __syncthreads();
+        float total = 0.f;
+        if (tid < RPI) {
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) total += red[buf][w2][tid];
+        }
+        buf ^= 1;
+
+        // ---- epilogues (row u*RPI + tid lives in thread tid < RPI) ----
+        if constexpr (KIND == K_PLAIN) {
+            const int row = u * RPI + tid;
+            if (tid < RPI && row < p.rows) p.out[row] = total;
+        } else if constexpr (KIND == K_RESID) {
+            const int row = u * RPI + tid;
+            if (tid < RPI && row < p.rows) p.x_resid[row] += total;
+        } else if constexpr (KIND == K_QKV) {
+            // RoPE ("run.c 逐行解讀" §4 step 2d): rows 2j, 2j+1 of a head form
+            // one pair, turned by the angle pos * theta^(-2j/head_size); the
+            // (cos, sin) of that angle come from the table.  q rows are
+            // rotated, k rows are rotated and written to cache row pos, v rows
+            // go to the value cache unrotated (step 2b).
+            const float other = __shfl_xor(total, 1);
+            const int row = u * RPI + tid;
+            if (tid < RPI && row < p.rows) {
+                const bool odd = tid & 1;
+                if (row < p.seg2) {
+                    const bool is_q = row < p.seg1;
+                    const int local = is_q ? row : row - p.seg1;
+                    const int hs = p.head_size;
+                    const int j = (local % hs) >> 1;
+                    const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + j];
+                    const float a = odd ? other : total;  // element 2j
+                    const float b = odd ? total : other;  // element 2j+1
+                    const float v = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
+                    if (is_q)
+                        p.out[row] = v;
+                    else
+                        p.kc[(size_t)pos * p.kv_stride + local] = v;
+                } else {
+                    p.vc[(size_t)pos * p.kv_stride + (row - p.seg2)] = total;
+                }
+            }
+        } else if constexpr (KIND == K_SWIGLU) {
+            // hb = silu(w1 x) * (w3 x), silu(u) = u * 1/(1 + e^-u) ("run.c
+            // 逐行解讀" §4 step 2h).  Even threads hold the w1 row, odd the w3 row.
+            const float other = __shfl_xor(total, 1);
+            const int e = u * (RPI / 2) + (tid >> 1);
+            if (tid < RPI && !(tid & 1) && e < p.rows) {
+                float a = total;
+                a *= 1.0f / (1.0f + expf(-a));
+                a *= other;
+                p.out[e] = a;
+            }
+        } else if constexpr (KIND == K_CLS) {
+            const int row = u * RPI + tid;
+            if (tid < RPI && row < p.rows) {
+                p.out[row] = total;
+                if (better(total, row, bv, bi)) {
+                    bv = total;
+                    bi = row;
+                }
+            }
+        }
+    }
+
+    if constexpr (KIND == K_CLS) publish_best<NT>(bv, bi, p.best);
+}
+
+// Argmax of a vector: per-block bests (the reduction the classifier uses),
+// then argmax_final_kernel.
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const float* v, int n, float2* best) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int i = blockIdx.x * kArgmaxThreads + threadIdx.x; i < n; i += gridDim.x * kArgmaxThreads)
+        if (better(v[i], i, bv, bi)) {
+            bv = v[i];
+            bi = i;
+        }
+    publish_best<kArgmaxThreads>(bv, bi, best);
+}
+
+__global__ void set_state_kernel(StepState* st, int token, int pos) {
+    st->token = token;
+    st->pos = pos;
+    st->next = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Causal grouped-query attention at one position ("run.c 逐行解讀" §4 step
+// 2e), split along the key axis (flash-decoding).
+//
+// The n = pos+1 keys form tiles of CH rows.  Block (g, s) serves kv head g and
+// a contiguous run of tiles; at small n each block gets one tile and blocks
+// past the last tile exit at once, so one launch shape serves every position.
+// For each tile the block stages the key and value rows in LDS (coalesced
+// 16-byte loads), scores them against every query head h with
+// floor(h*KV/H) = g (the group shares the staged rows), and folds them into a
+// running max m, exp-sum l and unnormalised value sum (online softmax: when m
+// grows, l and the sum are rescaled by e^{m_old - m_new}).  The next tile's
+// loads are issued before the current tile is computed, so the block keeps
+// HBM requests in flight throughout.  Each block leaves (m, l, sum) as a
+// partial; attn_merge_kernel combines them exactly:
+// out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, M = max_s m_s.
+//
+// All 256 threads work in every phase: a (head, key) score is split over up to
+// 16 threads when the group is small, and the value sum over key groups whose
+// float4 partials are added through LDS at the end.
+
+__device__ __forceinline__ void group_of(int g, int H, int KV, int& h_lo, int& G) {
+    h_lo = (g * H + KV - 1) / KV;              // ceil(g H / KV)
+    G = ((g + 1) * H + KV - 1) / KV - h_lo;    // query heads with floor(h KV / H) = g
+}
+
+// Tiles of a position: `per` consecutive tiles per split, `nact` splits in use.
+__device__ __forceinline__ void split_of(int n, int ch, int nsplit, int& tiles, int& per, int& nact) {
+    tiles = (n + ch - 1) / ch;
+    per = (tiles + nsplit - 1) / nsplit;
+    nact = (tiles + per - 1) / per;
+}
+
+template <int HS, int CH>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
+    constexpr int H4 = HS / 4;
+    constexpr int KP = HS + 4;  // padded LDS row
+    constexpr int NLOAD = (CH * H4 + kAttnThreads - 1) / kAttnThreads;
+    constexpr int NACC = (kMaxGroup * H4 + kAttnThreads - 1) / kAttnThreads;  // float4 outputs per thread
+    __shared__ float4 q_s[kMaxGroup][H4];
+    __shared__ __align__(16) float k_s[CH * KP];
+    __shared__ __align__(16) float v_s[CH * KP];
+    __shared__ float p_s[kMaxGroup][CH];
+    __shared__ float m_s[kMaxGroup], l_s[kMaxGroup], r_s[kMaxGroup];
+    __shared__ float4 red_s[kAttnThreads];
+
+    const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = p.state->pos + 1;
+    int tiles, per, nact;
+    split_of(n, CH, p.nsplit, tiles, per, nact);
+    if (s >= nact) return;
+    const int tile0 = s * per, tile1 = min(tiles, tile0 + per);
+    int h_lo, G;
+    group_of(g, p.n_heads, p.n_kv_heads, h_lo, G);
+    const float* kbase = p.kc + (size_t)g * HS;
+    const float* vbase = p.vc + (size_t)g * HS;
+
+    // first tile's loads, then q
+    float4 kk[NLOAD], vv[NLOAD];
+    auto load_tile = [&](int tile) {
+        const int t0 = tile * CH, nt = min(CH, n - t0);
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int e = tid + i * kAttnThreads;
+            const int t = min(e / H4, nt - 1), c = e % H4;  // rows past the tile re-read its last row
+            const size_t off = (size_t)(t0 + t) * p.kv_dim + (size_t)c * 4;
+            kk[i] = *reinterpret_cast<const float4*>(kbase + off);
+            vv[i] = *reinterpret_cast<const float4*>(vbase + off);
+        }
+    };
+    load_tile(tile0);
+    const float4* q4 = reinterpret_cast<const float4*>(p.q);
+    for (int e = tid; e < G * H4; e += kAttnThreads) q_s[e / H4][e % H4] = q4[(size_t)h_lo * H4 + e];
+    if (tid < kMaxGroup) {
+        m_s[tid] = -INFINITY;
+        l_s[tid] = 0.f;
+    }
+
+    // value-sum mapping: float4 output slot o (head o / H4, column o % H4), key group kg
+    const int slots = G * H4;
+    const int KG = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    const int kg = slots < kAttnThreads ? tid / slots : 0;
+    float4 acc[NACC];
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // score mapping: tpp threads per (head, key) pair
+    const int P = G * CH;
+    int tpp = 1;
+    while (tpp < 16 && P * tpp * 2 <= kAttnThreads) tpp *= 2;
+    const int per_pass = kAttnThreads / tpp, passes = (P + per_pass - 1) / per_pass, sub = tid % tpp;
+    const float scale = 1.0f / sqrtf((float)HS);
+
+    for (int tile = tile0; tile < tile1; ++tile) {
+        const int t0 = tile * CH, nt = min(CH, n - t0);
+        __syncthreads();  // the previous tile is no longer read from LDS
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int e = tid + i * kAttnThreads;
+            if (e < CH * H4) {
+                const int t = e / H4, c = e % H4;
+                *reinterpret_cast<float4*>(&k_s[t * KP + c * 4]) = kk[i];
+                *reinterpret_cast<float4*>(&v_s[t * KP + c * 4]) = vv[i];
+            }
+        }
+        __syncthreads();
+        if (tile + 1 < tile1) load_tile(tile + 1);  // in flight while this tile is computed
+
+        // scores s_t = q_h . k_t / sqrt(head_size)
+        for (int it = 0; it < passes; ++it) {
+            const int pair = it * per_pass + tid / tpp;
+            const int hh = pair / CH, t = pair % CH;
+            float a = 0.f;
+            if (pair < P && t < nt) {
+                for (int c = sub; c < H4; c += tpp)
+                    a = dot4(*reinterpret_cast<const float4*>(&k_s[t * KP + c * 4]), q_s[hh][c], a);
+            }
+            for (int off = tpp >> 1; off > 0; off >>= 1) a += __shfl_xor(a, off);
+            if (pair < P && sub == 0) p_s[hh][t] = t < nt ? a * scale : -INFINITY;
+        }
+        __syncthreads();
+
+        // online softmax: new running max, weights e^{s - m}, rescale factor
+        for (int hh = wave; hh < G; hh += kAttnThreads / 64) {
+            const float sc = lane < CH ? p_s[hh][lane] : -INFINITY;
+            const float m_old = m_s[hh];
+            const float m_new = fmaxf(m_old, wave_max(sc));
+            const float e = lane < nt ? __expf(sc - m_new) : 0.f;
+            const float sum = wave_sum(e);
+            if (lane < CH) p_s[hh][lane] = e;
+            if (lane == 0) {
+                const float r = __expf(m_old - m_new);  // 0 on the first tile
+                r_s[hh] = r;
+                l_s[hh] = l_s[hh] * r + sum;
+                m_s[hh] = m_new;
+            }
+        }
+        __syncthreads();
+
+        // value sum: acc = acc * r + sum_t e_t v_t over this thread's keys
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            const int o = slots < kAttnThreads ? tid % slots : tid + j * kAttnThreads;
+            if ((slots < kAttnThreads ? kg < KG : o < slots) && (j == 0 || slots >= kAttnThreads)) {
+                const int hh = o / H4, c = o % H4;
+                const float r = r_s[hh];
+                float4 a = make_float4(acc[j].x * r, acc[j].y * r, acc[j].z * r, acc[j].w * r);
+                for (int t = kg; t < nt; t += KG) {
+                    const float pw = p_s[hh][t];
+                    const float4 v = *reinterpret_cast<const float4*>(&v_s[t * KP + c * 4]);
+                    a = make_float4(fmaf(pw, v.x, a.x), fmaf(pw, v.y, a.y), fmaf(pw, v.z, a.z), fmaf(pw, v.w, a.w));
+                }
+                acc[j] = a;
+            }
+        }
+    }
+
+    // this split's partial: (m, l) per head and the value sum
+    float4* part4 = reinterpret_cast<float4*>(p.part_acc);
+    if (slots >= kAttnThreads) {
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            const int o = tid + j * kAttnThreads;
+            if (o < slots) part4[((size_t)(h_lo + o / H4) * p.nsplit + s) * H4 + o % H4] = acc[j];
+        }
+    } else {
+        red_s[tid] = acc[0];
+        __syncthreads();
+        if (tid < slots) {
+            float4 a = acc[0];
+            for (int k = 1; k < KG; ++k) {
+                const float4 b = red_s[k * slots + tid];
+                a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+            }
+            part4[((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4] = a;
+        }
+    }
+    if (tid < G) p.part_ml[(size_t)(h_lo + tid) * p.nsplit + s] = make_float2(m_s[tid], l_s[tid]);
+}
+
+// Exact merge of the split partials of the query heads of kv head blockIdx.x.
+template <int HS>
+__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams p) {
+    constexpr int H4 = HS / 4;
+    __shared__ float m_s[kMaxGroup], l_s[kMaxGroup];
+    __shared__ float4 red_s[kAttnThreads];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int tiles, per, nact, h_lo, G;
+    split_of(p.state->pos + 1, p.chunk, p.nsplit, tiles, per, nact);
+    group_of(blockIdx.x, p.n_heads, p.n_kv_heads, h_lo, G);
+
+    for (int hh = wave; hh < G; hh += kAttnThreads / 64) {
+        const float2* ml = p.part_ml + (size_t)(h_lo + hh) * p.nsplit;
+        float m = -INFINITY;
+        for (int sp = lane; sp < nact; sp += 64) m = fmaxf(m, ml[sp].x);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int sp = lane; sp < nact; sp += 64) {
+            const float2 e = ml[sp];
+            l = fmaf(e.y, __expf(e.x - m), l);
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            m_s[hh] = m;
+            l_s[hh] = l;
+        }
+    }
+    __syncthreads();
+    const int slots = G * H4;
+    const float4* acc4 = reinterpret_cast<const float4*>(p.part_acc);
+    float4* out4 = reinterpret_cast<float4*>(p.out);
+    const int KG = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    for (int o0 = 0; o0 < slots; o0 += kAttnThreads) {
+        const int o = slots < kAttnThreads ? tid % slots : o0 + tid;
+        const int kg = slots < kAttnThreads ? tid / slots : 0;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kg < KG && o < slots) {
+            const int hh = o / H4, c = o % H4, h = h_lo + hh;
+            const float2* ml = p.part_ml + (size_t)h * p.nsplit;
+            const float M = m_s[hh];
+#pragma unroll 4
+            for (int sp = kg; sp < nact; sp += KG) {
+                const float wgt = __expf(ml[sp].x - M);
+                const float4 v = acc4[((size_t)h * p.nsplit + sp) * H4 + c];
+                a = make_float4(fmaf(wgt, v.x, a.x), fmaf(wgt, v.y, a.y), fmaf(wgt, v.z, a.z), fmaf(wgt, v.w, a.w));
+            }
+        }
+        if (slots < kAttnThreads) {
+            red_s[tid] = a;
+            __syncthreads();
+            if (tid < slots) {
+                for (int k = 1; k < KG; ++k) {
+                    const float4 b = red_s[k * slots + tid];
+                    a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+                }
+            }
+        }
+        if ((slots < kAttnThreads ? tid < slots : o < slots)) {
+            const int hh = o / H4, c = o % H4;
+            const float il = 1.0f / l_s[hh];
+            out4[(size_t)(h_lo + hh) * H4 + c] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+
+struct Tpl {
+    int nt, nx, rpi;
+};
+
+// Ordered by capacity nt*nx float4 (= input floats / 4).  Two groups of
+// weights are live at once (the pipelined loads), so rpi*nx stays near 16.
+// The q/k/v and w1/w3 kernels pair rows and use at least 2 rows per group.
+constexpr Tpl kTpl[] = {
+    {64, 1, 4},    // n <= 256
+    {64, 2, 4},    // n <= 512
+    {64, 4, 4},    // n <= 1024
+    {256, 4, 4},   // n <= 4096
+    {256, 8, 2},   // n <= 8192
+    {256, 11, 1},  // n <= 11264
+    {256, 12, 1},  // n <= 12288
+    {512, 14, 1},  // n <= 28672
+    {512, 16, 1},  // n <= 32768
+};
+constexpr int kNumTpl = sizeof(kTpl) / sizeof(kTpl[0]);
+
+constexpr int rows_per_group(int t, int kind) {
+    return (kind == K_QKV || kind == K_SWIGLU) && kTpl[t].rpi < 2 ? 2 : kTpl[t].rpi;
+}
+
+using GemvFn = void (*)(GemvParams);
+
+template <int KIND, int T>
+GemvFn gemv_fn_t() {
+    return gemv_kernel<kTpl[T].nt, kTpl[T].nx, rows_per_group(T, KIND), KIND>;
+}
+
+template <int KIND>
+GemvFn gemv_fn(int t) {
+    switch (t) {
+        case 0: return gemv_fn_t<KIND, 0>();
+        case 1: return gemv_fn_t<KIND, 1>();
+        case 2: return gemv_fn_t<KIND, 2>();
+        case 3: return gemv_fn_t<KIND, 3>();
+        case 4: return gemv_fn_t<KIND, 4>();
+        case 5: return gemv_fn_t<KIND, 5>();
+        case 6: return gemv_fn_t<KIND, 6>();
+        case 7: return gemv_fn_t<KIND, 7>();
+        case 8: return gemv_fn_t<KIND, 8>();
+    }
+    return nullptr;
+}
+
+GemvFn gemv_fn_kind(int kind, int t) {
+    switch (kind) {
+        case K_PLAIN: return gemv_fn<K_PLAIN>(t);
+        case K_RESID: return gemv_fn<K_RESID>(t);
+        case K_QKV: return gemv_fn<K_QKV>(t);
+        case K_SWIGLU: return gemv_fn<K_SWIGLU>(t);
+        case K_CLS: return gemv_fn<K_CLS>(t);
+    }
+    return nullptr;
+}
+
+int template_for(const GemvPlan& pl) {
+    for (int t = 0; t < kNumTpl; ++t)
+        if (kTpl[t].nt == pl.nt && kTpl[t].nx == pl.nx && rows_per_group(t, pl.kind) == pl.rpi) return t;
+    return -1;
+}
+
+// Largest divisor of `units` in [lo, hi], or 0.
+int divisor_in(int units, int lo, int hi) {
+    for (int g = hi; g >= lo && g >= 1; --g)
+        if (units % g == 0) return g;
+    return 0;
+}
+
+}  // namespace
+
+hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan) {
+    if (n <= 0 || rows <= 0 || (n & 3) || n > kMaxN) return hipErrorInvalidValue;
+    const int n4 = n / 4;
+    int t = 0;
+    while (t < kNumTpl && kTpl[t].nt * kTpl[t].nx < n4) ++t;
+    if (t == kNumTpl) return hipErrorInvalidValue;
+    const Tpl tp = kTpl[t];
+    const int rpi = rows_per_group(t, kind);
+    const int per_iter = kind == K_SWIGLU ? rpi / 2 : rpi;
+    plan->kind = kind;
+    plan->nt = tp.nt;
+    plan->nx = tp.nx;
+    plan->rpi = rpi;
+    plan->units = (rows + per_iter - 1) / per_iter;
+
+    int dev = 0, cus = 0, occ = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_fn_kind(kind, t), tp.nt, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    // One resident wave of blocks; when possible a grid that divides the row
+    // groups evenly, so that every block streams the same number of rows and
+    // none is left running alone at the end.
+    const int slots = cus * occ;
+    if (plan->units <= slots) {
+        plan->grid = plan->units;
+    } else {
+        const int even = divisor_in(plan->units, (slots + 1) / 2, slots);
+        plan->grid = even ? even : slots;
+    }
+    return hipSuccess;
+}
+
+hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s) {
+    const int t = template_for(plan);
+    if (t < 0) return hipErrorInvalidValue;
+    GemvParams p = p0;
+    p.units = plan.units;
+    hipLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    return hipGetLastError();
+}
+
+int attn_chunk(int hs) {
+    switch (hs) {
+        case 16:
+        case 32:
+        case 48:
+        case 64:
+        case 80:
+        case 96: return 64;
+        case 128: return 32;
+        case 256: return 16;
+    }
+    return 0;
+}
+
+int attn_splits(int hs, int seq_len, int n_kv_heads) {
+    const int ch = attn_chunk(hs);
+    if (!ch) return 0;
+    const int tiles = (seq_len + ch - 1) / ch;
+    // about 512 blocks at the longest context: two per compute unit, each
+    // walking several tiles so that its loads stay in flight
+    int want = (512 + n_kv_heads - 1) / n_kv_heads;
+    if (want < 1) want = 1;
+    return want < tiles ? want : tiles;
+}
+
+hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
+    AttnParams p = p0;
+    p.chunk = attn_chunk(hs);
+    const dim3 grid(p.n_kv_heads, p.nsplit), block(kAttnThreads);
+    switch (hs) {
+#define LD_ATTN_CASE(HS, CH)                                                               \
+    case HS:                                                                               \
+        hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);                   \
+        hipLaunchKernelGGL((attn_merge_kernel<HS>), dim3(p.n_kv_heads), block, 0, s, p);   \
+        break;
+        LD_ATTN_CASE(16, 64)
+        LD_ATTN_CASE(32, 64)
+        LD_ATTN_CASE(48, 64)
+        LD_ATTN_CASE(64, 64)
+        LD_ATTN_CASE(80, 64)
+        LD_ATTN_CASE(96, 64)
+        LD_ATTN_CASE(128, 32)
+        LD_ATTN_CASE(256, 16)
+#undef LD_ATTN_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s) {
+    hipLaunchKernelGGL(set_state_kernel, dim3(1), dim3(1), 0, s, st, token, pos);
+    return hipGetLastError();
+}
+
+int argmax_blocks(int n) {
+    int b = (n + kArgmaxThreads * 8 - 1) / (kArgmaxThreads * 8);
+    return b < 1 ? 1 : (b > 1024 ? 1024 : b);
+}
+
+hipError_t argmax_launch(const float* v, int n, float2* best, int nblocks, StepState* st, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_partial_kernel, dim3(nblocks), dim3(kArgmaxThreads), 0, s, v, n, best);
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, s, best, nblocks, st, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t argmax_final_launch(const float2* best, int nblocks, StepState* st, int32_t* tokens_out, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, s, best, nblocks, st, tokens_out);
+    return hipGetLastError();
+}
+
+}  // namespace ld

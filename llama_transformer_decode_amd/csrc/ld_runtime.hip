@@ -1,0 +1,747 @@
+// ld_runtime.hip -- the C ABI of include/ld.h: validation, device buffer
+// plan, the launch sequence of one decode step, HIP-graph capture/replay.
+//
+// One decode step ("run.c 逐行解讀" §4, forward()) is 5 launches per layer plus
+// one: per layer
+//   qkv_rope_append  RMSNorm(x) -> [Wq;Wk;Wv] -> RoPE -> q, cache row pos
+//                    (layer 0 also copies the embedding row into x)
+//   attention        split-key GQA attention over rows 0..pos -> xb
+//   wo_residual      x += Wo xb
+//   w1w3_swiglu      RMSNorm(x) -> silu(W1 .) * (W3 .) -> hb
+//   w2_residual      x += W2 hb
+// then classifier_argmax: RMSNorm(x) -> Wcls -> logits -> greedy token.
+// Token and position live in device memory, so the same captured graph
+// replays every step of a greedy generation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ld.h"
+#include "ld_internal.h"
+
+using namespace ld;
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail_hip(hipError_t e, const char* what) {
+    std::snprintf(g_detail, sizeof(g_detail), "%s: %s", what, hipGetErrorString(e));
+    return e == hipErrorOutOfMemory ? LD_E_OOM : LD_E_HIP;
+}
+
+#define HIP_TRY(call)                                         \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return fail_hip(e_, #call);     \
+    } while (0)
+
+bool supported_head_size(int hs) { return attn_chunk(hs) > 0; }
+
+int validate(const ld_config* c, const ld_options* o) {
+    if (!c || !o) return LD_E_NULL;
+    if (c->dim <= 0 || c->hidden_dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->vocab_size <= 0 || c->seq_len <= 0)
+        return LD_E_CONFIG;
+    if (c->dim % c->n_heads) return LD_E_CONFIG;
+    const int hs = c->dim / c->n_heads;
+    if (hs % 2) return LD_E_CONFIG;
+    if (c->n_kv_heads > c->n_heads) return LD_E_CONFIG;
+    if (((long long)c->dim * c->n_kv_heads) % c->n_heads) return LD_E_CONFIG;
+    const long long kv = (long long)c->dim * c->n_kv_heads / c->n_heads;
+    if ((c->dim % 4) || (c->hidden_dim % 4) || (kv % 4)) return LD_E_CONFIG;
+    if (!(o->norm_eps >= 0.f) || !(o->rope_theta > 0.f) || !std::isfinite(o->rope_theta)) return LD_E_CONFIG;
+    if (o->shared_classifier != 0 && o->shared_classifier != 1) return LD_E_CONFIG;
+    if (!supported_head_size(hs)) return LD_E_UNSUPPORTED;
+    const int group = (c->n_heads + c->n_kv_heads - 1) / c->n_kv_heads;
+    if (group > kMaxGroup) return LD_E_UNSUPPORTED;
+    if (c->dim > kMaxN || c->hidden_dim > kMaxN) return LD_E_UNSUPPORTED;
+    return LD_OK;
+}
+
+// Blob size in floats (tensor order of the header comment).
+long long blob_floats(const ld_config* c, const ld_options* o) {
+    const long long d = c->dim, h = c->hidden_dim, L = c->n_layers, V = c->vocab_size;
+    const long long kv = d * c->n_kv_heads / c->n_heads;
+    long long f = V * d;                 // embedding
+    f += L * d;                          // rms_att
+    f += L * d * d + 2 * L * kv * d;     // wq, wk, wv
+    f += L * d * d;                      // wo
+    f += L * d;                          // rms_ffn
+    f += 3 * L * h * d;                  // w1, w2, w3
+    f += d;                              // rms_final
+    if (!o->shared_classifier) f += V * d;
+    return f;
+}
+
+enum Kind { KQKV = 0, KATTN, KWO, KFFN, KW2, KCLS, KNUM };
+const char* kKindName[KNUM] = {"qkv_rope_append", "attention", "wo_residual",
+                               "w1w3_swiglu",     "w2_residual", "classifier_argmax"};
+
+// Events around each launch, for ld_profile_steps.
+struct Timer {
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> kind;
+    size_t used = 0;
+};
+
+}  // namespace
+
+struct ld_model {
+    ld_config cfg{};
+    ld_options opt{};
+    int device = 0;
+    int hs = 0, kv_dim = 0, nsplit = 0;
+    const float *emb = nullptr, *rms_att = nullptr, *wq = nullptr, *wk = nullptr, *wv = nullptr, *wo = nullptr,
+                *rms_ffn = nullptr, *w1 = nullptr, *w2 = nullptr, *w3 = nullptr, *rms_final = nullptr,
+                *wcls = nullptr;
+    float *x = nullptr, *xb = nullptr, *q = nullptr, *hb = nullptr, *logits = nullptr;
+    float *kc = nullptr, *vc = nullptr, *part_acc = nullptr;
+    float2 *part_ml = nullptr, *rope = nullptr, *best = nullptr;
+    StepState* state = nullptr;
+    int32_t* tokens = nullptr;     // tokens[pos] = argmax of step pos
+    int32_t* h_tokens = nullptr;   // pinned staging
+    GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
+    hipStream_t stream = nullptr, user = nullptr;
+    hipEvent_t ev_in = nullptr, ev_out = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    bool use_graph = true;
+    std::vector<void*> dev_allocs;
+};
+
+namespace {
+
+template <class T>
+int dalloc(ld_model* m, T** p, size_t count) {
+    void* q = nullptr;
+    hipError_t e = hipMalloc(&q, count * sizeof(T) < 256 ? 256 : count * sizeof(T));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc");
+    m->dev_allocs.push_back(q);
+    *p = static_cast<T*>(q);
+    return LD_OK;
+}
+
+void release(ld_model* m) {
+    if (!m) return;
+    (void)hipSetDevice(m->device);
+    if (m->stream) (void)hipStreamSynchronize(m->stream);
+    if (m->exec) (void)hipGraphExecDestroy(m->exec);
+    if (m->graph) (void)hipGraphDestroy(m->graph);
+    for (void* p : m->dev_allocs) (void)hipFree(p);
+    if (m->h_tokens) (void)hipHostFree(m->h_tokens);
+    if (m->ev_in) (void)hipEventDestroy(m->ev_in);
+    if (m->ev_out) (void)hipEventDestroy(m->ev_out);
+    if (m->stream) (void)hipStreamDestroy(m->stream);
+    delete m;
+}
+
+// Order the model's stream after the caller's queued work, and back.
+int enter(ld_model* m) {
+    HIP_TRY(hipSetDevice(m->device));
+    HIP_TRY(hipEventRecord(m->ev_in, m->user));
+    HIP_TRY(hipStreamWaitEvent(m->stream, m->ev_in, 0));
+    return LD_OK;
+}
+
+int leave(ld_model* m) {
+    HIP_TRY(hipEventRecord(m->ev_out, m->stream));
+    HIP_TRY(hipStreamWaitEvent(m->user, m->ev_out, 0));
+    return LD_OK;
+}
+
+// RoPE table: entry (p, j) = (cos, sin) of p * theta^(-2j/head_size) for the
+// pair (2j, 2j+1) of every head ("run.c 逐行解讀" §4 step 2d: freq =
+// 1/theta^(head_dim/head_size), angle = pos * freq), evaluated in double and
+// rounded once, so the angle carries no fp32 error at large positions.
+std::vector<float2> rope_table(int positions, int hs, double theta) {
+    std::vector<float2> t((size_t)positions * (hs / 2));
+    for (int p = 0; p < positions; ++p)
+        for (int j = 0; j < hs / 2; ++j) {
+            const double freq = 1.0 / std::pow(theta, (2.0 * j) / (double)hs);
+            const double ang = (double)p * freq;
+            t[(size_t)p * (hs / 2) + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+    return t;
+}
+
+GemvParams base_params(const ld_model* m) {
+    GemvParams p{};
+    p.eps = m->opt.norm_eps;
+    p.state = m->state;
+    return p;
+}
+
+void mark(Timer* t, hipStream_t s, int kind, bool before) {
+    if (!t) return;
+    if (before) {
+        t->kind[t->used / 2] = kind;
+    }
+    (void)hipEventRecord(t->ev[t->used++], s);
+}
+
+// One decode step, reading (token, pos) from m->state.
+int launch_step(ld_model* m, Timer* timer) {
+    const ld_config& c = m->cfg;
+    const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
+    const size_t cache_layer = (size_t)c.seq_len * kv;
+    hipStream_t s = m->stream;
+    for (int l = 0; l < c.n_layers; ++l) {
+        {
+            GemvParams p = base_params(m);
+            p.x = m->x;
+            p.emb = l == 0 ? m->emb : nullptr;
+            p.x_resid = m->x;
+            p.gain = m->rms_att + (size_t)l * d;
+            p.n = c.dim;
+            p.rows = c.dim + 2 * m->kv_dim;
+            p.w0 = m->wq + (size_t)l * d * d;
+            p.w1 = m->wk + (size_t)l * kv * d;
+            p.w2 = m->wv + (size_t)l * kv * d;
+            p.seg1 = c.dim;
+            p.seg2 = c.dim + m->kv_dim;
+            p.out = m->q;
+            p.kc = m->kc + (size_t)l * cache_layer;
+            p.vc = m->vc + (size_t)l * cache_layer;
+            p.kv_stride = m->kv_dim;
+            p.head_size = m->hs;
+            p.rope = m->rope;
+            mark(timer, s, KQKV, true);
+            HIP_TRY(gemv_launch(m->pq, p, s));
+            mark(timer, s, KQKV, false);
+        }
+        {
+            AttnParams a{};
+            a.q = m->q;
+            a.kc = m->kc + (size_t)l * cache_layer;
+            a.vc = m->vc + (size_t)l * cache_layer;
+            a.out = m->xb;
+            a.part_ml = m->part_ml;
+            a.part_acc = m->part_acc;
+            a.state = m->state;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            a.kv_dim = m->kv_dim;
+            a.nsplit = m->nsplit;
+            mark(timer, s, KATTN, true);
+            HIP_TRY(attn_launch(m->hs, a, s));
+            mark(timer, s, KATTN, false);
+        }
+        {
+            GemvParams p = base_params(m);
+            p.x = m->xb;
+            p.x_resid = m->x;
+            p.n = c.dim;
+            p.rows = c.dim;
+            p.w0 = m->wo + (size_t)l * d * d;
+            mark(timer, s, KWO, true);
+            HIP_TRY(gemv_launch(m->pwo, p, s));
+            mark(timer, s, KWO, false);
+        }
+        {
+            GemvParams p = base_params(m);
+            p.x = m->x;
+            p.gain = m->rms_ffn + (size_t)l * d;
+            p.n = c.dim;
+            p.rows = c.hidden_dim;
+            p.w0 = m->w1 + (size_t)l * h * d;
+            p.w1 = m->w3 + (size_t)l * h * d;
+            p.out = m->hb;
+            mark(timer, s, KFFN, true);
+            HIP_TRY(gemv_launch(m->pffn, p, s));
+            mark(timer, s, KFFN, false);
+        }
+        {
+            GemvParams p = base_params(m);
+            p.x = m->hb;
+            p.x_resid = m->x;
+            p.n = c.hidden_dim;
+            p.rows = c.dim;
+            p.w0 = m->w2 + (size_t)l * d * h;
+            mark(timer, s, KW2, true);
+            HIP_TRY(gemv_launch(m->pw2, p, s));
+            mark(timer, s, KW2, false);
+        }
+    }
+    GemvParams p = base_params(m);
+    p.x = m->x;
+    p.gain = m->rms_final;
+    p.n = c.dim;
+    p.rows = c.vocab_size;
+    p.w0 = m->wcls;
+    p.out = m->logits;
+    p.best = m->best;
+    mark(timer, s, KCLS, true);
+    HIP_TRY(gemv_launch(m->pcls, p, s));
+    HIP_TRY(argmax_final_launch(m->best, m->pcls.grid, m->state, m->tokens, s));
+    mark(timer, s, KCLS, false);
+    return LD_OK;
+}
+
+int ensure_graph(ld_model* m) {
+    if (m->exec) return LD_OK;
+    HIP_TRY(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+    int rc = launch_step(m, nullptr);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(m->stream, &g);
+    if (rc != LD_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess) return fail_hip(e, "hipStreamEndCapture");
+    m->graph = g;
+    HIP_TRY(hipGraphInstantiate(&m->exec, m->graph, nullptr, nullptr, 0));
+    return LD_OK;
+}
+
+int run_step(ld_model* m) {
+    if (m->use_graph) {
+        int rc = ensure_graph(m);
+        if (rc != LD_OK) return rc;
+        HIP_TRY(hipGraphLaunch(m->exec, m->stream));
+        return LD_OK;
+    }
+    return launch_step(m, nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ld_strerror(int status) {
+    switch (status) {
+        case LD_OK: return "ok";
+        case LD_E_NULL: return "a required pointer argument is NULL";
+        case LD_E_CONFIG: return "invalid model configuration or options";
+        case LD_E_SIZE: return "weight blob has the wrong size";
+        case LD_E_ALIGN: return "device pointer is not 16-byte aligned";
+        case LD_E_RANGE: return "token, position or step count out of range";
+        case LD_E_OOM: return "device allocation failed";
+        case LD_E_HIP: return "HIP runtime call failed";
+        case LD_E_UNSUPPORTED: return "shape not covered by the compiled kernels";
+    }
+    return "unknown status";
+}
+
+const char* ld_last_error_detail(void) { return g_detail; }
+
+int ld_weights_size(const ld_config* cfg, const ld_options* opt, size_t* bytes_out) {
+    if (!cfg || !opt || !bytes_out) return LD_E_NULL;
+    const int v = validate(cfg, opt);
+    if (v == LD_E_CONFIG || v == LD_E_NULL) return v;
+    *bytes_out = (size_t)blob_floats(cfg, opt) * sizeof(float);
+    return LD_OK;
+}
+
+int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights, size_t bytes, void* hip_stream,
+              ld_model** out) {
+    if (!cfg || !opt || !d_weights || !out) return LD_E_NULL;
+    *out = nullptr;
+    const int v = validate(cfg, opt);
+    if (v != LD_OK) return v;
+    if ((size_t)blob_floats(cfg, opt) * sizeof(float) != bytes) return LD_E_SIZE;
+    if (reinterpret_cast<uintptr_t>(d_weights) % 16) return LD_E_ALIGN;
+
+    ld_model* m = new (std::nothrow) ld_model();
+    if (!m) return LD_E_OOM;
+    int rc = LD_OK;
+    do {
+        m->cfg = *cfg;
+        m->opt = *opt;
+        m->use_graph = !(opt->flags & LD_OPT_NO_GRAPH);
+        m->user = static_cast<hipStream_t>(hip_stream);
+        hipError_t e = hipGetDevice(&m->device);
+        if (e != hipSuccess) { rc = fail_hip(e, "hipGetDevice"); break; }
+        m->hs = cfg->dim / cfg->n_heads;
+        m->kv_dim = cfg->dim * cfg->n_kv_heads / cfg->n_heads;
+        m->nsplit = attn_splits(m->hs, cfg->seq_len, cfg->n_kv_heads);
+
+        // weight pointers: 64-bit offsets into the blob
+        const float* w = static_cast<const float*>(d_weights);
+        const size_t d = cfg->dim, h = cfg->hidden_dim, L = cfg->n_layers, V = cfg->vocab_size, kv = m->kv_dim;
+        size_t off = 0;
+        auto take = [&](size_t count) { const float* p = w + off; off += count; return p; };
+        m->emb = take(V * d);
+        m->rms_att = take(L * d);
+        m->wq = take(L * d * d);
+        m->wk = take(L * kv * d);
+        m->wv = take(L * kv * d);
+        m->wo = take(L * d * d);
+        m->rms_ffn = take(L * d);
+        m->w1 = take(L * h * d);
+        m->w2 = take(L * d * h);
+        m->w3 = take(L * h * d);
+        m->rms_final = take(d);
+        m->wcls = opt->shared_classifier ? m->emb : take(V * d);
+
+        e = hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking);
+        if (e != hipSuccess) { rc = fail_hip(e, "hipStreamCreate"); break; }
+        e = hipEventCreateWithFlags(&m->ev_in, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_out, hipEventDisableTiming);
+        if (e != hipSuccess) { rc = fail_hip(e, "hipEventCreate"); break; }
+
+        const size_t cache = (size_t)cfg->n_layers * cfg->seq_len * kv;
+        if ((rc = dalloc(m, &m->kc, cache)) || (rc = dalloc(m, &m->vc, cache)) || (rc = dalloc(m, &m->x, d)) ||
+            (rc = dalloc(m, &m->xb, d)) || (rc = dalloc(m, &m->q, d)) || (rc = dalloc(m, &m->hb, h)) ||
+            (rc = dalloc(m, &m->logits, V)) ||
+            (rc = dalloc(m, &m->part_acc, (size_t)cfg->n_heads * m->nsplit * m->hs)) ||
+            (rc = dalloc(m, &m->part_ml, (size_t)cfg->n_heads * m->nsplit)) ||
+            (rc = dalloc(m, &m->rope, (size_t)cfg->seq_len * (m->hs / 2))) ||
+            (rc = dalloc(m, &m->state, 1)) ||
+            (rc = dalloc(m, &m->tokens, (size_t)cfg->seq_len)))
+            break;
+        e = hipHostMalloc((void**)&m->h_tokens, sizeof(int32_t) * (size_t)cfg->seq_len, hipHostMallocDefault);
+        if (e != hipSuccess) { rc = fail_hip(e, "hipHostMalloc"); break; }
+
+        if ((rc = (gemv_plan(K_QKV, cfg->dim + 2 * m->kv_dim, cfg->dim, &m->pq) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
+            (rc = (gemv_plan(K_RESID, cfg->dim, cfg->dim, &m->pwo) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
+            (rc = (gemv_plan(K_SWIGLU, cfg->hidden_dim, cfg->dim, &m->pffn) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
+            (rc = (gemv_plan(K_RESID, cfg->dim, cfg->hidden_dim, &m->pw2) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
+            (rc = (gemv_plan(K_CLS, cfg->vocab_size, cfg->dim, &m->pcls) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED))
+            break;
+        rc = dalloc(m, &m->best, (size_t)m->pcls.grid);
+        if (rc) break;
+
+        std::vector<float2> rt = rope_table(cfg->seq_len, m->hs, (double)opt->rope_theta);
+        e = hipMemcpy(m->rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice);
+        if (e != hipSuccess) { rc = fail_hip(e, "hipMemcpy rope"); break; }
+        e = hipMemset(m->kc, 0, cache * sizeof(float));
+        if (e == hipSuccess) e = hipMemset(m->vc, 0, cache * sizeof(float));
+        if (e == hipSuccess) e = hipMemset(m->state, 0, sizeof(StepState));
+        if (e == hipSuccess) e = hipMemset(m->tokens, 0, sizeof(int32_t) * (size_t)cfg->seq_len);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) { rc = fail_hip(e, "initialise buffers"); break; }
+    } while (0);
+    if (rc != LD_OK) {
+        release(m);
+        return rc;
+    }
+    *out = m;
+    return LD_OK;
+}
+
+int ld_reset(ld_model* m) {
+    if (!m) return LD_E_NULL;
+    int rc = enter(m);
+    if (rc) return rc;
+    const size_t cache = (size_t)m->cfg.n_layers * m->cfg.seq_len * m->kv_dim * sizeof(float);
+    HIP_TRY(hipMemsetAsync(m->kc, 0, cache, m->stream));
+    HIP_TRY(hipMemsetAsync(m->vc, 0, cache, m->stream));
+    return leave(m);
+}
+
+int ld_forward(ld_model* m, int32_t token, int32_t pos, const float** d_logits_out) {
+    if (!m || !d_logits_out) return LD_E_NULL;
+    if (token < 0 || token >= m->cfg.vocab_size || pos < 0 || pos >= m->cfg.seq_len) return LD_E_RANGE;
+    int rc = enter(m);
+    if (rc) return rc;
+    HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
+    rc = run_step(m);
+    if (rc) return rc;
+    *d_logits_out = m->logits;
+    return leave(m);
+}
+
+int ld_argmax_last(ld_model* m, int32_t* h_token_out) {
+    if (!m || !h_token_out) return LD_E_NULL;
+    int rc = enter(m);
+    if (rc) return rc;
+    HIP_TRY(hipMemcpyAsync(m->h_tokens, &m->state->next, sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    *h_token_out = m->h_tokens[0];
+    return leave(m);
+}
+
+int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, int32_t* h_tokens_out) {
+    if (!m || (!h_tokens_out && n_steps > 0)) return LD_E_NULL;
+    if (token < 0 || token >= m->cfg.vocab_size || pos < 0 || n_steps < 0 ||
+        (long long)pos + n_steps > m->cfg.seq_len)
+        return LD_E_RANGE;
+    if (n_steps == 0) return LD_OK;
+    int rc = enter(m);
+    if (rc) return rc;
+    HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
+    for (int i = 0; i < n_steps; ++i) {
+        rc = run_step(m);
+        if (rc) return rc;
+    }
+    HIP_TRY(hipMemcpyAsync(m->h_tokens, m->tokens + pos, sizeof(int32_t) * (size_t)n_steps, hipMemcpyDeviceToHost,
+                           m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    std::memcpy(h_tokens_out, m->h_tokens, sizeof(int32_t) * (size_t)n_steps);
+    return leave(m);
+}
+
+int ld_kv_cache(ld_model* m, float** d_key_out, float** d_value_out, size_t* floats_out) {
+    if (!m || !d_key_out || !d_value_out || !floats_out) return LD_E_NULL;
+    *d_key_out = m->kc;
+    *d_value_out = m->vc;
+    *floats_out = (size_t)m->cfg.n_layers * m->cfg.seq_len * m->kv_dim;
+    return LD_OK;
+}
+
+void ld_destroy(ld_model* m) { release(m); }
+
+int ld_profile_steps(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, ld_kernel_stat* stats,
+                     int32_t max_stats, int32_t* n_stats_out) {
+    if (!m || !stats || !n_stats_out) return LD_E_NULL;
+    if (token < 0 || token >= m->cfg.vocab_size || pos < 0 || n_steps < 0 ||
+        (long long)pos + n_steps > m->cfg.seq_len)
+        return LD_E_RANGE;
+    int rc = enter(m);
+    if (rc) return rc;
+    const int launches = 5 * m->cfg.n_layers + 1;
+    Timer t;
+    t.ev.resize(2 * (size_t)launches, nullptr);
+    t.kind.resize(launches, 0);
+    for (auto& e : t.ev) {
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) {
+            for (auto& x : t.ev)
+                if (x) (void)hipEventDestroy(x);
+            return fail_hip(err, "hipEventCreate");
+        }
+    }
+    double total[KNUM] = {0};
+    int count[KNUM] = {0};
+    HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
+    for (int i = 0; i < n_steps && rc == LD_OK; ++i) {
+        t.used = 0;
+        rc = launch_step(m, &t);
+        if (rc) break;
+        hipError_t err = hipStreamSynchronize(m->stream);
+        if (err != hipSuccess) {
+            rc = fail_hip(err, "hipStreamSynchronize");
+            break;
+        }
+        for (int k = 0; k < launches; ++k) {
+            float ms = 0.f;
+            err = hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]);
+            if (err != hipSuccess) {
+                rc = fail_hip(err, "hipEventElapsedTime");
+                break;
+            }
+            total[t.kind[k]] += ms;
+            count[t.kind[k]] += 1;
+        }
+    }
+    for (auto& e : t.ev) (void)hipEventDestroy(e);
+    if (rc) return rc;
+    int n = 0;
+    for (int k = 0; k < KNUM && n < max_stats; ++k) {
+        std::memset(stats[n].name, 0, sizeof(stats[n].name));
+        std::strncpy(stats[n].name, kKindName[k], sizeof(stats[n].name) - 1);
+        stats[n].launches = count[k];
+        stats[n].total_ms = total[k];
+        ++n;
+    }
+    *n_stats_out = n;
+    return leave(m);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Single-kernel entry points (synchronous, own temporaries).
+
+namespace {
+
+struct Temps {
+    std::vector<void*> p;
+    ~Temps() {
+        for (void* q : p) (void)hipFree(q);
+    }
+    template <class T>
+    hipError_t get(T** out, size_t count) {
+        void* q = nullptr;
+        hipError_t e = hipMalloc(&q, (count ? count : 1) * sizeof(T));
+        if (e == hipSuccess) {
+            p.push_back(q);
+            *out = static_cast<T*>(q);
+        }
+        return e;
+    }
+};
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+int op_shape_ok(int rows, int n) {
+    if (rows <= 0 || n <= 0 || (n % 4)) return LD_E_CONFIG;
+    if (n > kMaxN) return LD_E_UNSUPPORTED;
+    return LD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ld_op_rmsnorm_gemv(const float* d_x, const float* d_g, float eps, const float* d_w, int32_t rows, int32_t n,
+                       float* d_out, void* hip_stream) {
+    if (!d_x || !d_w || !d_out) return LD_E_NULL;
+    if (int rc = op_shape_ok(rows, n)) return rc;
+    if (!aligned16(d_x) || !aligned16(d_w) || (d_g && !aligned16(d_g))) return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    GemvPlan pl;
+    HIP_TRY(gemv_plan(K_PLAIN, rows, n, &pl));
+    GemvParams p{};
+    p.x = d_x;
+    p.gain = d_g;
+    p.eps = eps;
+    p.n = n;
+    p.rows = rows;
+    p.w0 = d_w;
+    p.out = d_out;
+    HIP_TRY(gemv_launch(pl, p, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_gemv_residual(const float* d_in, const float* d_w, int32_t rows, int32_t n, float* d_x, void* hip_stream) {
+    if (!d_in || !d_w || !d_x) return LD_E_NULL;
+    if (int rc = op_shape_ok(rows, n)) return rc;
+    if (!aligned16(d_in) || !aligned16(d_w)) return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    GemvPlan pl;
+    HIP_TRY(gemv_plan(K_RESID, rows, n, &pl));
+    GemvParams p{};
+    p.x = d_in;
+    p.x_resid = d_x;
+    p.n = n;
+    p.rows = rows;
+    p.w0 = d_w;
+    HIP_TRY(gemv_launch(pl, p, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_swiglu(const float* d_x, const float* d_g, float eps, const float* d_w1, const float* d_w3, int32_t hidden,
+                 int32_t n, float* d_hb, void* hip_stream) {
+    if (!d_x || !d_w1 || !d_w3 || !d_hb) return LD_E_NULL;
+    if (int rc = op_shape_ok(hidden, n)) return rc;
+    if (!aligned16(d_x) || !aligned16(d_w1) || !aligned16(d_w3) || (d_g && !aligned16(d_g))) return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    GemvPlan pl;
+    HIP_TRY(gemv_plan(K_SWIGLU, hidden, n, &pl));
+    GemvParams p{};
+    p.x = d_x;
+    p.gain = d_g;
+    p.eps = eps;
+    p.n = n;
+    p.rows = hidden;
+    p.w0 = d_w1;
+    p.w1 = d_w3;
+    p.out = d_hb;
+    HIP_TRY(gemv_launch(pl, p, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d_wq, const float* d_wk,
+                   const float* d_wv, int32_t dim, int32_t n_heads, int32_t n_kv_heads, int32_t pos, float theta,
+                   float* d_q, float* d_k, float* d_v, void* hip_stream) {
+    if (!d_x || !d_wq || !d_wk || !d_wv || !d_q || !d_k || !d_v) return LD_E_NULL;
+    if (dim <= 0 || n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || dim % n_heads ||
+        ((long long)dim * n_kv_heads) % n_heads || ((dim / n_heads) % 2) || !(theta > 0.f))
+        return LD_E_CONFIG;
+    const int hs = dim / n_heads, kv = (int)((long long)dim * n_kv_heads / n_heads);
+    if ((dim % 4) || (kv % 4)) return LD_E_CONFIG;
+    if (pos < 0) return LD_E_RANGE;
+    if (int rc = op_shape_ok(dim, dim)) return rc;
+    if (!aligned16(d_x) || !aligned16(d_wq) || !aligned16(d_wk) || !aligned16(d_wv) || (d_g && !aligned16(d_g)))
+        return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    Temps tmp;
+    float2* rope = nullptr;
+    StepState* st = nullptr;
+    HIP_TRY(tmp.get(&rope, (size_t)(pos + 1) * (hs / 2)));
+    HIP_TRY(tmp.get(&st, 1));
+    std::vector<float2> rt = rope_table(pos + 1, hs, (double)theta);
+    HIP_TRY(hipMemcpy(rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice));
+    StepState hs_state{0, pos, -1, 0};
+    HIP_TRY(hipMemcpy(st, &hs_state, sizeof(hs_state), hipMemcpyHostToDevice));
+    GemvPlan pl;
+    HIP_TRY(gemv_plan(K_QKV, dim + 2 * kv, dim, &pl));
+    GemvParams p{};
+    p.x = d_x;
+    p.gain = d_g;
+    p.eps = eps;
+    p.n = dim;
+    p.rows = dim + 2 * kv;
+    p.w0 = d_wq;
+    p.w1 = d_wk;
+    p.w2 = d_wv;
+    p.seg1 = dim;
+    p.seg2 = dim + kv;
+    p.out = d_q;
+    p.kc = d_k;
+    p.vc = d_v;
+    p.kv_stride = 0;
+    p.head_size = hs;
+    p.rope = rope;
+    p.state = st;
+    HIP_TRY(gemv_launch(pl, p, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads, int32_t n_kv_heads,
+                    int32_t head_size, int32_t pos, float* d_out, void* hip_stream) {
+    if (!d_q || !d_kc || !d_vc || !d_out) return LD_E_NULL;
+    if (n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || head_size <= 0 || head_size % 2)
+        return LD_E_CONFIG;
+    if (!supported_head_size(head_size)) return LD_E_UNSUPPORTED;
+    if ((n_heads + n_kv_heads - 1) / n_kv_heads > kMaxGroup) return LD_E_UNSUPPORTED;
+    if (pos < 0) return LD_E_RANGE;
+    if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc)) return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int nsplit = attn_splits(head_size, pos + 1, n_kv_heads);
+    Temps tmp;
+    float2* ml = nullptr;
+    float* acc = nullptr;
+    StepState* st = nullptr;
+    HIP_TRY(tmp.get(&ml, (size_t)n_heads * nsplit));
+    HIP_TRY(tmp.get(&acc, (size_t)n_heads * nsplit * head_size));
+    HIP_TRY(tmp.get(&st, 1));
+    StepState hs_state{0, pos, -1, 0};
+    HIP_TRY(hipMemcpy(st, &hs_state, sizeof(hs_state), hipMemcpyHostToDevice));
+    AttnParams a{};
+    a.q = d_q;
+    a.kc = d_kc;
+    a.vc = d_vc;
+    a.out = d_out;
+    a.part_ml = ml;
+    a.part_acc = acc;
+    a.state = st;
+    a.n_heads = n_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.kv_dim = n_kv_heads * head_size;
+    a.nsplit = nsplit;
+    HIP_TRY(attn_launch(head_size, a, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_stream) {
+    if (!d_v || !h_index_out) return LD_E_NULL;
+    if (n <= 0) return LD_E_RANGE;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int nb = argmax_blocks(n);
+    Temps tmp;
+    float2* best = nullptr;
+    StepState* st = nullptr;
+    HIP_TRY(tmp.get(&best, (size_t)nb));
+    HIP_TRY(tmp.get(&st, 1));
+    HIP_TRY(hipMemset(st, 0, sizeof(StepState)));
+    HIP_TRY(argmax_launch(d_v, n, best, nb, st, s));
+    StepState out{};
+    HIP_TRY(hipMemcpyAsync(&out, st, sizeof(out), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    *h_index_out = out.next;
+    return LD_OK;
+}
+
+}  // extern "C"
