@@ -418,10 +418,15 @@ __device__ __forceinline__ void group_of(int g, int H, int KV, int& h_lo, int& G
     G = ((g + 1) * H + KV - 1) / KV - h_lo;    // query heads with floor(h KV / H) = g
 }
 
-// Tiles of a position: `per` consecutive tiles per split, `nact` splits in use.
+#ifndef LD_ATTN_MIN_TILES
+#define LD_ATTN_MIN_TILES 2  // fewest key tiles a split takes (below that one split serves all keys)
+#endif
+
+// Tiles of a position: `per` consecutive tiles per split (at least min_tiles),
+// `nact` splits in use.
 __device__ __forceinline__ void split_of(int n, int ch, int nsplit, int& tiles, int& per, int& nact) {
     tiles = (n + ch - 1) / ch;
-    per = (tiles + nsplit - 1) / nsplit;
+    per = max((tiles + nsplit - 1) / nsplit, LD_ATTN_MIN_TILES);
     nact = (tiles + per - 1) / per;
 }
 
@@ -567,10 +572,172 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
                 const float4 b = red_s[k * slots + tid];
                 a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
             }
-            part4[((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4] = a;
+            if (nact == 1) {  // one split holds every key: this is the output
+                const float il = 1.0f / l_s[tid / H4];
+                reinterpret_cast<float4*>(p.out)[(size_t)(h_lo + tid / H4) * H4 + tid % H4] =
+                    make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+            } else {
+                part4[((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4] = a;
+            }
         }
+        if (nact == 1) return;
+    }
+    if (nact == 1) {
+        // (slots >= threads): outputs written unnormalised above; normalise in place
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            const int o = tid + j * kAttnThreads;
+            if (o < slots) {
+                const float il = 1.0f / l_s[o / H4];
+                const float4 a = acc[j];
+                reinterpret_cast<float4*>(p.out)[(size_t)(h_lo + o / H4) * H4 + o % H4] =
+                    make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+            }
+        }
+        return;
     }
     if (tid < G) p.part_ml[(size_t)(h_lo + tid) * p.nsplit + s] = make_float2(m_s[tid], l_s[tid]);
+}
+
+// Head size 128: a register-only variant.  Each wave is an independent
+// flash-decoding worker over its own batches of 2U keys: one key row (512 B)
+// per half-wave and U rows per half in flight, the next batch loaded while
+// the current one is scored, q of every head of the group held in registers,
+// scores reduced across the 32 lanes of a half with DPP, and the online
+// softmax state (m, l per head) wave-uniform.  No LDS and no barrier inside the
+// key loop; the four waves merge once at the end of the block.
+__device__ __forceinline__ float half_sum(float v) {  // lanes 16-31: sum of 0-31; lanes 48-63: of 32-63
+    v += dpp<kQuadSwap1>(0.f, v);
+    v += dpp<kQuadSwap2>(0.f, v);
+    v += dpp<kRowHalfMirror>(0.f, v);
+    v += dpp<kRowMirror>(0.f, v);
+    v += dpp<kRowBcast15, 0xa>(0.f, v);
+    return v;
+}
+
+__device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
+    return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
+}
+
+template <int GMAX, int U>
+__global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
+    constexpr int HS = 128, CH = 32, NW = kAttnThreads / 64;
+    __shared__ float ms_s[NW][GMAX], ls_s[NW][GMAX];
+    __shared__ float4 acc_s[NW][GMAX][32];
+    const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, c = lane & 31;
+    const int n = p.state->pos + 1;
+    int tiles, per, nact;
+    split_of(n, CH, p.nsplit, tiles, per, nact);
+    if (s >= nact) return;
+    const int kb = s * per * CH, ke = min(n, (s + 1) * per * CH);  // this block's keys
+    int h_lo, G;
+    group_of(g, p.n_heads, p.n_kv_heads, h_lo, G);
+
+    const float* kbase = p.kc + (size_t)g * HS + 4 * c;
+    const float* vbase = p.vc + (size_t)g * HS + 4 * c;
+    float4 K[U], V[U];
+    auto load = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = min(kb + b * 2 * U + 2 * u + half, n - 1);  // past the end: re-read the last key
+            K[u] = *reinterpret_cast<const float4*>(kbase + (size_t)t * p.kv_dim);
+            V[u] = *reinterpret_cast<const float4*>(vbase + (size_t)t * p.kv_dim);
+        }
+    };
+    int b = wave;
+    if (kb + b * 2 * U < ke) load(b);
+
+    float4 q[GMAX], acc[GMAX];
+    float m[GMAX], l[GMAX];
+    const float4* q4 = reinterpret_cast<const float4*>(p.q);
+#pragma unroll
+    for (int hh = 0; hh < GMAX; ++hh) {
+        q[hh] = hh < G ? q4[(size_t)(h_lo + hh) * 32 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        acc[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
+        m[hh] = -INFINITY;
+        l[hh] = 0.f;
+    }
+    const float scale = 1.0f / sqrtf((float)HS);
+
+    for (; kb + b * 2 * U < ke; b += NW) {
+        float4 Kc[U], Vc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            Kc[u] = K[u];
+            Vc[u] = V[u];
+        }
+        if (kb + (b + NW) * 2 * U < ke) load(b + NW);  // in flight while this batch is scored
+        const int key0 = kb + b * 2 * U;
+#pragma unroll
+        for (int hh = 0; hh < GMAX; ++hh) {
+            if (hh < G) {
+                float se[U], so[U];
+                float mb = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float d = half_sum(dot4(Kc[u], q[hh], 0.f));
+                    se[u] = key0 + 2 * u < ke ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 31)) * scale
+                                             : -INFINITY;
+                    so[u] = key0 + 2 * u + 1 < ke
+                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 63)) * scale
+                                : -INFINITY;
+                    mb = fmaxf(mb, fmaxf(se[u], so[u]));
+                }
+                const float mn = fmaxf(m[hh], mb);
+                const float r = __expf(m[hh] - mn);
+                float4 a = make_float4(acc[hh].x * r, acc[hh].y * r, acc[hh].z * r, acc[hh].w * r);
+                float ls = 0.f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float ee = __expf(se[u] - mn), eo = __expf(so[u] - mn);
+                    ls += ee + eo;
+                    a = fma4(half ? eo : ee, Vc[u], a);
+                }
+                acc[hh] = a;
+                l[hh] = l[hh] * r + ls;
+                m[hh] = mn;
+            }
+        }
+    }
+
+    // the halves hold different keys of the same columns: add them, then merge the waves
+#pragma unroll
+    for (int hh = 0; hh < GMAX; ++hh) {
+        if (hh < G) {
+            const float4 o = make_float4(__shfl_xor(acc[hh].x, 32), __shfl_xor(acc[hh].y, 32), __shfl_xor(acc[hh].z, 32),
+                                         __shfl_xor(acc[hh].w, 32));
+            if (half == 0) acc_s[wave][hh][c] = make_float4(acc[hh].x + o.x, acc[hh].y + o.y, acc[hh].z + o.z, acc[hh].w + o.w);
+            if (lane == 0) {
+                ms_s[wave][hh] = m[hh];
+                ls_s[wave][hh] = l[hh];
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < G * 32) {
+        const int hh = tid / 32, cc = tid % 32;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ms_s[w][hh]);
+        float L = 0.f;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float e = __expf(ms_s[w][hh] - M);  // 0 for a wave without keys
+            L = fmaf(ls_s[w][hh], e, L);
+            A = fma4(e, acc_s[w][hh][cc], A);
+        }
+        const int h = h_lo + hh;
+        if (nact == 1) {
+            const float il = 1.0f / L;
+            reinterpret_cast<float4*>(p.out)[(size_t)h * 32 + cc] = make_float4(A.x * il, A.y * il, A.z * il, A.w * il);
+        } else {
+            reinterpret_cast<float4*>(p.part_acc)[((size_t)h * p.nsplit + s) * 32 + cc] = A;
+            if (cc == 0) p.part_ml[(size_t)h * p.nsplit + s] = make_float2(M, L);
+        }
+    }
 }
 
 // Exact merge of the split partials of the query heads of kv head blockIdx.x.
@@ -582,6 +749,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams p) 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int tiles, per, nact, h_lo, G;
     split_of(p.state->pos + 1, p.chunk, p.nsplit, tiles, per, nact);
+    if (nact == 1) return;  // the attention kernel wrote the output itself
     group_of(blockIdx.x, p.n_heads, p.n_kv_heads, h_lo, G);
 
     for (int hh = wave; hh < G; hh += kAttnThreads / 64) {
@@ -777,17 +945,38 @@ int attn_splits(int hs, int seq_len, int n_kv_heads) {
     const int ch = attn_chunk(hs);
     if (!ch) return 0;
     const int tiles = (seq_len + ch - 1) / ch;
-    // about 512 blocks at the longest context: two per compute unit, each
-    // walking several tiles so that its loads stay in flight
+    // about 512 blocks at the longest context (two per compute unit), and no
+    // split shorter than LD_ATTN_MIN_TILES tiles
     int want = (512 + n_kv_heads - 1) / n_kv_heads;
-    if (want < 1) want = 1;
-    return want < tiles ? want : tiles;
+    const int most = (tiles + LD_ATTN_MIN_TILES - 1) / LD_ATTN_MIN_TILES;
+    if (want > most) want = most;
+    return want < 1 ? 1 : want;
 }
+
+#ifndef LD_ATTN_REG128
+#define LD_ATTN_REG128 1  // head size 128 takes the register-only kernel
+#endif
+#ifndef LD_ATTN_U
+#define LD_ATTN_U 4  // key pairs per wave batch in the register-only kernel
+#endif
 
 hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     AttnParams p = p0;
     p.chunk = attn_chunk(hs);
     const dim3 grid(p.n_kv_heads, p.nsplit), block(kAttnThreads);
+    const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
+    if (hs == 128 && LD_ATTN_REG128) {
+        if (group <= 1)
+            hipLaunchKernelGGL((attn128_kernel<1, LD_ATTN_U>), grid, block, 0, s, p);
+        else if (group <= 2)
+            hipLaunchKernelGGL((attn128_kernel<2, LD_ATTN_U>), grid, block, 0, s, p);
+        else if (group <= 4)
+            hipLaunchKernelGGL((attn128_kernel<4, LD_ATTN_U>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn128_kernel<8, LD_ATTN_U>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.n_kv_heads), block, 0, s, p);
+        return hipGetLastError();
+    }
     switch (hs) {
 #define LD_ATTN_CASE(HS, CH)                                                               \
     case HS:                                                                               \
