@@ -83,17 +83,23 @@ def load_traffic(kernel: str, workload: str):
     return t.get("bytes_per_launch")
 
 
-def windows_for(seq_len: int, steps: int, width: int = 16):
-    """Chunk boundaries of the timed generation: 16-step windows at the start,
-    around position 511 and at the end, so per-position rates come from the same
-    timed pass."""
-    marks = {0, min(width, steps)}
-    if steps > 520:
+# Where each workload's timed decode starts: the 70B-layer workload first fills
+# the cache with 3584 seeded tokens through forward calls (untimed), then times
+# greedy decode from position 3584 to the end of its 4096-position context.
+START = {"llama70b_8l": 3584}
+
+
+def windows_for(seq_len: int, steps: int, width: int = 16, start: int = 0):
+    """Chunk boundaries (absolute positions) of the timed generation: 16-step
+    windows at the start, around position 511 (when inside the range) and at
+    the end, so per-position rates come from the same timed pass."""
+    end = start + steps
+    marks = {start, min(start + width, end), end}
+    if start < 504 and end > 520:
         marks |= {504, 520}
     if steps > 2 * width:
-        marks |= {steps - width, steps}
-    marks.add(steps)
-    b = sorted(m for m in marks if 0 <= m <= steps)
+        marks.add(end - width)
+    b = sorted(m for m in marks if start <= m <= end)
     return list(zip(b[:-1], b[1:]))
 
 
@@ -139,7 +145,8 @@ def main() -> int:
         return 0
     cfg = synth.CONFIGS[args.config]
     S = cfg.seq_len
-    steps = args.steps or S
+    start = START.get(cfg.name, 0)
+    steps = args.steps or (S - start)
     warm = max(0, args.warmup)
 
     t = time.time()
@@ -157,16 +164,30 @@ def main() -> int:
     if warm:
         model.generate(1, 0, min(warm, S))
     model.reset()
+    tok = 1
+    if start:
+        prefill = synth.prefill_tokens(cfg, start)
+        t = time.time()
+        for p in range(start):
+            model.forward_async(int(prefill[p]), p)
+        tok = model.argmax_last()
+        print(f"# cache filled by {start} forward calls in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    first_tok = tok
 
-    # ---- timed region: greedy decode of `steps` tokens from token 1 at pos 0 ----
+    # ---- timed region: greedy decode of `steps` tokens from (tok, start) ----
     chunks = []
-    done, tok, t_total = 0, 1, 0.0
+    done, t_total = 0, 0.0
     while done < steps:
-        n_pass = min(S, steps - done)
-        if done:
+        n_pass = min(S - start, steps - done)
+        if done:  # a second pass over the context (only when more steps than positions are asked for)
             model.reset()
-        for a, b in windows_for(S, n_pass):
+            tok = 1
+            if start:
+                for p in range(start):
+                    model.forward_async(int(prefill[p]), p)
+                tok = model.argmax_last()
+        for a, b in windows_for(S, n_pass, start=start):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             toks = model.generate(tok, a, b - a)
@@ -175,7 +196,6 @@ def main() -> int:
             chunks.append((a, b, t1 - t0))
             t_total += t1 - t0
         done += n_pass
-        tok = 1
     torch.cuda.synchronize()
 
     total_bytes = sum(bytes_per_token(cfg, p) for a, b, _ in chunks for p in range(a, b))
@@ -195,10 +215,10 @@ def main() -> int:
     roofline = None
     kernels = None
     if not args.no_kernel_timing:
-        model.reset()
-        n_prof = min(steps, S)
-        stats = model.profile(1, 0, n_prof)
-        pos_list = list(range(n_prof))
+        # same positions as the timed pass; a prefilled prefix stays in the cache
+        n_prof = min(steps, S - start)
+        stats = model.profile(first_tok, start, n_prof)
+        pos_list = list(range(start, start + n_prof))
         kernels = {}
         for s in stats:
             if s["launches"]:
@@ -227,17 +247,18 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         cache = oracle.KVCache(cfg)
-        n_cpu = max(1, min(args.cpu_steps, S))
+        n_cpu = max(1, min(args.cpu_steps, S - start))
+        # a step's cost does not depend on the cache contents: late positions run on a zero cache
         t0 = time.perf_counter()
         tok = 1
-        for p in range(n_cpu):
+        for p in range(start, start + n_cpu):
             logits = oracle.forward(cfg, blob, cache, tok, p)
             tok = oracle.argmax(logits)
         dt = time.perf_counter() - t0
         cpu = {"value": round(n_cpu / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_cpu} greedy decode steps (positions 0-{n_cpu - 1}) of the {cfg.name} workload, "
-                         f"single-threaded C oracle with double accumulation, {dt:.1f} s",
-               "GBps": round(sum(bytes_per_token(cfg, p) for p in range(n_cpu)) / dt / 1e9, 2),
+               "sample": f"{n_cpu} greedy decode steps (positions {start}-{start + n_cpu - 1}) of the {cfg.name} "
+                         f"workload, single-threaded C oracle with double accumulation, {dt:.1f} s",
+               "GBps": round(sum(bytes_per_token(cfg, p) for p in range(start, start + n_cpu)) / dt / 1e9, 2),
                "host_cores_available": os.cpu_count()}
 
     line = {
@@ -253,7 +274,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: greedy decode of {steps} tokens from token 1 at position 0, batch 1, "
+        "config": {"workload": f"{cfg.name}: greedy decode of {steps} tokens from position {start}"
+                               f"{' after a ' + str(start) + '-token seeded prefill' if start else ' (token 1)'}, batch 1, "
                                f"dim {cfg.dim}, hidden {cfg.hidden_dim}, {cfg.n_layers} layers, "
                                f"{cfg.n_heads}/{cfg.n_kv_heads} heads, vocab {cfg.vocab_size}, "
                                f"seq_len {cfg.seq_len}, fp32 N(0,0.02) weights (seed {cfg.seed})",

@@ -813,17 +813,19 @@ struct Tpl {
     int nt, nx, rpi;
 };
 
+
 // Ordered by capacity nt*nx float4 (= input floats / 4).  Two groups of
 // weights are live at once (the pipelined loads), so rpi*nx stays near 16.
 // The q/k/v and w1/w3 kernels pair rows and use at least 2 rows per group.
+// (The 1024-thread shape for 8192 < n <= 12288 was the fastest of the shapes
+// timed for the 11008-wide down projection.)
 constexpr Tpl kTpl[] = {
     {64, 1, 4},    // n <= 256
     {64, 2, 4},    // n <= 512
     {64, 4, 4},    // n <= 1024
     {256, 4, 4},   // n <= 4096
     {256, 8, 2},   // n <= 8192
-    {256, 11, 1},  // n <= 11264
-    {256, 12, 1},  // n <= 12288
+    {1024, 3, 4},  // n <= 12288
     {512, 14, 1},  // n <= 28672
     {512, 16, 1},  // n <= 32768
 };
@@ -851,7 +853,6 @@ GemvFn gemv_fn(int t) {
         case 5: return gemv_fn_t<KIND, 5>();
         case 6: return gemv_fn_t<KIND, 6>();
         case 7: return gemv_fn_t<KIND, 7>();
-        case 8: return gemv_fn_t<KIND, 8>();
     }
     return nullptr;
 }
