@@ -670,9 +670,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
         }
         if (kb + (b + NW) * 2 * U < ke) load(b + NW);  // in flight while this batch is scored
         const int key0 = kb + b * 2 * U;
+        // every head slot of the template is computed (a slot past the group has
+        // q = 0 and is never written), so the loop has no per-head branch
 #pragma unroll
         for (int hh = 0; hh < GMAX; ++hh) {
-            if (hh < G) {
+            {
                 float se[U], so[U];
                 float mb = -INFINITY;
 #pragma unroll
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
     // the halves hold different keys of the same columns: add them, then merge the waves
 #pragma unroll
     for (int hh = 0; hh < GMAX; ++hh) {
-        if (hh < G) {
+        {
             const float4 o = make_float4(__shfl_xor(acc[hh].x, 32), __shfl_xor(acc[hh].y, 32), __shfl_xor(acc[hh].z, 32),
                                          __shfl_xor(acc[hh].w, 32));
             if (half == 0) acc_s[wave][hh][c] = make_float4(acc[hh].x + o.x, acc[hh].y + o.y, acc[hh].z + o.z, acc[hh].w + o.w);
@@ -740,20 +742,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
     }
 }
 
-// Exact merge of the split partials of the query heads of kv head blockIdx.x.
+// Exact merge of the split partials of query head blockIdx.x (one block per
+// query head, so a group of 8 heads spreads over 8 blocks).  Wave 0 finds
+// M = max_s m_s and L = sum_s e^{m_s - M} l_s over the splits (lane-strided
+// loads); then every column's float4 is summed over split groups, 8 loads in
+// flight per thread, and the groups are added through LDS.
 template <int HS>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams p) {
     constexpr int H4 = HS / 4;
-    __shared__ float m_s[kMaxGroup], l_s[kMaxGroup];
+    constexpr int KG = kAttnThreads / H4;  // split groups (H4 <= 64, so at least 4)
+    __shared__ float M_s, L_s;
     __shared__ float4 red_s[kAttnThreads];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int tiles, per, nact, h_lo, G;
+    const int tid = threadIdx.x, lane = tid & 63, h = blockIdx.x;
+    int tiles, per, nact;
     split_of(p.state->pos + 1, p.chunk, p.nsplit, tiles, per, nact);
     if (nact == 1) return;  // the attention kernel wrote the output itself
-    group_of(blockIdx.x, p.n_heads, p.n_kv_heads, h_lo, G);
-
-    for (int hh = wave; hh < G; hh += kAttnThreads / 64) {
-        const float2* ml = p.part_ml + (size_t)(h_lo + hh) * p.nsplit;
+    const float2* ml = p.part_ml + (size_t)h * p.nsplit;
+    if (tid < 64) {
         float m = -INFINITY;
         for (int sp = lane; sp < nact; sp += 64) m = fmaxf(m, ml[sp].x);
         m = wave_max(m);
@@ -764,45 +769,31 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams p) 
         }
         l = wave_sum(l);
         if (lane == 0) {
-            m_s[hh] = m;
-            l_s[hh] = l;
+            M_s = m;
+            L_s = l;
         }
     }
     __syncthreads();
-    const int slots = G * H4;
-    const float4* acc4 = reinterpret_cast<const float4*>(p.part_acc);
-    float4* out4 = reinterpret_cast<float4*>(p.out);
-    const int KG = slots < kAttnThreads ? kAttnThreads / slots : 1;
-    for (int o0 = 0; o0 < slots; o0 += kAttnThreads) {
-        const int o = slots < kAttnThreads ? tid % slots : o0 + tid;
-        const int kg = slots < kAttnThreads ? tid / slots : 0;
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (kg < KG && o < slots) {
-            const int hh = o / H4, c = o % H4, h = h_lo + hh;
-            const float2* ml = p.part_ml + (size_t)h * p.nsplit;
-            const float M = m_s[hh];
-#pragma unroll 4
-            for (int sp = kg; sp < nact; sp += KG) {
-                const float wgt = __expf(ml[sp].x - M);
-                const float4 v = acc4[((size_t)h * p.nsplit + sp) * H4 + c];
-                a = make_float4(fmaf(wgt, v.x, a.x), fmaf(wgt, v.y, a.y), fmaf(wgt, v.z, a.z), fmaf(wgt, v.w, a.w));
-            }
+    const int c = tid % H4, kg = tid / H4;
+    const float M = M_s;
+    const float4* acc4 = reinterpret_cast<const float4*>(p.part_acc) + (size_t)h * p.nsplit * H4 + c;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (kg < KG) {
+#pragma unroll 8
+        for (int sp = kg; sp < nact; sp += KG) {
+            const float wgt = __expf(ml[sp].x - M);
+            a = fma4(wgt, acc4[(size_t)sp * H4], a);
         }
-        if (slots < kAttnThreads) {
-            red_s[tid] = a;
-            __syncthreads();
-            if (tid < slots) {
-                for (int k = 1; k < KG; ++k) {
-                    const float4 b = red_s[k * slots + tid];
-                    a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-                }
-            }
+    }
+    red_s[tid] = a;
+    __syncthreads();
+    if (tid < H4) {
+        for (int k = 1; k < KG; ++k) {
+            const float4 b = red_s[k * H4 + tid];
+            a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
         }
-        if ((slots < kAttnThreads ? tid < slots : o < slots)) {
-            const int hh = o / H4, c = o % H4;
-            const float il = 1.0f / l_s[hh];
-            out4[(size_t)(h_lo + hh) * H4 + c] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
-        }
+        const float il = 1.0f / L_s;
+        reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + tid] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
     }
 }
 
@@ -942,13 +933,17 @@ int attn_chunk(int hs) {
     return 0;
 }
 
+#ifndef LD_ATTN_BLOCKS
+#define LD_ATTN_BLOCKS 512
+#endif
+
 int attn_splits(int hs, int seq_len, int n_kv_heads) {
     const int ch = attn_chunk(hs);
     if (!ch) return 0;
     const int tiles = (seq_len + ch - 1) / ch;
-    // about 512 blocks at the longest context (two per compute unit), and no
-    // split shorter than LD_ATTN_MIN_TILES tiles
-    int want = (512 + n_kv_heads - 1) / n_kv_heads;
+    // about LD_ATTN_BLOCKS blocks at the longest context (two per compute
+    // unit), and no split shorter than LD_ATTN_MIN_TILES tiles
+    int want = (LD_ATTN_BLOCKS + n_kv_heads - 1) / n_kv_heads;
     const int most = (tiles + LD_ATTN_MIN_TILES - 1) / LD_ATTN_MIN_TILES;
     if (want > most) want = most;
     return want < 1 ? 1 : want;
@@ -957,9 +952,6 @@ int attn_splits(int hs, int seq_len, int n_kv_heads) {
 #ifndef LD_ATTN_REG128
 #define LD_ATTN_REG128 1  // head size 128 takes the register-only kernel
 #endif
-#ifndef LD_ATTN_U
-#define LD_ATTN_U 4  // key pairs per wave batch in the register-only kernel
-#endif
 
 hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     AttnParams p = p0;
@@ -967,22 +959,24 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     const dim3 grid(p.n_kv_heads, p.nsplit), block(kAttnThreads);
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
     if (hs == 128 && LD_ATTN_REG128) {
+        // 4 key pairs per wave batch for one or two heads per kv head, 2 for
+        // larger groups (whose per-batch register and ALU load is larger)
         if (group <= 1)
-            hipLaunchKernelGGL((attn128_kernel<1, LD_ATTN_U>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn128_kernel<1, 4>), grid, block, 0, s, p);
         else if (group <= 2)
-            hipLaunchKernelGGL((attn128_kernel<2, LD_ATTN_U>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn128_kernel<2, 4>), grid, block, 0, s, p);
         else if (group <= 4)
-            hipLaunchKernelGGL((attn128_kernel<4, LD_ATTN_U>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((attn128_kernel<4, 2>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((attn128_kernel<8, LD_ATTN_U>), grid, block, 0, s, p);
-        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.n_kv_heads), block, 0, s, p);
+            hipLaunchKernelGGL((attn128_kernel<8, 2>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.n_heads), block, 0, s, p);
         return hipGetLastError();
     }
     switch (hs) {
 #define LD_ATTN_CASE(HS, CH)                                                               \
     case HS:                                                                               \
         hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);                   \
-        hipLaunchKernelGGL((attn_merge_kernel<HS>), dim3(p.n_kv_heads), block, 0, s, p);   \
+        hipLaunchKernelGGL((attn_merge_kernel<HS>), dim3(p.n_heads), block, 0, s, p);      \
         break;
         LD_ATTN_CASE(16, 64)
         LD_ATTN_CASE(32, 64)
