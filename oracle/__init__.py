@@ -71,6 +71,9 @@ def _load(page: bool = False):
             "oracle_forward": ([_P, _P, _P, _P, _P, _I, _I, _P], _I),
             "oracle_generate": ([_P, _P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
             "oracle_bruteforce": ([_P, _P, _P, _P, _I, _P], _I),
+            "oracle_sample": ([_P, _I, ctypes.c_double, ctypes.c_double, ctypes.c_double], _I),
+            "oracle_generate_sampled": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_double, ctypes.c_double, _I,
+                                         _P, _P, _P, _P], _I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -196,3 +199,26 @@ def bruteforce(cfg, blob, tokens, p: int, page: bool = False, shared=None) -> np
     if rc:
         raise ValueError("oracle_bruteforce rejected its arguments")
     return logits
+
+
+def sample(logits, temperature, topp, coin, page: bool = False) -> int:
+    v = _f32(logits)
+    return int(_load(page).oracle_sample(_ptr(v), v.size, temperature, topp, coin))
+
+
+def generate_sampled(cfg, blob, cache: KVCache, prompt, pos: int, n_steps: int, temperature: float, topp: float,
+                     stop_token: int, coins, keep_logits: bool = False, page: bool = False):
+    """Returns (tokens[:n_out], logits or None)."""
+    prompt = np.ascontiguousarray(prompt, dtype=np.int32)
+    coins = np.ascontiguousarray(coins, dtype=np.float32)
+    assert coins.size >= n_steps
+    toks = np.zeros(max(n_steps, 1), np.int32)
+    n_out = ctypes.c_int(0)
+    logits = np.empty((n_steps, cfg.vocab_size), np.float32) if keep_logits else None
+    rc = _load(page).oracle_generate_sampled(ctypes.byref(_cfg(cfg)), ctypes.byref(_opt(cfg)), _ptr(blob),
+                                             _ptr(cache.k), _ptr(cache.v), _ptr(prompt), prompt.size, pos, n_steps,
+                                             temperature, topp, stop_token, _ptr(coins), _ptr(toks),
+                                             ctypes.byref(n_out), _ptr(logits) if logits is not None else None)
+    if rc:
+        raise ValueError("oracle_generate_sampled rejected its arguments")
+    return toks[:n_out.value], (logits[:n_out.value] if logits is not None else None)

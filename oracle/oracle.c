@@ -197,6 +197,68 @@ int oracle_argmax(const float* v, int n) {
     return best;
 }
 
+typedef struct {
+    acc_t p;
+    int i;
+} prob_index;
+
+/* descending probability, ties to the lower index */
+static int by_prob_desc(const void* a, const void* b) {
+    const prob_index* x = (const prob_index*)a;
+    const prob_index* y = (const prob_index*)b;
+    if (x->p > y->p) return -1;
+    if (x->p < y->p) return 1;
+    return x->i - y->i;
+}
+
+/* Sampling: "run.c 逐行解讀" §6 (temperature 0 -> argmax; otherwise divide by the
+ * temperature, softmax, then top-p or plain multinomial), with the
+ * cumulative-distribution walk of sample() on the "run.c" page. */
+int oracle_sample(const float* logits, int n, double temperature, double topp, double coin) {
+    if (!(temperature > 0)) return oracle_argmax(logits, n);
+    prob_index* pi = (prob_index*)malloc(sizeof(prob_index) * (size_t)n);
+    acc_t m = (acc_t)logits[0] / (acc_t)temperature;
+    for (int i = 0; i < n; ++i) {
+        pi[i].p = (acc_t)logits[i] / (acc_t)temperature;
+        pi[i].i = i;
+        if (pi[i].p > m) m = pi[i].p;
+    }
+    acc_t sum = 0;
+    for (int i = 0; i < n; ++i) {
+        pi[i].p = ACC_EXP(pi[i].p - m);
+        sum += pi[i].p;
+    }
+    for (int i = 0; i < n; ++i) pi[i].p /= sum;
+    int chosen = n - 1;
+    if (topp <= 0 || topp >= 1) {
+        acc_t cdf = 0;
+        for (int i = 0; i < n; ++i) {
+            cdf += pi[i].p;
+            if ((acc_t)coin < cdf) {
+                chosen = i;
+                break;
+            }
+        }
+    } else {
+        qsort(pi, (size_t)n, sizeof(prob_index), by_prob_desc);
+        acc_t mass = 0;
+        int k = 0;
+        while (k < n && mass < (acc_t)topp) mass += pi[k++].p;
+        const acc_t r = (acc_t)coin * mass;
+        acc_t cdf = 0;
+        chosen = pi[k - 1].i;
+        for (int j = 0; j < k; ++j) {
+            cdf += pi[j].p;
+            if (r < cdf) {
+                chosen = pi[j].i;
+                break;
+            }
+        }
+    }
+    free(pi);
+    return chosen;
+}
+
 static void add_into(float* x, const float* y, int n) {
     for (int i = 0; i < n; ++i) x[i] = (float)((acc_t)x[i] + (acc_t)y[i]);
 }
@@ -276,6 +338,33 @@ int oracle_generate(const oracle_config* c, const oracle_options* o, const float
         token = oracle_argmax(logits, c->vocab_size);
         tokens_out[i] = token;
         if (logits_out) memcpy(logits_out + (int64_t)i * c->vocab_size, logits, sizeof(float) * (size_t)c->vocab_size);
+    }
+    free(logits);
+    return rc;
+}
+
+/* The generation loop of "run.c 逐行解讀" §7: prompt tokens are forced while the
+ * prompt lasts, then tokens are sampled; the loop ends at the stop token. */
+int oracle_generate_sampled(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
+                            float* vcache, const int32_t* prompt, int n_prompt, int pos, int n_steps,
+                            double temperature, double topp, int stop_token, const float* coins,
+                            int32_t* tokens_out, int* n_out, float* logits_out) {
+    if (!config_ok(c) || !prompt || n_prompt < 1 || n_steps < 0 || pos < 0 || (int64_t)pos + n_steps > c->seq_len ||
+        !tokens_out || !n_out || !coins)
+        return -1;
+    float* logits = (float*)malloc(sizeof(float) * (size_t)c->vocab_size);
+    int rc = 0, token = prompt[0];
+    *n_out = 0;
+    for (int i = 0; i < n_steps; ++i) {
+        rc = oracle_forward(c, o, blob, kcache, vcache, token, pos + i, logits);
+        if (rc) break;
+        if (logits_out) memcpy(logits_out + (int64_t)i * c->vocab_size, logits, sizeof(float) * (size_t)c->vocab_size);
+        const int next = i + 1 < n_prompt ? prompt[i + 1]
+                                          : oracle_sample(logits, c->vocab_size, temperature, topp, (double)coins[i]);
+        tokens_out[i] = next;
+        *n_out = i + 1;
+        if (stop_token >= 0 && next == stop_token) break;
+        token = next;
     }
     free(logits);
     return rc;

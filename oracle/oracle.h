@@ -69,6 +69,15 @@ void oracle_swiglu(float* hb, const float* h1, const float* h3, int n);
 /* Lowest index holding the maximum of v[0..n). */
 int oracle_argmax(const float* v, int n);
 
+/* Next token from logits ("run.c 逐行解讀" §6, three modes): temperature 0 is the
+ * argmax; otherwise logits are divided by the temperature and softmaxed, and
+ * with 0 < topp < 1 the draw is restricted to the smallest set of most likely
+ * tokens (descending probability, ties to the lower index) whose cumulative
+ * probability reaches topp, else it is over all tokens.  The draw walks the
+ * cumulative distribution ("run.c", sample): the first token whose cumulative
+ * probability exceeds coin * (mass of the set); coin is in [0, 1). */
+int oracle_sample(const float* logits, int n, double temperature, double topp, double coin);
+
 /* One decode step: writes cache row pos of every layer, returns logits (V).
  * Returns 0, or -1 when an argument is out of range. */
 int oracle_forward(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
@@ -78,6 +87,17 @@ int oracle_forward(const oracle_config* c, const oracle_options* o, const float*
  * logits_out, if not NULL, receives n*V floats. */
 int oracle_generate(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
                     float* vcache, int token, int pos, int n, int32_t* tokens_out, float* logits_out);
+
+/* The generation loop of "run.c 逐行解讀" §7: step i runs at position pos+i on
+ * token t_i (t_0 = prompt[0]); its next token is prompt[i+1] while the prompt
+ * lasts, else oracle_sample(logits, temperature, topp, coins[i]).
+ * tokens_out[i] = next token of step i; the loop ends after n_steps steps or
+ * after the step whose next token equals stop_token (>= 0; included in the
+ * output).  *n_out = steps run.  logits_out, if not NULL, gets n_steps*V floats. */
+int oracle_generate_sampled(const oracle_config* c, const oracle_options* o, const float* blob, float* kcache,
+                            float* vcache, const int32_t* prompt, int n_prompt, int pos, int n_steps,
+                            double temperature, double topp, int stop_token, const float* coins,
+                            int32_t* tokens_out, int* n_out, float* logits_out);
 
 /* Logits at position p recomputed from tokens[0..p] with no cache: every layer
  * over the whole prefix, causal mask of -inf above the diagonal. */

@@ -44,6 +44,7 @@ _lib = None
 GAIN_MEAN, GAIN_STD = 1.0, 0.01
 WEIGHT_MEAN, WEIGHT_STD = 0.0, 0.02
 TOKEN_STREAM = 255
+COIN_STREAM = 254
 
 
 def build(force: bool = True) -> str:
@@ -105,6 +106,12 @@ def uniform_int(n: int, bound: int, seed: int, stream: int = TOKEN_STREAM, first
     out = np.empty(n, np.int32)
     _load().synth_fill_uniform_int(out.ctypes.data, first, n, seed, stream, bound, default_threads())
     return out
+
+
+def coins(n: int, seed: int, stream: int = COIN_STREAM, first: int = 0) -> np.ndarray:
+    """Seeded fp32 draws in [0, 1) on the 2^-24 grid (24 random bits over 2^24,
+    the resolution of a float draw), one per sampled token."""
+    return (uniform_int(n, 1 << 24, seed, stream, first).astype(np.float64) / float(1 << 24)).astype(np.float32)
 
 
 @dataclass(frozen=True)

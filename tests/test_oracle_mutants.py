@@ -1,7 +1,7 @@
 """The oracle's pins catch plausible mistakes.
 
 Each case plants one mistake in a copy of ``oracle/oracle.c`` (on the CPU, in a
-temporary directory), builds it, and runs the pin suite against the mutant:
+temporary directory), builds it, and runs the pin suites against the mutant:
 the suite must fail.  A mutation that the pins let through would mean the
 oracle is not pinned against that mistake.
 """
@@ -36,7 +36,19 @@ MUTANTS = {
     "ffn_norm_uses_attention_gain": ("oracle_rmsnorm(xb, x, w.rms_ffn + lw * dim, dim, o->norm_eps);",
                                      "oracle_rmsnorm(xb, x, w.rms_att + lw * dim, dim, o->norm_eps);"),
     "softmax_max_not_subtracted_wrongly": ("att[t] = ACC_EXP(att[t] - m);", "att[t] = ACC_EXP(att[t] + m);"),
+    "sample_temperature_ignored": ("pi[i].p = (acc_t)logits[i] / (acc_t)temperature;", "pi[i].p = (acc_t)logits[i];"),
+    "top_p_not_renormalised": ("const acc_t r = (acc_t)coin * mass;", "const acc_t r = (acc_t)coin;"),
+    "top_p_ascending_order": ("if (x->p > y->p) return -1;\n    if (x->p < y->p) return 1;",
+                              "if (x->p > y->p) return 1;\n    if (x->p < y->p) return -1;"),
+    "top_p_ties_to_higher_index": ("return x->i - y->i;", "return y->i - x->i;"),
+    "top_p_set_stops_below_p": ("while (k < n && mass < (acc_t)topp) mass += pi[k++].p;",
+                                "while (k < n && mass + pi[k].p < (acc_t)topp) mass += pi[k++].p;\n        if (k == 0) mass += pi[k++].p;"),
+    "multinomial_walks_sorted_order": ("if (topp <= 0 || topp >= 1) {", "if (0) {"),
+    "stop_not_checked_on_forced_tokens": ("if (stop_token >= 0 && next == stop_token) break;",
+                                          "if (stop_token >= 0 && i + 1 >= n_prompt && next == stop_token) break;"),
+    "prompt_forcing_off_by_one": ("const int next = i + 1 < n_prompt ? prompt[i + 1]", "const int next = i + 2 < n_prompt ? prompt[i + 1]"),
 }
+PIN_FILES = ("test_oracle_sampling.py", "test_oracle_pins.py")
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -50,7 +62,7 @@ def test_pins_reject_mutant(name, tmp_path):
     subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared",
                     "-I", os.path.join(ROOT, "oracle"), str(mut), "-o", str(so), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(so))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
