@@ -113,6 +113,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle decode steps timed for the CPU baseline")
+    ap.add_argument("--sampled-steps", type=int, default=256,
+                    help="steps of the temperature / top-p generation loop timed beside greedy decode (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes three times (reference for "
                          "scaling the HBM byte counters of a profiler) and exit")
@@ -238,6 +240,25 @@ def main() -> int:
                     "traffic": traffic, "bytes_per_launch": kd["bytes_per_launch"], "avg_us": kd["avg_us"]}
         print(f"# kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
+    # ---- the sampling generation loop beside greedy decode, same positions ----
+    sampled = None
+    if args.sampled_steps > 0:
+        n_s = min(args.sampled_steps, S - start)
+        coins = synth.coins(n_s, cfg.seed, 7)
+        sampled = {"steps": n_s, "positions": [start, start + n_s - 1], "modes": {}}
+        for name, T, topp in (("greedy", 0.0, 0.0), ("temperature_0.9", 0.9, 0.0), ("top_p_0.9", 0.9, 0.9)):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            got = model.generate_sampled([first_tok], start, n_s, T, topp, -1, coins)
+            dt = time.perf_counter() - t0
+            assert got.size == n_s
+            sampled["modes"][name] = {"temperature": T, "topp": topp, "tok_s": round(n_s / dt, 2),
+                                      "ms_per_step": round(1e3 * dt / n_s, 4)}
+        g = sampled["modes"]["greedy"]["ms_per_step"]
+        for v in sampled["modes"].values():
+            v["us_over_greedy"] = round(1e3 * (v["ms_per_step"] - g), 2)
+        print(f"# generation loop: {json.dumps(sampled)}", file=sys.stderr, flush=True)
+
     model.close()
     del weights
     torch.cuda.empty_cache()
@@ -287,6 +308,7 @@ def main() -> int:
         "per_position": per_pos,
         "roofline": roofline,
         "kernels": kernels,
+        "generation_loop": sampled,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -122,6 +122,44 @@ int ld_argmax_last(ld_model* m, int32_t* h_token_out);
  * h_tokens_out: caller-owned host array of n_steps int32.  Synchronous. */
 int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, int32_t* h_tokens_out);
 
+/* How the generation loop chooses tokens after the prompt ("run.c 逐行解讀"
+ * §6, sample(), three modes):
+ *   temperature <= 0: the argmax (greedy, as above);
+ *   temperature > 0:  a draw from softmax(logits / temperature), with coin c
+ *     in [0, 1): the first token, in walk order, whose cumulative probability
+ *     exceeds c times the candidates' mass.  With topp <= 0 or topp >= 1 every
+ *     token is a candidate and the walk is in index order (sample() of the
+ *     "run.c" page).  With 0 < topp < 1 the candidates are the smallest set of
+ *     most likely tokens whose probabilities sum to at least topp, walked in
+ *     descending probability, equal probabilities in index order.
+ * stop_token: -1 for none, else a token id that ends the loop (§7, which ends
+ * at BOS = 1; the id is the caller's choice here). */
+typedef struct {
+    float temperature;
+    float topp;
+    int32_t stop_token;
+    int32_t reserved; /* 0 */
+} ld_sampling;
+
+/* The generation loop of "run.c 逐行解讀" §7.  Step i (i = 0, 1, ...) runs the
+ * decode step on token t_i at position pos + i, t_0 = h_prompt[0]; its next
+ * token t_{i+1} is h_prompt[i + 1] while the prompt lasts (i + 1 < n_prompt),
+ * else the choice `sampling` describes, drawing with coin h_coins[i].
+ * h_tokens_out[i] = t_{i+1}.  The loop ends after n_steps steps, or after the
+ * step whose next token (forced or chosen) equals the stop token; that token
+ * is the last one written.  *n_out receives the number of steps run.
+ *
+ * h_prompt: n_prompt >= 1 token ids in [0, vocab_size).  h_coins: host array
+ * of n_steps floats in [0, 1); entries i < n_prompt - 1 are not read; may be
+ * NULL when temperature <= 0.  Random numbers are the caller's, so a run is a
+ * function of its arguments.  Needs pos + n_steps <= seq_len.  Cache rows
+ * pos .. pos + *n_out - 1 are written; nothing above them.
+ * Errors: LD_E_NULL, LD_E_RANGE (a token, position, count, coin, temperature
+ * or stop id out of range), LD_E_UNSUPPORTED (temperature > 0 with
+ * vocab_size > 32768).  Synchronous. */
+int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t pos, int32_t n_steps,
+                const ld_sampling* sampling, const float* h_coins, int32_t* h_tokens_out, int32_t* n_out);
+
 /* Device pointers of the key and value caches, each (n_layers, seq_len,
  * kv_dim) fp32 row-major, and their size in floats.  The caller may read or
  * overwrite them between calls (e.g. to install a cache prefix). */
@@ -190,6 +228,12 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
 
 /* Lowest index of the maximum of d_v[0..n) ("run.c", argmax). */
 int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_stream);
+
+/* One token drawn from the logits d_logits[0..n) as ld_sampling describes
+ * (temperature, topp; stop_token unused), with coin in [0, 1).  n <= 32768
+ * when temperature > 0 (else LD_E_UNSUPPORTED).  Synchronous. */
+int ld_op_sample(const float* d_logits, int32_t n, float temperature, float topp, float coin,
+                 int32_t* h_token_out, void* hip_stream);
 
 #ifdef __cplusplus
 }

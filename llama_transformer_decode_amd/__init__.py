@@ -103,6 +103,12 @@ class Model:
     def generate(self, token: int, pos: int, n: int) -> np.ndarray:
         return ld.ld_generate_greedy(self.h, int(token), int(pos), int(n))
 
+    def generate_sampled(self, prompt, pos: int, n: int, temperature: float = 0.0, topp: float = 0.0,
+                         stop_token: int = -1, coins=None) -> np.ndarray:
+        """The prompt-forcing, sampling generation loop (ld_generate)."""
+        return ld.ld_generate(self.h, prompt, int(pos), int(n), float(temperature), float(topp), int(stop_token),
+                              coins)
+
     def reset(self) -> None:
         ld.ld_reset(self.h)
 

@@ -9,13 +9,39 @@
 namespace ld {
 
 // Per-step scalars kept in device memory so that one captured graph serves
-// every position: the classifier kernel writes `next` and advances
-// (token, pos) for the following step.
+// every position: the next-token kernel writes `next` and advances
+// (token, pos) for the following step.  Once a step has chosen the stop token
+// `stopped` is set: later steps write no cache row and choose nothing, so
+// graph replays queued past the stop leave the model where it stopped.
 struct StepState {
     int32_t token;
     int32_t pos;
     int32_t next;
-    int32_t pad;
+    int32_t stopped;
+};
+
+// How the next token is chosen ("run.c 逐行解讀" §6 and §7).  The step at
+// position p takes forced[p + 1] while p + 1 < force_end (the prompt); else
+// the argmax when temperature <= 0; else a draw with coin coins[p] from
+// softmax(logits / temperature), over the smallest most likely set of
+// cumulative probability >= topp when 0 < topp < 1.
+struct GenControl {
+    float temperature;
+    float topp;
+    int32_t stop_token;  // -1: none
+    int32_t force_end;   // absolute position bound of the forced tokens
+};
+
+struct NextTokenParams {
+    const float2* best;    // per-block (value, index bits) of the logits
+    int nblocks;
+    const float* logits;
+    int n;                 // vocabulary size
+    const GenControl* ctl;
+    const int32_t* forced; // by position
+    const float* coins;    // by position
+    StepState* state;
+    int32_t* tokens_out;   // tokens_out[pos] = the token chosen at position pos (may be NULL)
 };
 
 // Kinds of the matrix-vector kernel family.  All read one fp32 row-major
@@ -90,14 +116,17 @@ int attn_splits(int head_size, int seq_len, int n_kv_heads);  // grid.y of the a
 hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention + merge
 
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
-// argmax of v: per-block bests, then the final reduction into st->next
-hipError_t argmax_launch(const float* v, int n, float2* best, int nblocks, StepState* st, hipStream_t s);
-// final reduction of the classifier's per-block bests: st->next, tokens_out[pos], advance (token, pos)
-hipError_t argmax_final_launch(const float2* best, int nblocks, StepState* st, int32_t* tokens_out, hipStream_t s);
+hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s);
+// per-block bests of v (the classifier kernel writes its own)
+hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblocks, hipStream_t s);
 int argmax_blocks(int n);
+// the next token from the per-block bests and the logits: st->next,
+// tokens_out[pos], advance (token, pos), set `stopped` at the stop token
+hipError_t next_token_launch(const NextTokenParams& p, hipStream_t s);
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxGroup = 8;   // query heads per kv head
 constexpr int kMaxN = 32768;   // longest input vector of a matrix-vector kernel
+constexpr int kMaxSampleVocab = 32768;  // largest vocabulary the sampler holds in registers
 
 }  // namespace ld

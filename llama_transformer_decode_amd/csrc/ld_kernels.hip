@@ -4,7 +4,9 @@
 // The step is the forward() walkthrough of the "run.c 逐行解讀" page (§4):
 // RMSNorm, q/k/v matmuls, RoPE, KV-cache write, grouped-query attention,
 // output matmul + residual, FFN RMSNorm, SwiGLU, down matmul + residual, final
-// RMSNorm, classifier, and the greedy argmax of the "run.c" page.
+// RMSNorm, classifier, and the choice of the next token: the greedy argmax of
+// the "run.c" page, or the temperature / top-p draw and prompt forcing of the
+// "run.c 逐行解讀" page (§6, §7).
 //
 // At batch 1 every weight is used once per token for one multiply-add, so the
 // step is bound by HBM bandwidth (0.5 flop per byte).  The matrix-vector
@@ -121,27 +123,245 @@ __device__ void publish_best(float bv, int bi, float2* best) {
 
 constexpr int kArgmaxThreads = 256;
 
-__global__ __launch_bounds__(kArgmaxThreads) void argmax_final_kernel(const float2* best, int nblocks,
-                                                                      StepState* st, int32_t* tokens_out) {
-    float v = -INFINITY;
-    int i = INT_MAX;
-#pragma unroll 4
-    for (int b = threadIdx.x; b < nblocks; b += kArgmaxThreads) {
-        const float2 e = best[b];
-        const int ei = __float_as_int(e.y);
-        if (better(e.x, ei, v, i)) {
-            v = e.x;
-            i = ei;
+// ---------------------------------------------------------------------------
+// The next token ("run.c 逐行解讀" §6 sample() and §7 generate()).
+//
+// One block of NT threads.  A forced prompt token is taken as is.
+// Otherwise the per-block bests of the logits give the greedy choice and the
+// maximum logit; at a positive temperature the threads then hold the softmax
+// numerators e_i = exp((l_i - max) / T) in registers, and the draw is the
+// cumulative walk of the "run.c" sample(): the first token, in walk order,
+// whose cumulative mass exceeds coin * (mass of the candidates).  Masses are
+// summed in double, every block sum in one fixed order, so every thread holds
+// the same bits and takes the same branch.  No sort and no scan: each search
+// below is a bisection whose test is one block sum.
+//  * Without top-p the walk runs in index order: the token is the first i
+//    whose prefix mass exceeds coin * S (bisection over i).
+//  * With top-p it runs in descending probability, ties to the lower index.
+//    Bisections over fp32 bit patterns (the integer order of positive floats
+//    is their numeric order) find
+//    (a) v_k, the value of the last candidate: the largest v whose mass
+//        G(v) = sum of e_i >= v reaches topp * S.  The candidates are every
+//        e_i > v_k and the first j tokens (index order) equal to v_k, j the
+//        fewest that bring the candidate mass M to topp * S;
+//    (b) u, the value of the drawn token: the largest candidate value with
+//        G(u) > coin * M.  Among the tokens equal to u the draw takes the
+//        (q+1)-th in index order, q = floor((coin * M - G(> u)) / u), found by
+//        (c) a bisection over i on the count of those tokens up to i.
+
+template <int NW>
+struct SampleShared {
+    double red[2][NW];
+    int ired[2][NW];
+};
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+// the wave's total, the same bits in every lane (the wave_sum pattern in double)
+__device__ __forceinline__ double wave_sum_d(double v) {
+    v += dpp_d<kQuadSwap1>(v);
+    v += dpp_d<kQuadSwap2>(v);
+    v += dpp_d<kRowHalfMirror>(v);
+    v += dpp_d<kRowMirror>(v);
+    v += dpp_d<kRowBcast15, 0xa>(v);
+    v += dpp_d<kRowBcast31, 0xc>(v);
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+    return __hiloint2double(hi, lo);
+}
+
+// Block reductions alternate between two LDS slots, so one barrier per call
+// suffices: a slot is rewritten two calls later, after every thread has
+// passed the barrier of the call in between and so has read it.
+template <int NW>
+__device__ double block_sum_d(double v, SampleShared<NW>& sh, int& ph) {
+    v = wave_sum_d(v);
+    if ((threadIdx.x & 63) == 0) sh.red[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += sh.red[ph][w];
+    ph ^= 1;
+    return t;
+}
+
+template <int NW>
+__device__ int block_sum_i(int v, SampleShared<NW>& sh, int& ph) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) sh.ired[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += sh.ired[ph][w];
+    ph ^= 1;
+    return t;
+}
+
+template <int NT, int E>
+__device__ int sample_draw(const float* __restrict__ logits, int n, float lmax, float temperature, float topp,
+                           float coin, SampleShared<NT / 64>& sh) {
+    // thread t holds tokens t + k * NT (coalesced loads)
+    const int t = threadIdx.x;
+    const double inv_t = 1.0 / (double)temperature;
+    float e[E];  // first the logits, then in place their numerators
+    // unconditional loads from a clamped index (no branch per load); tokens
+    // past the end are masked in the next loop
+#pragma unroll
+    for (int k = 0; k < E; ++k) e[k] = logits[(unsigned)min(t + k * NT, n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const float x = expf((float)(((double)e[k] - (double)lmax) * inv_t));
+        e[k] = (x == x && k * NT < n - t) ? x : 0.f;  // a NaN logit carries no mass
+        s += (double)e[k];
+        __builtin_amdgcn_sched_barrier(0);  // one exp at a time: E live floats, not E in flight
+    }
+    int ph = 0;
+    const double S = block_sum_d(s, sh, ph);
+    const double dcoin = (double)coin;
+
+    // masses and counts, the same bits in every thread; each is monotone in
+    // its argument because every partial sum adds non-negative terms in a
+    // fixed order
+    auto mass_at_least = [&](float v) {  // sum of e_i >= v
+        double a = 0.0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            a += (double)(e[k] >= v ? e[k] : 0.f);  // converted after the select: no E doubles held
+            if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        return block_sum_d(a, sh, ph);
+    };
+    // (index tests as k * NT <= idx - t: constants against one register, so
+    // no per-element index is kept live)
+    auto mass_upto = [&](int idx) {  // sum of e_i, i <= idx
+        const int rel = idx - t;
+        double a = 0.0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            a += (double)(k * NT <= rel ? e[k] : 0.f);
+            if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        return block_sum_d(a, sh, ph);
+    };
+    auto count_equal_upto = [&](float v, int idx) {  // number of e_i == v, i <= idx
+        const int rel = idx - t;
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) c += (e[k] == v) & (k * NT <= rel);
+        return block_sum_i(c, sh, ph);
+    };
+
+    if (!(topp > 0.f && topp < 1.f)) {
+        // index order: the first i with mass_upto(i) > coin * S.  mass_upto(-1)
+        // = 0 <= r and mass_upto(n - 1) = S > r (coin < 1)
+        const double r = dcoin * S;
+        int lo = -1, hi = n - 1;
+        while (hi - lo > 1) {
+            const int mid = lo + (hi - lo) / 2;
+            if (mass_upto(mid) > r)
+                hi = mid;
+            else
+                lo = mid;
+        }
+        return hi;
+    }
+
+    constexpr uint32_t kAboveOne = 0x3f800001u;  // the float just above 1 (the largest e_i is exp(0) = 1)
+    const double P = (double)topp * S;
+    // (a) G(bits lo) >= P > G(bits hi); G(0) = S > P, G(above 1) = 0
+    uint32_t lo = 0, hi = kAboveOne;
+    double g_hi = 0.0;
+    while (hi - lo > 1) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        const double g = mass_at_least(__uint_as_float(mid));
+        if (g >= P) {
+            lo = mid;
+        } else {
+            hi = mid;
+            g_hi = g;
         }
     }
-    block_best<kArgmaxThreads>(v, i);
+    const float vk = __uint_as_float(lo);  // > 0: G(smallest positive) = S > P
+    const double above_vk = g_hi;          // mass of the e_i > v_k
+    const int n_vk = count_equal_upto(vk, n - 1);
+    int j = (int)ceil((P - above_vk) / (double)vk);
+    j = max(1, min(j, n_vk));
+    const double M = above_vk + (double)j * (double)vk;
+    const double r = dcoin * M;
+
+    // (b) the largest candidate value u with G(u) > r; at v_k the candidate
+    // mass is M > r
+    uint32_t lo2 = lo, hi2 = kAboveOne;
+    double g_hi2 = 0.0;
+    while (hi2 - lo2 > 1) {
+        const uint32_t mid = lo2 + (hi2 - lo2) / 2;
+        const double g = mass_at_least(__uint_as_float(mid));
+        if (g > r) {
+            lo2 = mid;
+        } else {
+            hi2 = mid;
+            g_hi2 = g;
+        }
+    }
+    const float u = __uint_as_float(lo2);
+    const int n_u = lo2 == lo ? j : count_equal_upto(u, n - 1);
+    int q = (int)floor((r - g_hi2) / (double)u);
+    q = max(0, min(q, n_u - 1));
+
+    // (c) the (q+1)-th token equal to u in index order: the first i with
+    // count_equal_upto(u, i) >= q + 1
+    int ilo = -1, ihi = n - 1;
+    while (ihi - ilo > 1) {
+        const int mid = ilo + (ihi - ilo) / 2;
+        if (count_equal_upto(u, mid) >= q + 1)
+            ihi = mid;
+        else
+            ilo = mid;
+    }
+    return ihi;
+}
+
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void next_token_kernel(NextTokenParams p) {
+    __shared__ SampleShared<NT / 64> sh;
+    const int pos = p.state->pos;
+    if (p.state->stopped) return;
+    const GenControl c = *p.ctl;
+    int next;
+    if (pos + 1 < c.force_end) {
+        next = p.forced[pos + 1];
+    } else {
+        float v = -INFINITY;
+        int i = INT_MAX;
+        for (int b = threadIdx.x; b < p.nblocks; b += NT) {
+            const float2 e = p.best[b];
+            const int ei = __float_as_int(e.y);
+            if (better(e.x, ei, v, i)) {
+                v = e.x;
+                i = ei;
+            }
+        }
+        block_best<NT>(v, i);
+        next = i == INT_MAX ? 0 : i;  // every value NaN: token 0
+        // a non-finite maximum leaves no distribution to draw from: greedy
+        if (c.temperature > 0.f && isfinite(v) && p.n <= E * NT)
+            next = sample_draw<NT, E>(p.logits, p.n, v, c.temperature, c.topp, p.coins[pos], sh);
+    }
+    __syncthreads();  // every thread has read the state
     if (threadIdx.x == 0) {
-        if (i == INT_MAX) i = 0;  // every value was NaN
-        const int pos = st->pos;
-        st->next = i;
-        if (tokens_out) tokens_out[pos] = i;
-        st->token = i;
-        st->pos = pos + 1;
+        p.state->next = next;
+        if (p.tokens_out) p.tokens_out[pos] = next;
+        p.state->token = next;
+        p.state->pos = pos + 1;
+        if (c.stop_token >= 0 && next == c.stop_token) p.state->stopped = 1;
     }
 }
 
@@ -235,10 +455,11 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     float4 w[RPI][NX];
     if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
 
-    int pos = 0, token = 0;
+    int pos = 0, token = 0, stopped = 0;
     if constexpr (KIND == K_QKV || KIND == K_CLS) {
         pos = p.state->pos;
         token = p.state->token;
+        stopped = p.state->stopped;
     }
 
     // ---- prologue: x (layer 0 of the q/k/v kernel reads the embedding row) ----
@@ -341,9 +562,9 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
                     const float v = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
                     if (is_q)
                         p.out[row] = v;
-                    else
+                    else if (!stopped)
                         p.kc[(size_t)pos * p.kv_stride + local] = v;
-                } else {
+                } else if (!stopped) {
                     p.vc[(size_t)pos * p.kv_stride + (row - p.seg2)] = total;
                 }
             }
@@ -374,7 +595,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
 }
 
 // Argmax of a vector: per-block bests (the reduction the classifier uses),
-// then argmax_final_kernel.
+// then next_token_kernel.
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const float* v, int n, float2* best) {
     float bv = -INFINITY;
     int bi = INT_MAX;
@@ -386,10 +607,13 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const fl
     publish_best<kArgmaxThreads>(bv, bi, best);
 }
 
+__global__ void set_control_kernel(GenControl* dst, GenControl c) { *dst = c; }
+
 __global__ void set_state_kernel(StepState* st, int token, int pos) {
     st->token = token;
     st->pos = pos;
     st->next = -1;
+    st->stopped = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -992,6 +1216,11 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s) {
+    hipLaunchKernelGGL(set_control_kernel, dim3(1), dim3(1), 0, s, dst, c);
+    return hipGetLastError();
+}
+
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s) {
     hipLaunchKernelGGL(set_state_kernel, dim3(1), dim3(1), 0, s, st, token, pos);
     return hipGetLastError();
@@ -1002,14 +1231,16 @@ int argmax_blocks(int n) {
     return b < 1 ? 1 : (b > 1024 ? 1024 : b);
 }
 
-hipError_t argmax_launch(const float* v, int n, float2* best, int nblocks, StepState* st, hipStream_t s) {
+hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblocks, hipStream_t s) {
     hipLaunchKernelGGL(argmax_partial_kernel, dim3(nblocks), dim3(kArgmaxThreads), 0, s, v, n, best);
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, s, best, nblocks, st, nullptr);
     return hipGetLastError();
 }
 
-hipError_t argmax_final_launch(const float2* best, int nblocks, StepState* st, int32_t* tokens_out, hipStream_t s) {
-    hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(kArgmaxThreads), 0, s, best, nblocks, st, tokens_out);
+// 1024 threads of 32 tokens each hold a vocabulary of up to kMaxSampleVocab;
+// a larger one is only ever chosen from greedily (the kernel checks)
+hipError_t next_token_launch(const NextTokenParams& p, hipStream_t s) {
+    static_assert(kMaxSampleVocab == 1024 * 32, "sampler register layout");
+    hipLaunchKernelGGL((next_token_kernel<1024, 32>), dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

@@ -9,9 +9,11 @@
 //   wo_residual      x += Wo xb
 //   w1w3_swiglu      RMSNorm(x) -> silu(W1 .) * (W3 .) -> hb
 //   w2_residual      x += W2 hb
-// then classifier_argmax: RMSNorm(x) -> Wcls -> logits -> greedy token.
-// Token and position live in device memory, so the same captured graph
-// replays every step of a greedy generation.
+// then classifier_argmax: RMSNorm(x) -> Wcls -> logits -> next token (the
+// greedy argmax, a forced prompt token or a temperature / top-p draw, as the
+// device-side GenControl says).  Token, position and the sampling control
+// live in device memory, so the same captured graph replays every step of a
+// generation.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -103,8 +105,16 @@ struct ld_model {
     float *kc = nullptr, *vc = nullptr, *part_acc = nullptr;
     float2 *part_ml = nullptr, *rope = nullptr, *best = nullptr;
     StepState* state = nullptr;
-    int32_t* tokens = nullptr;     // tokens[pos] = argmax of step pos
+    int32_t* tokens = nullptr;     // tokens[pos] = the token chosen at step pos
     int32_t* h_tokens = nullptr;   // pinned staging
+    GenControl* ctl = nullptr;     // device copy of the sampling control
+    GenControl ctl_host{};         // what the queued work last set it to
+    int32_t* forced = nullptr;     // forced prompt tokens by position (seq_len + 1)
+    float* coins = nullptr;        // coins by position (seq_len)
+    int32_t* h_forced = nullptr;   // pinned staging of ld_generate's inputs
+    float* h_coins = nullptr;
+    StepState* h_poll = nullptr;   // pinned: 3 state snapshots
+    hipEvent_t ev_poll[2] = {nullptr, nullptr};
     GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
@@ -134,10 +144,25 @@ void release(ld_model* m) {
     if (m->graph) (void)hipGraphDestroy(m->graph);
     for (void* p : m->dev_allocs) (void)hipFree(p);
     if (m->h_tokens) (void)hipHostFree(m->h_tokens);
+    if (m->h_forced) (void)hipHostFree(m->h_forced);
+    if (m->h_coins) (void)hipHostFree(m->h_coins);
+    if (m->h_poll) (void)hipHostFree(m->h_poll);
+    for (hipEvent_t e : m->ev_poll)
+        if (e) (void)hipEventDestroy(e);
     if (m->ev_in) (void)hipEventDestroy(m->ev_in);
     if (m->ev_out) (void)hipEventDestroy(m->ev_out);
     if (m->stream) (void)hipStreamDestroy(m->stream);
     delete m;
+}
+
+constexpr GenControl kGreedy = {0.f, 0.f, -1, 0};
+
+// Queue a change of the device-side control when it differs from the last one.
+int set_control(ld_model* m, const GenControl& c) {
+    if (std::memcmp(&c, &m->ctl_host, sizeof(c)) == 0) return LD_OK;
+    HIP_TRY(set_control_launch(m->ctl, c, m->stream));
+    m->ctl_host = c;
+    return LD_OK;
 }
 
 // Order the model's stream after the caller's queued work, and back.
@@ -277,7 +302,17 @@ int launch_step(ld_model* m, Timer* timer) {
     p.best = m->best;
     mark(timer, s, KCLS, true);
     HIP_TRY(gemv_launch(m->pcls, p, s));
-    HIP_TRY(argmax_final_launch(m->best, m->pcls.grid, m->state, m->tokens, s));
+    NextTokenParams nt{};
+    nt.best = m->best;
+    nt.nblocks = m->pcls.grid;
+    nt.logits = m->logits;
+    nt.n = c.vocab_size;
+    nt.ctl = m->ctl;
+    nt.forced = m->forced;
+    nt.coins = m->coins;
+    nt.state = m->state;
+    nt.tokens_out = m->tokens;
+    HIP_TRY(next_token_launch(nt, s));
     mark(timer, s, KCLS, false);
     return LD_OK;
 }
@@ -382,6 +417,8 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e != hipSuccess) { rc = fail_hip(e, "hipStreamCreate"); break; }
         e = hipEventCreateWithFlags(&m->ev_in, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_out, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[0], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[1], hipEventDisableTiming);
         if (e != hipSuccess) { rc = fail_hip(e, "hipEventCreate"); break; }
 
         const size_t cache = (size_t)cfg->n_layers * cfg->seq_len * kv;
@@ -392,9 +429,16 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             (rc = dalloc(m, &m->part_ml, (size_t)cfg->n_heads * m->nsplit)) ||
             (rc = dalloc(m, &m->rope, (size_t)cfg->seq_len * (m->hs / 2))) ||
             (rc = dalloc(m, &m->state, 1)) ||
-            (rc = dalloc(m, &m->tokens, (size_t)cfg->seq_len)))
+            (rc = dalloc(m, &m->tokens, (size_t)cfg->seq_len)) || (rc = dalloc(m, &m->ctl, 1)) ||
+            (rc = dalloc(m, &m->forced, (size_t)cfg->seq_len + 1)) ||
+            (rc = dalloc(m, &m->coins, (size_t)cfg->seq_len)))
             break;
         e = hipHostMalloc((void**)&m->h_tokens, sizeof(int32_t) * (size_t)cfg->seq_len, hipHostMallocDefault);
+        if (e == hipSuccess)
+            e = hipHostMalloc((void**)&m->h_forced, sizeof(int32_t) * ((size_t)cfg->seq_len + 1), hipHostMallocDefault);
+        if (e == hipSuccess)
+            e = hipHostMalloc((void**)&m->h_coins, sizeof(float) * (size_t)cfg->seq_len, hipHostMallocDefault);
+        if (e == hipSuccess) e = hipHostMalloc((void**)&m->h_poll, sizeof(StepState) * 3, hipHostMallocDefault);
         if (e != hipSuccess) { rc = fail_hip(e, "hipHostMalloc"); break; }
 
         if ((rc = (gemv_plan(K_QKV, cfg->dim + 2 * m->kv_dim, cfg->dim, &m->pq) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
@@ -413,6 +457,10 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e == hipSuccess) e = hipMemset(m->vc, 0, cache * sizeof(float));
         if (e == hipSuccess) e = hipMemset(m->state, 0, sizeof(StepState));
         if (e == hipSuccess) e = hipMemset(m->tokens, 0, sizeof(int32_t) * (size_t)cfg->seq_len);
+        if (e == hipSuccess) e = hipMemset(m->forced, 0, sizeof(int32_t) * ((size_t)cfg->seq_len + 1));
+        if (e == hipSuccess) e = hipMemset(m->coins, 0, sizeof(float) * (size_t)cfg->seq_len);
+        if (e == hipSuccess) e = hipMemcpy(m->ctl, &kGreedy, sizeof(GenControl), hipMemcpyHostToDevice);
+        m->ctl_host = kGreedy;
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) { rc = fail_hip(e, "initialise buffers"); break; }
     } while (0);
@@ -439,6 +487,7 @@ int ld_forward(ld_model* m, int32_t token, int32_t pos, const float** d_logits_o
     if (token < 0 || token >= m->cfg.vocab_size || pos < 0 || pos >= m->cfg.seq_len) return LD_E_RANGE;
     int rc = enter(m);
     if (rc) return rc;
+    if ((rc = set_control(m, kGreedy))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     rc = run_step(m);
     if (rc) return rc;
@@ -464,6 +513,7 @@ int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps,
     if (n_steps == 0) return LD_OK;
     int rc = enter(m);
     if (rc) return rc;
+    if ((rc = set_control(m, kGreedy))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     for (int i = 0; i < n_steps; ++i) {
         rc = run_step(m);
@@ -473,6 +523,76 @@ int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps,
                            m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
     std::memcpy(h_tokens_out, m->h_tokens, sizeof(int32_t) * (size_t)n_steps);
+    return leave(m);
+}
+
+int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t pos, int32_t n_steps,
+                const ld_sampling* sampling, const float* h_coins, int32_t* h_tokens_out, int32_t* n_out) {
+    if (!m || !h_prompt || !sampling || !n_out || (!h_tokens_out && n_steps > 0)) return LD_E_NULL;
+    *n_out = 0;
+    const ld_config& c = m->cfg;
+    if (n_prompt < 1 || pos < 0 || n_steps < 0 || (long long)pos + n_steps > c.seq_len) return LD_E_RANGE;
+    for (int i = 0; i < n_prompt; ++i)
+        if (h_prompt[i] < 0 || h_prompt[i] >= c.vocab_size) return LD_E_RANGE;
+    const float T = sampling->temperature;
+    if (std::isnan(T) || std::isinf(T) || std::isnan(sampling->topp)) return LD_E_RANGE;
+    if (sampling->stop_token < -1 || sampling->stop_token >= c.vocab_size) return LD_E_RANGE;
+    const int n_forced = n_prompt - 1 < n_steps ? n_prompt - 1 : n_steps;  // steps whose next token is forced
+    const bool draws = T > 0.f && n_forced < n_steps;
+    if (draws) {
+        if (c.vocab_size > kMaxSampleVocab) return LD_E_UNSUPPORTED;
+        if (!h_coins) return LD_E_NULL;
+        for (int i = n_forced; i < n_steps; ++i)
+            if (!(h_coins[i] >= 0.f && h_coins[i] < 1.f)) return LD_E_RANGE;
+    }
+    if (n_steps == 0) return LD_OK;
+    int rc = enter(m);
+    if (rc) return rc;
+
+    // the step at position p takes forced[p + 1] while p + 1 < force_end
+    const GenControl ctl = {T > 0.f ? T : 0.f, sampling->topp, sampling->stop_token, pos + 1 + n_forced};
+    if ((rc = set_control(m, ctl))) return rc;
+    if (n_forced > 0) {
+        std::memcpy(m->h_forced, h_prompt + 1, sizeof(int32_t) * (size_t)n_forced);
+        HIP_TRY(hipMemcpyAsync(m->forced + pos + 1, m->h_forced, sizeof(int32_t) * (size_t)n_forced,
+                               hipMemcpyHostToDevice, m->stream));
+    }
+    if (draws) {
+        const int nd = n_steps - n_forced;
+        std::memcpy(m->h_coins, h_coins + n_forced, sizeof(float) * (size_t)nd);
+        HIP_TRY(hipMemcpyAsync(m->coins + pos + n_forced, m->h_coins, sizeof(float) * (size_t)nd,
+                               hipMemcpyHostToDevice, m->stream));
+    }
+    HIP_TRY(set_state_launch(m->state, h_prompt[0], pos, m->stream));
+
+    // Steps go out in chunks.  With a stop token each chunk is followed by a
+    // snapshot of the step state; the host reads the previous chunk's
+    // snapshot while the current chunk runs, and stops queueing once a step
+    // has chosen the stop token (steps queued past it change nothing).
+    constexpr int kChunk = 16;
+    const bool polls = sampling->stop_token >= 0;
+    int issued = 0;
+    for (int chunk = 0; issued < n_steps; ++chunk) {
+        const int k = n_steps - issued < kChunk ? n_steps - issued : kChunk;
+        for (int i = 0; i < k; ++i)
+            if ((rc = run_step(m))) return rc;
+        issued += k;
+        if (!polls || issued >= n_steps) continue;
+        const int slot = chunk & 1;
+        HIP_TRY(hipMemcpyAsync(&m->h_poll[slot], m->state, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+        HIP_TRY(hipEventRecord(m->ev_poll[slot], m->stream));
+        if (chunk > 0) {
+            HIP_TRY(hipEventSynchronize(m->ev_poll[slot ^ 1]));
+            if (m->h_poll[slot ^ 1].stopped) break;
+        }
+    }
+    HIP_TRY(hipMemcpyAsync(&m->h_poll[2], m->state, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    HIP_TRY(hipMemcpyAsync(m->h_tokens, m->tokens + pos, sizeof(int32_t) * (size_t)n_steps, hipMemcpyDeviceToHost,
+                           m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    const int ran = m->h_poll[2].pos - pos;
+    std::memcpy(h_tokens_out, m->h_tokens, sizeof(int32_t) * (size_t)ran);
+    *n_out = ran;
     return leave(m);
 }
 
@@ -508,6 +628,7 @@ int ld_profile_steps(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, l
     }
     double total[KNUM] = {0};
     int count[KNUM] = {0};
+    if ((rc = set_control(m, kGreedy))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     for (int i = 0; i < n_steps && rc == LD_OK; ++i) {
         t.used = 0;
@@ -568,6 +689,41 @@ struct Temps {
 };
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// per-block bests of v, then the next-token kernel at position 0 with control c
+int op_next_token(const float* d_v, int n, const GenControl& c, float coin, int32_t* h_out, hipStream_t s) {
+    const int nb = argmax_blocks(n);
+    Temps tmp;
+    float2* best = nullptr;
+    StepState* st = nullptr;
+    GenControl* ctl = nullptr;
+    float* coins = nullptr;
+    HIP_TRY(tmp.get(&best, (size_t)nb));
+    HIP_TRY(tmp.get(&st, 1));
+    HIP_TRY(tmp.get(&ctl, 1));
+    HIP_TRY(tmp.get(&coins, 1));
+    const StepState st0 = {0, 0, -1, 0};
+    HIP_TRY(hipMemcpy(st, &st0, sizeof(st0), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(ctl, &c, sizeof(c), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(coins, &coin, sizeof(coin), hipMemcpyHostToDevice));
+    HIP_TRY(argmax_partial_launch(d_v, n, best, nb, s));
+    NextTokenParams p{};
+    p.best = best;
+    p.nblocks = nb;
+    p.logits = d_v;
+    p.n = n;
+    p.ctl = ctl;
+    p.forced = nullptr;
+    p.coins = coins;
+    p.state = st;
+    p.tokens_out = nullptr;
+    HIP_TRY(next_token_launch(p, s));
+    StepState out{};
+    HIP_TRY(hipMemcpyAsync(&out, st, sizeof(out), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    *h_out = out.next;
+    return LD_OK;
+}
 
 int op_shape_ok(int rows, int n) {
     if (rows <= 0 || n <= 0 || (n % 4)) return LD_E_CONFIG;
@@ -728,20 +884,19 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
 int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_stream) {
     if (!d_v || !h_index_out) return LD_E_NULL;
     if (n <= 0) return LD_E_RANGE;
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const int nb = argmax_blocks(n);
-    Temps tmp;
-    float2* best = nullptr;
-    StepState* st = nullptr;
-    HIP_TRY(tmp.get(&best, (size_t)nb));
-    HIP_TRY(tmp.get(&st, 1));
-    HIP_TRY(hipMemset(st, 0, sizeof(StepState)));
-    HIP_TRY(argmax_launch(d_v, n, best, nb, st, s));
-    StepState out{};
-    HIP_TRY(hipMemcpyAsync(&out, st, sizeof(out), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    *h_index_out = out.next;
-    return LD_OK;
+    return op_next_token(d_v, n, kGreedy, 0.f, h_index_out, static_cast<hipStream_t>(hip_stream));
+}
+
+int ld_op_sample(const float* d_logits, int32_t n, float temperature, float topp, float coin,
+                 int32_t* h_token_out, void* hip_stream) {
+    if (!d_logits || !h_token_out) return LD_E_NULL;
+    if (n <= 0 || std::isnan(temperature) || std::isinf(temperature) || std::isnan(topp)) return LD_E_RANGE;
+    if (temperature > 0.f) {
+        if (!(coin >= 0.f && coin < 1.f)) return LD_E_RANGE;
+        if (n > kMaxSampleVocab) return LD_E_UNSUPPORTED;
+    }
+    const GenControl c = {temperature > 0.f ? temperature : 0.f, topp, -1, 0};
+    return op_next_token(d_logits, n, c, coin, h_token_out, static_cast<hipStream_t>(hip_stream));
 }
 
 }  // extern "C"

@@ -27,9 +27,9 @@ LD_OPT_NO_GRAPH = 1
 # Every symbol include/ld.h declares.
 EXPORTS = (
     "ld_weights_size", "ld_create", "ld_reset", "ld_forward", "ld_argmax_last", "ld_generate_greedy",
-    "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail", "ld_profile_steps",
+    "ld_generate", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail", "ld_profile_steps",
     "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope", "ld_op_attention",
-    "ld_op_argmax",
+    "ld_op_argmax", "ld_op_sample",
 )
 
 
@@ -50,6 +50,11 @@ class ld_config(ctypes.Structure):
 class ld_options(ctypes.Structure):
     _fields_ = [("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("shared_classifier", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class ld_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("topp", ctypes.c_float), ("stop_token", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class ld_kernel_stat(ctypes.Structure):
@@ -83,6 +88,7 @@ def library():
             "ld_forward": ([_P, _I, _I, ctypes.POINTER(_P)], ctypes.c_int),
             "ld_argmax_last": ([_P, ctypes.POINTER(_I)], ctypes.c_int),
             "ld_generate_greedy": ([_P, _I, _I, _I, _P], ctypes.c_int),
+            "ld_generate": ([_P, _P, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I)], ctypes.c_int),
             "ld_kv_cache": ([_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t)],
                             ctypes.c_int),
             "ld_destroy": ([_P], None),
@@ -95,6 +101,7 @@ def library():
             "ld_op_qkv_rope": ([_P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P], ctypes.c_int),
             "ld_op_attention": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_argmax": ([_P, _I, ctypes.POINTER(_I), _P], ctypes.c_int),
+            "ld_op_sample": ([_P, _I, _F, _F, _F, ctypes.POINTER(_I), _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -161,6 +168,24 @@ def ld_generate_greedy(h: int, token: int, pos: int, n_steps: int) -> np.ndarray
     return out[:n_steps]
 
 
+def ld_generate(h: int, prompt, pos: int, n_steps: int, temperature: float = 0.0, topp: float = 0.0,
+                stop_token: int = -1, coins=None) -> np.ndarray:
+    """Returns the tokens of the steps run (fewer than n_steps after a stop)."""
+    prompt = np.ascontiguousarray(prompt, dtype=np.int32)
+    c = None
+    if coins is not None:
+        c = np.ascontiguousarray(coins, dtype=np.float32)
+        if c.size < n_steps:
+            raise ValueError("need one coin per step")
+    out = np.zeros(max(n_steps, 1), np.int32)
+    n_out = _I(0)
+    smp = ld_sampling(temperature, topp, stop_token, 0)
+    _check(library().ld_generate(h, prompt.ctypes.data if prompt.size else None, prompt.size, pos, n_steps,
+                                 ctypes.byref(smp), c.ctypes.data if c is not None else None, out.ctypes.data,
+                                 ctypes.byref(n_out)), "ld_generate")
+    return out[:n_out.value]
+
+
 def ld_kv_cache(h: int):
     k, v, n = _P(), _P(), ctypes.c_size_t(0)
     _check(library().ld_kv_cache(h, ctypes.byref(k), ctypes.byref(v), ctypes.byref(n)), "ld_kv_cache")
@@ -208,4 +233,11 @@ def ld_op_attention(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out,
 def ld_op_argmax(d_v, n, stream=0) -> int:
     out = _I(0)
     _check(library().ld_op_argmax(d_v, n, ctypes.byref(out), stream or None), "ld_op_argmax")
+    return out.value
+
+
+def ld_op_sample(d_logits, n, temperature, topp, coin, stream=0) -> int:
+    out = _I(0)
+    _check(library().ld_op_sample(d_logits, n, temperature, topp, coin, ctypes.byref(out), stream or None),
+           "ld_op_sample")
     return out.value

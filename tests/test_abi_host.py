@@ -109,3 +109,23 @@ def test_create_rejects_before_touching_the_device():
     assert lib.ld_create(ctypes.byref(wide), ctypes.byref(o), fake, nbytes, None, ctypes.byref(h)) == \
         ld.LD_E_UNSUPPORTED
     assert h.value is None
+
+
+def test_generate_and_sample_argument_checks_come_first():
+    lib = pkg.library()
+    smp = ld.ld_sampling(0.8, 0.9, -1, 0)
+    toks = (ctypes.c_int32 * 4)()
+    n_out = ctypes.c_int32(7)
+    prompt = (ctypes.c_int32 * 1)(1)
+    assert lib.ld_generate(None, prompt, 1, 0, 4, ctypes.byref(smp), None, toks, ctypes.byref(n_out)) == ld.LD_E_NULL
+    fake = 0x10000  # never dereferenced: every case fails its argument check first
+    tok = ctypes.c_int32()
+    assert lib.ld_op_sample(None, 8, 1.0, 0.0, 0.5, ctypes.byref(tok), None) == ld.LD_E_NULL
+    assert lib.ld_op_sample(fake, 8, 1.0, 0.0, 0.5, None, None) == ld.LD_E_NULL
+    assert lib.ld_op_sample(fake, 0, 1.0, 0.0, 0.5, ctypes.byref(tok), None) == ld.LD_E_RANGE
+    for coin in (-0.1, 1.0, float("nan")):
+        assert lib.ld_op_sample(fake, 8, 1.0, 0.0, coin, ctypes.byref(tok), None) == ld.LD_E_RANGE
+    for t in (float("nan"), float("inf")):
+        assert lib.ld_op_sample(fake, 8, t, 0.0, 0.5, ctypes.byref(tok), None) == ld.LD_E_RANGE
+    assert lib.ld_op_sample(fake, 8, 1.0, float("nan"), 0.5, ctypes.byref(tok), None) == ld.LD_E_RANGE
+    assert lib.ld_op_sample(fake, 40000, 1.0, 0.9, 0.5, ctypes.byref(tok), None) == ld.LD_E_UNSUPPORTED
