@@ -122,6 +122,19 @@ int ld_argmax_last(ld_model* m, int32_t* h_token_out);
  * h_tokens_out: caller-owned host array of n_steps int32.  Synchronous. */
 int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, int32_t* h_tokens_out);
 
+/* Prompt prefill: the decode step for h_tokens[i] at position pos + i, for
+ * i = 0 .. n_tokens - 1, computed for all prompt tokens at once (the R/Keras
+ * page's call_with_cache over a whole prompt with its causal mask; the same
+ * result as n_tokens ld_forward calls in order).  Cache rows pos ..
+ * pos + n_tokens - 1 of every layer are written; *d_logits_out receives the
+ * logits of the last token (library-owned device memory, as ld_forward's),
+ * and ld_argmax_last then returns their argmax.  Needs 1 <= n_tokens and
+ * pos + n_tokens <= seq_len; every token id in [0, vocab_size).
+ * h_tokens: caller-owned host array, read before the call returns.
+ * Asynchronous on the model's stream, like ld_forward.  LD_E_UNSUPPORTED for
+ * a head size the prefill attention kernel has no instance for. */
+int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t pos, const float** d_logits_out);
+
 /* How the generation loop chooses tokens after the prompt ("run.c 逐行解讀"
  * §6, sample(), three modes):
  *   temperature <= 0: the argmax (greedy, as above);
@@ -225,6 +238,23 @@ int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d
  * (n_heads * head_size).  Query head h reads kv head floor(h*n_kv/n_heads). */
 int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
                     int32_t n_kv_heads, int32_t head_size, int32_t pos, float* d_out, void* hip_stream);
+
+/* d_out (m x n) = d_a (m x k) * d_w (n x k)^T, all fp32 row-major: the
+ * matrix product of prefill, out[i][j] = sum_t a[i][t] w[j][t] ("run.c 逐行解讀"
+ * §4 Matmul, for m input vectors at once).  k % 4 == 0 (else LD_E_CONFIG);
+ * d_a and d_w 16-byte aligned (else LD_E_ALIGN).  Synchronous. */
+int ld_op_gemm(const float* d_a, const float* d_w, int32_t m, int32_t n, int32_t k, float* d_out,
+               void* hip_stream);
+
+/* Causal attention of n_tokens queries at positions pos .. pos + n_tokens - 1
+ * ("run.c 逐行解讀" §4 step 2e for each of them): d_q (n_tokens,
+ * n_heads * head_size), caches with rows of n_kv_heads * head_size floats,
+ * rows 0 .. pos + n_tokens - 1 read; query head h reads kv head
+ * floor(h * n_kv_heads / n_heads).  d_out (n_tokens, n_heads * head_size).
+ * Synchronous. */
+int ld_op_attention_prefill(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_size, int32_t pos, int32_t n_tokens, float* d_out,
+                            void* hip_stream);
 
 /* Lowest index of the maximum of d_v[0..n) ("run.c", argmax). */
 int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_stream);

@@ -93,6 +93,15 @@ class Model:
         ptr = ld.ld_forward(self.h, int(token), int(pos))
         return copy_from_device(ptr, (self.cfg.vocab_size,), stream=self.stream)
 
+    def prefill(self, tokens, pos: int):
+        """All prompt tokens at positions pos.. at once; returns the last token's logits (a copy)."""
+        ptr = self.prefill_async(tokens, pos)
+        return copy_from_device(ptr, (self.cfg.vocab_size,), stream=self.stream)
+
+    def prefill_async(self, tokens, pos: int) -> int:
+        """Queue a prompt prefill; returns the library-owned device logits pointer."""
+        return ld.ld_prefill(self.h, tokens, int(pos))
+
     def forward_async(self, token: int, pos: int) -> int:
         """Queue one decode step; returns the library-owned device logits pointer."""
         return ld.ld_forward(self.h, int(token), int(pos))

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SO = os.path.join(PKG, "libld.so")
-SOURCES = ["ld_kernels.hip", "ld_runtime.hip"]
+SOURCES = ["ld_kernels.hip", "ld_prefill.hip", "ld_runtime.hip"]
 ARCH = os.environ.get("LD_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

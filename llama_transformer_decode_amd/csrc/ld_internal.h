@@ -106,6 +106,54 @@ struct AttnParams {
     int chunk;             // keys per split (set by the launcher)
 };
 
+// Prompt prefill (ld_prefill.hip).  C(M x N) = A(M x K) B(N x K)^T on the
+// matrix cores, A the T tokens' activations, B's rows the weight rows, with
+// the decode GEMVs' epilogues.
+enum GemmKind : int {
+    G_PLAIN = 0,   // out[m][n] = C
+    G_RESID = 1,   // out[m][n] += C
+    G_QKV = 2,     // rows [Wq;Wk;Wv]; RoPE at position pos0 + m; q -> out, k/v -> cache rows
+    G_SWIGLU = 3,  // rows interleaved (w1 row u, w3 row u); out[m][u] = silu(C[m][2u]) * C[m][2u+1]
+};
+
+struct GemmParams {
+    const float* a;        // M x K, row stride lda
+    int lda;
+    int m, n, k;
+    const float* w0;       // B rows (as GemvParams)
+    const float* w1;
+    const float* w2;
+    int seg1, seg2;
+    float* out;
+    int ldo;
+    float* kc;             // G_QKV: this layer's caches
+    float* vc;
+    int kv_stride;
+    int head_size;
+    const float2* rope;
+    int pos0;
+};
+
+struct AttnPrefillParams {
+    const float* q;        // T x ldq (query heads contiguous)
+    int ldq;
+    const float* kc;       // this layer's caches, rows of kv_stride floats
+    const float* vc;
+    int kv_stride;
+    float* out;            // T x ldo
+    int ldo;
+    int t;                 // queries: positions pos0 .. pos0 + t - 1
+    int pos0;
+    int n_heads;
+    int n_kv_heads;
+};
+
+hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s);
+hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s);
+hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s);
+bool attn_prefill_supported(int head_size);
+hipError_t attn_prefill_launch(int head_size, const AttnPrefillParams& p, hipStream_t s);
+
 // Plans and launchers.  Return hipSuccess, or hipErrorInvalidValue for a
 // shape outside the compiled kernels.
 hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan);

@@ -1,0 +1,420 @@
+// ld_prefill.hip -- gfx950 (CDNA4) kernels of batched prompt prefill: the
+// decode step of the "run.c 逐行解讀" page (§4 forward()) applied to T
+// consecutive prompt tokens at once, as the R/Keras page's call_with_cache
+// does for a whole prompt under a causal mask.  With T tokens every weight is
+// used T times, so the projections are dense fp32 contractions
+// (2 flops per weight per token) and run on the matrix cores:
+//
+//   gemm_kernel     C(T x N) = A(T x K) * B(N x K)^T with v_mfma_f32_32x32x2f32,
+//                   epilogues: plain store, residual add, RoPE + cache append,
+//                   SwiGLU (the same epilogues as the decode GEMVs)
+//   attn_prefill    causal grouped-query attention of T queries over the
+//                   cache rows with v_mfma_f32_16x16x4f32 (flash-attention
+//                   style: online softmax, scores never leave registers)
+//   embed / rmsnorm_rows   the per-token gather and RMSNorm
+//
+// All arithmetic is fp32 (products and sums), as in the decode kernels.
+#include "ld_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+namespace ld {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Embedding gather and per-token RMSNorm.
+
+__global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ emb, const int32_t* __restrict__ tokens,
+                                                    int dim, float* __restrict__ x) {
+    const int t = blockIdx.x;
+    const float4* src = reinterpret_cast<const float4*>(emb + (size_t)tokens[t] * dim);
+    float4* dst = reinterpret_cast<float4*>(x + (size_t)t * dim);
+    for (int i = threadIdx.x; i < dim / 4; i += 256) dst[i] = src[i];
+}
+
+// out[t] = g * (x[t] * 1/sqrt(mean(x[t]^2) + eps)), one block per token, the
+// decode kernels' formula and order of operations.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                           float eps, int dim, float* __restrict__ out) {
+    __shared__ float part[4];
+    const int t = blockIdx.x;
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * dim);
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < dim / 4; i += 256) {
+        const float4 v = x4[i];
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    const float r = 1.0f / sqrtf(tot / (float)dim + eps);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    float4* o4 = reinterpret_cast<float4*>(out + (size_t)t * dim);
+    for (int i = threadIdx.x; i < dim / 4; i += 256) {
+        const float4 v = x4[i], w = g4[i];
+        o4[i] = make_float4(w.x * (r * v.x), w.y * (r * v.y), w.z * (r * v.z), w.w * (r * v.w));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// C = A * B^T on the matrix cores.
+//
+// A block of 256 threads computes a 128 x 128 tile of C: 4 waves in 2 x 2,
+// each a 64 x 64 quarter as 2 x 2 tiles of v_mfma_f32_32x32x2f32.  K is
+// walked in slabs of 16: both operand slabs go global -> registers -> LDS
+// (row-major, K contiguous, rows padded to 20 floats), double-buffered with
+// one barrier per slab; the next slab's global loads are in flight while the
+// current one is multiplied.  Within a slab, the MFMA's two k positions per
+// step are taken as k = 8h + s (lane half h, step s = 0..7), so each lane
+// reads 8 consecutive floats of its row with two 16-byte LDS loads; every k
+// is still used exactly once.  Rows of A past M and of B past N are clamped
+// (their results are not stored); k past K reads as zero.
+
+constexpr int kBM = 128, kBN = 128, kBK = 16, kRow = kBK + 4, kGemmThreads = 256;
+
+template <int KIND>
+__device__ __forceinline__ const float* b_row(const GemmParams& p, int r) {
+    if constexpr (KIND == G_SWIGLU) return ((r & 1) ? p.w1 : p.w0) + (size_t)(r >> 1) * p.k;
+    if constexpr (KIND == G_QKV) {
+        if (r < p.seg1) return p.w0 + (size_t)r * p.k;
+        if (r < p.seg2) return p.w1 + (size_t)(r - p.seg1) * p.k;
+        return p.w2 + (size_t)(r - p.seg2) * p.k;
+    }
+    return p.w0 + (size_t)r * p.k;
+}
+
+__device__ __forceinline__ float4 load_k4(const float* row, int k, int K) {
+    const float4 v = *reinterpret_cast<const float4*>(row + min(k, K - 4));
+    return k < K ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
+// runs a contiguous range of tiles (tiles that share a B slab then share an L2).
+__device__ __forceinline__ int xcd_local_block(int b, int nb) {
+    const int q = nb / 8, r = nb % 8, x = b % 8;
+    return x * q + min(x, r) + b / 8;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) float As[2][kBM][kRow];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kBN][kRow];
+
+    const int mtiles = (p.m + kBM - 1) / kBM;
+    const int tile = xcd_local_block(blockIdx.x, gridDim.x);
+    const int m0 = (tile % mtiles) * kBM, n0 = (tile / mtiles) * kBN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+
+    // this thread's two A rows and two B rows of every slab, and its k quad
+    const int lrow0 = tid >> 2, lrow1 = (tid >> 2) + 64, lk = (tid & 3) * 4;
+    const float* arow0 = p.a + (size_t)min(m0 + lrow0, p.m - 1) * p.lda;
+    const float* arow1 = p.a + (size_t)min(m0 + lrow1, p.m - 1) * p.lda;
+    const float* brow0 = b_row<KIND>(p, min(n0 + lrow0, p.n - 1));
+    const float* brow1 = b_row<KIND>(p, min(n0 + lrow1, p.n - 1));
+
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (p.k + kBK - 1) / kBK;
+    float4 ra0 = load_k4(arow0, lk, p.k), ra1 = load_k4(arow1, lk, p.k);
+    float4 rb0 = load_k4(brow0, lk, p.k), rb1 = load_k4(brow1, lk, p.k);
+    *reinterpret_cast<float4*>(&As[0][lrow0][lk]) = ra0;
+    *reinterpret_cast<float4*>(&As[0][lrow1][lk]) = ra1;
+    *reinterpret_cast<float4*>(&Bs[0][lrow0][lk]) = rb0;
+    *reinterpret_cast<float4*>(&Bs[0][lrow1][lk]) = rb1;
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int k = (kt + 1) * kBK + lk;
+            ra0 = load_k4(arow0, k, p.k);
+            ra1 = load_k4(arow1, k, p.k);
+            rb0 = load_k4(brow0, k, p.k);
+            rb1 = load_k4(brow1, k, p.k);
+        }
+        float av[2][8], bv[2][8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&As[buf][wm + i * 32 + li][lh * 8]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&As[buf][wm + i * 32 + li][lh * 8 + 4]);
+            av[i][0] = x0.x; av[i][1] = x0.y; av[i][2] = x0.z; av[i][3] = x0.w;
+            av[i][4] = x1.x; av[i][5] = x1.y; av[i][6] = x1.z; av[i][7] = x1.w;
+            const float4 y0 = *reinterpret_cast<const float4*>(&Bs[buf][wn + i * 32 + li][lh * 8]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&Bs[buf][wn + i * 32 + li][lh * 8 + 4]);
+            bv[i][0] = y0.x; bv[i][1] = y0.y; bv[i][2] = y0.z; bv[i][3] = y0.w;
+            bv[i][4] = y1.x; bv[i][5] = y1.y; bv[i][6] = y1.z; bv[i][7] = y1.w;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
+        if (more) {
+            *reinterpret_cast<float4*>(&As[buf ^ 1][lrow0][lk]) = ra0;
+            *reinterpret_cast<float4*>(&As[buf ^ 1][lrow1][lk]) = ra1;
+            *reinterpret_cast<float4*>(&Bs[buf ^ 1][lrow0][lk]) = rb0;
+            *reinterpret_cast<float4*>(&Bs[buf ^ 1][lrow1][lk]) = rb1;
+        }
+        __syncthreads();
+    }
+
+    // Epilogue.  Register r of tile (i, j) holds C(row, col) with
+    // row = wm + 32i + 8(r/4) + 4h + r%4 and col = wn + 32j + (lane % 32):
+    // lanes 2c and 2c+1 hold the adjacent columns (2c, 2c+1) of one row, the
+    // pair RoPE rotates and the (w1, w3) pair SwiGLU combines.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                const int gn = n0 + wn + j * 32 + li;
+                const float v = acc[i][j][r];
+                if constexpr (KIND == G_QKV || KIND == G_SWIGLU) {
+                    const float other = __shfl_xor(v, 1);
+                    if (gm < p.m && gn < p.n) {
+                        const bool odd = gn & 1;
+                        if constexpr (KIND == G_SWIGLU) {
+                            // hb = silu(w1 x) * (w3 x), silu(u) = u * 1/(1 + e^-u)
+                            if (!odd) {
+                                float a = v;
+                                a *= 1.0f / (1.0f + expf(-a));
+                                a *= other;
+                                p.out[(size_t)gm * p.ldo + (gn >> 1)] = a;
+                            }
+                        } else {
+                            const int pos = p.pos0 + gm;
+                            if (gn < p.seg2) {
+                                const bool is_q = gn < p.seg1;
+                                const int local = is_q ? gn : gn - p.seg1;
+                                const int hs = p.head_size;
+                                const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + ((local % hs) >> 1)];
+                                const float a = odd ? other : v;  // element 2j
+                                const float b = odd ? v : other;  // element 2j+1
+                                const float rv = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
+                                if (is_q)
+                                    p.out[(size_t)gm * p.ldo + gn] = rv;
+                                else
+                                    p.kc[(size_t)pos * p.kv_stride + local] = rv;
+                            } else {
+                                p.vc[(size_t)pos * p.kv_stride + (gn - p.seg2)] = v;
+                            }
+                        }
+                    }
+                } else if (gm < p.m && gn < p.n) {
+                    float* o = p.out + (size_t)gm * p.ldo + gn;
+                    if constexpr (KIND == G_RESID)
+                        *o += v;
+                    else
+                        *o = v;
+                }
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Causal attention of T queries at positions pos0 .. pos0 + T - 1 over the
+// cache rows 0 .. pos0 + T - 1 ("run.c 逐行解讀" §4 step 2e for every query),
+// on the matrix cores with v_mfma_f32_16x16x4f32.
+//
+// A block (4 waves) takes 64 consecutive queries of one head h; each wave 16
+// of them.  Key tiles of 32 rows of K and V (kv head g(h)) are staged in LDS
+// by the whole block.  Per 16 keys a wave computes the transposed score tile
+// S^T (16 keys x 16 queries) = K Q^T: lane l then holds 4 keys of query
+// l % 16, so the online softmax statistics (m, l) of a query live in the four
+// lanes l % 16 + 16c and need two lane exchanges.  The same registers are
+// the B operand of O^T (hs x 16 queries) += V^T P^T, whose result keeps the
+// query in l % 16, so the rescale by e^(m_old - m_new) needs no exchange.
+// Q (hs/4 floats per lane) and O^T (hs/4) stay in registers.  The MFMA's four
+// k positions per step are k = (hs/4) c + s for lane quarter c in the score
+// product, and key 4c + s in the value product.
+
+constexpr int kAQ = 64;       // queries per block
+constexpr int kAK = 32;       // keys per LDS tile
+constexpr int kAPad = 4;
+
+template <int HS>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) {
+    constexpr int Q4 = HS / 4;    // d per lane quarter
+    constexpr int CT = HS / 16;   // 16-wide column tiles of the output
+    constexpr int ROW = HS + kAPad;
+    __shared__ __attribute__((aligned(16))) float Ks[kAK][ROW];
+    __shared__ __attribute__((aligned(16))) float Vs[kAK][ROW];
+
+    const int h = blockIdx.y;
+    const int g = (int)(((long long)h * p.n_kv_heads) / p.n_heads);
+    const int q0 = blockIdx.x * kAQ;  // first query (token index in the chunk) of the block
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 15, lc = lane >> 4;
+    const int wq0 = q0 + wave * 16;  // first query of the wave
+    const int tq = min(wq0 + lq, p.t - 1);  // this lane's query (clamped; results past T are not stored)
+    const int qpos = p.pos0 + tq;
+    const float scale = 1.0f / sqrtf((float)HS);
+
+    // Q row quarter: Q[tq][h*HS + lc*Q4 + s], pre-scaled by 1/sqrt(hs)
+    float qv[Q4];
+    {
+        const float4* q4 = reinterpret_cast<const float4*>(p.q + (size_t)tq * p.ldq + (size_t)h * HS + lc * Q4);
+#pragma unroll
+        for (int s = 0; s < Q4 / 4; ++s) {
+            const float4 v = q4[s];
+            qv[4 * s] = v.x * scale;
+            qv[4 * s + 1] = v.y * scale;
+            qv[4 * s + 2] = v.z * scale;
+            qv[4 * s + 3] = v.w * scale;
+        }
+    }
+    v4f o[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) o[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    const int last_q = min(q0 + kAQ, p.t) - 1;  // last query of the block
+    const int n_keys = p.pos0 + last_q + 1;
+    const int wave_last_pos = p.pos0 + min(wq0 + 15, p.t - 1);
+    const float* kbase = p.kc + (size_t)g * HS;
+    const float* vbase = p.vc + (size_t)g * HS;
+
+    for (int k0 = 0; k0 < n_keys; k0 += kAK) {
+        // stage keys k0 .. k0 + 31 (rows past the last key read the last key; they are masked)
+        __syncthreads();
+        for (int e = tid; e < kAK * (HS / 4); e += 256) {
+            const int r = e / (HS / 4), c4 = e % (HS / 4);
+            const size_t row = (size_t)min(k0 + r, n_keys - 1) * p.kv_stride;
+            *reinterpret_cast<float4*>(&Ks[r][4 * c4]) = reinterpret_cast<const float4*>(kbase + row)[c4];
+            *reinterpret_cast<float4*>(&Vs[r][4 * c4]) = reinterpret_cast<const float4*>(vbase + row)[c4];
+        }
+        __syncthreads();
+        if (k0 > wave_last_pos) continue;  // every key of the tile is after every query of this wave
+
+#pragma unroll
+        for (int sub = 0; sub < kAK / 16; ++sub) {
+            // S^T(16 keys x 16 queries): A = K rows (key lq), B = Q^T (query lq)
+            v4f st = v4f{0.f, 0.f, 0.f, 0.f};
+            const float* krow = &Ks[sub * 16 + lq][lc * Q4];
+#pragma unroll
+            for (int s = 0; s < Q4; s += 4) {
+                const float4 kk = *reinterpret_cast<const float4*>(krow + s);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.x, qv[s], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.y, qv[s + 1], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.z, qv[s + 2], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.w, qv[s + 3], st, 0, 0, 0);
+            }
+            // register r: key k0 + 16 sub + 4 lc + r of query tq; causal mask
+            float sc[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kpos = k0 + sub * 16 + lc * 4 + r;
+                sc[r] = kpos <= qpos ? st[r] : -INFINITY;
+                tmax = fmaxf(tmax, sc[r]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float m_new = fmaxf(m, tmax);  // finite: key 0 is in the first tile of every query
+            const float alpha = expf(m - m_new);
+            float psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[r] = expf(sc[r] - m_new);
+                psum += sc[r];
+            }
+            psum += __shfl_xor(psum, 16);
+            psum += __shfl_xor(psum, 32);
+            l = l * alpha + psum;
+            m = m_new;
+            // O^T(hs x 16 queries) += V^T P^T: A = V^T (column 16 c + lq, key 4 lc + r), B = P^T
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                o[c] *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(Vs[sub * 16 + lc * 4 + r][c * 16 + lq], sc[r], o[c],
+                                                                0, 0, 0);
+            }
+        }
+    }
+    // O^T register r of tile c: column 16 c + 4 lc + r of query tq
+    if (wq0 + lq < p.t) {
+        const float inv = 1.0f / l;
+        float* out = p.out + (size_t)tq * p.ldo + (size_t)h * HS;
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[c * 16 + lc * 4 + r] = o[c][r] * inv;
+    }
+}
+
+}  // namespace
+
+hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s) {
+    hipLaunchKernelGGL(embed_kernel, dim3(t), dim3(256), 0, s, emb, tokens, dim, x);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(t), dim3(256), 0, s, x, g, eps, dim, out);
+    return hipGetLastError();
+}
+
+hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s) {
+    if (p.m <= 0 || p.n <= 0 || p.k < 4 || (p.k % 4)) return hipErrorInvalidValue;
+    const long long tiles = (long long)((p.m + kBM - 1) / kBM) * ((p.n + kBN - 1) / kBN);
+    if (tiles > INT_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles), block(kGemmThreads);
+    switch (kind) {
+        case G_PLAIN: hipLaunchKernelGGL(gemm_kernel<G_PLAIN>, grid, block, 0, s, p); break;
+        case G_RESID: hipLaunchKernelGGL(gemm_kernel<G_RESID>, grid, block, 0, s, p); break;
+        case G_QKV: hipLaunchKernelGGL(gemm_kernel<G_QKV>, grid, block, 0, s, p); break;
+        case G_SWIGLU: hipLaunchKernelGGL(gemm_kernel<G_SWIGLU>, grid, block, 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+bool attn_prefill_supported(int hs) {
+    switch (hs) {
+        case 16: case 32: case 48: case 64: case 80: case 96: case 128: case 256: return true;
+    }
+    return false;
+}
+
+hipError_t attn_prefill_launch(int hs, const AttnPrefillParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)((p.t + kAQ - 1) / kAQ), (unsigned)p.n_heads), block(256);
+    switch (hs) {
+        case 16: hipLaunchKernelGGL(attn_prefill_kernel<16>, grid, block, 0, s, p); break;
+        case 32: hipLaunchKernelGGL(attn_prefill_kernel<32>, grid, block, 0, s, p); break;
+        case 48: hipLaunchKernelGGL(attn_prefill_kernel<48>, grid, block, 0, s, p); break;
+        case 64: hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, block, 0, s, p); break;
+        case 80: hipLaunchKernelGGL(attn_prefill_kernel<80>, grid, block, 0, s, p); break;
+        case 96: hipLaunchKernelGGL(attn_prefill_kernel<96>, grid, block, 0, s, p); break;
+        case 128: hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, block, 0, s, p); break;
+        case 256: hipLaunchKernelGGL(attn_prefill_kernel<256>, grid, block, 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ld

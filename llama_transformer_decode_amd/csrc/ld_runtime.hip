@@ -19,6 +19,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -115,6 +116,14 @@ struct ld_model {
     float* h_coins = nullptr;
     StepState* h_poll = nullptr;   // pinned: 3 state snapshots
     hipEvent_t ev_poll[2] = {nullptr, nullptr};
+    // prompt prefill: tokens by position, pinned staging, and the per-chunk
+    // activations (grown on demand, kept until ld_destroy)
+    int32_t* ptok = nullptr;
+    int32_t* h_ptok = nullptr;
+    hipEvent_t ev_ptok = nullptr;
+    bool ptok_pending = false;
+    int pf_cap = 0;
+    float *pf_x = nullptr, *pf_xn = nullptr, *pf_q = nullptr, *pf_att = nullptr, *pf_hb = nullptr;
     GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
@@ -143,6 +152,10 @@ void release(ld_model* m) {
     if (m->exec) (void)hipGraphExecDestroy(m->exec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
     for (void* p : m->dev_allocs) (void)hipFree(p);
+    for (float* p : {m->pf_x, m->pf_xn, m->pf_q, m->pf_att, m->pf_hb})
+        if (p) (void)hipFree(p);
+    if (m->h_ptok) (void)hipHostFree(m->h_ptok);
+    if (m->ev_ptok) (void)hipEventDestroy(m->ev_ptok);
     if (m->h_tokens) (void)hipHostFree(m->h_tokens);
     if (m->h_forced) (void)hipHostFree(m->h_forced);
     if (m->h_coins) (void)hipHostFree(m->h_coins);
@@ -343,6 +356,119 @@ int run_step(ld_model* m) {
     return launch_step(m, nullptr);
 }
 
+// Tokens per prefill chunk: chunks run one after another, each attending to
+// the cache rows the earlier ones wrote.
+constexpr int kPrefillChunk = 2048;
+
+int prefill_workspace(ld_model* m, int tokens) {
+    if (tokens <= m->pf_cap) return LD_OK;
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    for (float** p : {&m->pf_x, &m->pf_xn, &m->pf_q, &m->pf_att, &m->pf_hb}) {
+        if (*p) (void)hipFree(*p);
+        *p = nullptr;
+    }
+    m->pf_cap = 0;
+    const size_t d = (size_t)m->cfg.dim * tokens, h = (size_t)m->cfg.hidden_dim * tokens;
+    hipError_t e = hipMalloc((void**)&m->pf_x, d * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&m->pf_xn, d * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&m->pf_q, d * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&m->pf_att, d * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&m->pf_hb, h * sizeof(float));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc prefill workspace");
+    m->pf_cap = tokens;
+    return LD_OK;
+}
+
+// One chunk of T prompt tokens at positions p0 .. p0 + T - 1 (their ids in
+// m->ptok[p0 ..]): every layer of the step over all T tokens at once; leaves
+// the final residual stream in pf_x.
+int prefill_chunk(ld_model* m, int p0, int T) {
+    const ld_config& c = m->cfg;
+    const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
+    const size_t cache_layer = (size_t)c.seq_len * kv;
+    hipStream_t s = m->stream;
+    HIP_TRY(embed_launch(m->emb, m->ptok + p0, T, c.dim, m->pf_x, s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_att + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_xn, s));
+        {
+            GemmParams g{};
+            g.a = m->pf_xn;
+            g.lda = c.dim;
+            g.m = T;
+            g.n = c.dim + 2 * m->kv_dim;
+            g.k = c.dim;
+            g.w0 = m->wq + (size_t)l * d * d;
+            g.w1 = m->wk + (size_t)l * kv * d;
+            g.w2 = m->wv + (size_t)l * kv * d;
+            g.seg1 = c.dim;
+            g.seg2 = c.dim + m->kv_dim;
+            g.out = m->pf_q;
+            g.ldo = c.dim;
+            g.kc = m->kc + (size_t)l * cache_layer;
+            g.vc = m->vc + (size_t)l * cache_layer;
+            g.kv_stride = m->kv_dim;
+            g.head_size = m->hs;
+            g.rope = m->rope;
+            g.pos0 = p0;
+            HIP_TRY(gemm_launch(G_QKV, g, s));
+        }
+        {
+            AttnPrefillParams a{};
+            a.q = m->pf_q;
+            a.ldq = c.dim;
+            a.kc = m->kc + (size_t)l * cache_layer;
+            a.vc = m->vc + (size_t)l * cache_layer;
+            a.kv_stride = m->kv_dim;
+            a.out = m->pf_att;
+            a.ldo = c.dim;
+            a.t = T;
+            a.pos0 = p0;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            HIP_TRY(attn_prefill_launch(m->hs, a, s));
+        }
+        {
+            GemmParams g{};
+            g.a = m->pf_att;
+            g.lda = c.dim;
+            g.m = T;
+            g.n = c.dim;
+            g.k = c.dim;
+            g.w0 = m->wo + (size_t)l * d * d;
+            g.out = m->pf_x;
+            g.ldo = c.dim;
+            HIP_TRY(gemm_launch(G_RESID, g, s));
+        }
+        HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_ffn + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_xn, s));
+        {
+            GemmParams g{};
+            g.a = m->pf_xn;
+            g.lda = c.dim;
+            g.m = T;
+            g.n = 2 * c.hidden_dim;
+            g.k = c.dim;
+            g.w0 = m->w1 + (size_t)l * h * d;
+            g.w1 = m->w3 + (size_t)l * h * d;
+            g.out = m->pf_hb;
+            g.ldo = c.hidden_dim;
+            HIP_TRY(gemm_launch(G_SWIGLU, g, s));
+        }
+        {
+            GemmParams g{};
+            g.a = m->pf_hb;
+            g.lda = c.hidden_dim;
+            g.m = T;
+            g.n = c.dim;
+            g.k = c.hidden_dim;
+            g.w0 = m->w2 + (size_t)l * d * h;
+            g.out = m->pf_x;
+            g.ldo = c.dim;
+            HIP_TRY(gemm_launch(G_RESID, g, s));
+        }
+    }
+    return LD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -419,6 +545,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_out, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[0], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[1], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_ptok, hipEventDisableTiming);
         if (e != hipSuccess) { rc = fail_hip(e, "hipEventCreate"); break; }
 
         const size_t cache = (size_t)cfg->n_layers * cfg->seq_len * kv;
@@ -431,7 +558,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             (rc = dalloc(m, &m->state, 1)) ||
             (rc = dalloc(m, &m->tokens, (size_t)cfg->seq_len)) || (rc = dalloc(m, &m->ctl, 1)) ||
             (rc = dalloc(m, &m->forced, (size_t)cfg->seq_len + 1)) ||
-            (rc = dalloc(m, &m->coins, (size_t)cfg->seq_len)))
+            (rc = dalloc(m, &m->coins, (size_t)cfg->seq_len)) || (rc = dalloc(m, &m->ptok, (size_t)cfg->seq_len)))
             break;
         e = hipHostMalloc((void**)&m->h_tokens, sizeof(int32_t) * (size_t)cfg->seq_len, hipHostMallocDefault);
         if (e == hipSuccess)
@@ -439,6 +566,8 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e == hipSuccess)
             e = hipHostMalloc((void**)&m->h_coins, sizeof(float) * (size_t)cfg->seq_len, hipHostMallocDefault);
         if (e == hipSuccess) e = hipHostMalloc((void**)&m->h_poll, sizeof(StepState) * 3, hipHostMallocDefault);
+        if (e == hipSuccess)
+            e = hipHostMalloc((void**)&m->h_ptok, sizeof(int32_t) * (size_t)cfg->seq_len, hipHostMallocDefault);
         if (e != hipSuccess) { rc = fail_hip(e, "hipHostMalloc"); break; }
 
         if ((rc = (gemv_plan(K_QKV, cfg->dim + 2 * m->kv_dim, cfg->dim, &m->pq) == hipSuccess) ? LD_OK : LD_E_UNSUPPORTED) ||
@@ -593,6 +722,57 @@ int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t 
     const int ran = m->h_poll[2].pos - pos;
     std::memcpy(h_tokens_out, m->h_tokens, sizeof(int32_t) * (size_t)ran);
     *n_out = ran;
+    return leave(m);
+}
+
+int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t pos, const float** d_logits_out) {
+    if (!m || !h_tokens || !d_logits_out) return LD_E_NULL;
+    const ld_config& c = m->cfg;
+    if (n_tokens < 1 || pos < 0 || (long long)pos + n_tokens > c.seq_len) return LD_E_RANGE;
+    for (int i = 0; i < n_tokens; ++i)
+        if (h_tokens[i] < 0 || h_tokens[i] >= c.vocab_size) return LD_E_RANGE;
+    if (!attn_prefill_supported(m->hs)) return LD_E_UNSUPPORTED;
+    int rc = enter(m);
+    if (rc) return rc;
+    if ((rc = set_control(m, kGreedy))) return rc;
+    const int chunk = n_tokens < kPrefillChunk ? n_tokens : kPrefillChunk;
+    if ((rc = prefill_workspace(m, chunk))) return rc;
+    // the staging buffer is free once the previous prefill's copy has run
+    if (m->ptok_pending) HIP_TRY(hipEventSynchronize(m->ev_ptok));
+    std::memcpy(m->h_ptok, h_tokens, sizeof(int32_t) * (size_t)n_tokens);
+    HIP_TRY(hipMemcpyAsync(m->ptok + pos, m->h_ptok, sizeof(int32_t) * (size_t)n_tokens, hipMemcpyHostToDevice,
+                           m->stream));
+    HIP_TRY(hipEventRecord(m->ev_ptok, m->stream));
+    m->ptok_pending = true;
+    int last = 0;
+    for (int c0 = 0; c0 < n_tokens; c0 += chunk) {
+        const int T = n_tokens - c0 < chunk ? n_tokens - c0 : chunk;
+        if ((rc = prefill_chunk(m, pos + c0, T))) return rc;
+        last = T - 1;
+    }
+    // classifier and next token for the last prompt token, as a decode step ends
+    HIP_TRY(set_state_launch(m->state, h_tokens[n_tokens - 1], pos + n_tokens - 1, m->stream));
+    GemvParams p = base_params(m);
+    p.x = m->pf_x + (size_t)last * c.dim;
+    p.gain = m->rms_final;
+    p.n = c.dim;
+    p.rows = c.vocab_size;
+    p.w0 = m->wcls;
+    p.out = m->logits;
+    p.best = m->best;
+    HIP_TRY(gemv_launch(m->pcls, p, m->stream));
+    NextTokenParams nt{};
+    nt.best = m->best;
+    nt.nblocks = m->pcls.grid;
+    nt.logits = m->logits;
+    nt.n = c.vocab_size;
+    nt.ctl = m->ctl;
+    nt.forced = m->forced;
+    nt.coins = m->coins;
+    nt.state = m->state;
+    nt.tokens_out = m->tokens;
+    HIP_TRY(next_token_launch(nt, m->stream));
+    *d_logits_out = m->logits;
     return leave(m);
 }
 
@@ -877,6 +1057,53 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
     a.kv_dim = n_kv_heads * head_size;
     a.nsplit = nsplit;
     HIP_TRY(attn_launch(head_size, a, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_gemm(const float* d_a, const float* d_w, int32_t m, int32_t n, int32_t k, float* d_out, void* hip_stream) {
+    if (!d_a || !d_w || !d_out) return LD_E_NULL;
+    if (m <= 0 || n <= 0 || k <= 0) return LD_E_RANGE;
+    if (k % 4) return LD_E_CONFIG;
+    if (!aligned16(d_a) || !aligned16(d_w)) return LD_E_ALIGN;
+    GemmParams g{};
+    g.a = d_a;
+    g.lda = k;
+    g.m = m;
+    g.n = n;
+    g.k = k;
+    g.w0 = d_w;
+    g.out = d_out;
+    g.ldo = n;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    HIP_TRY(gemm_launch(G_PLAIN, g, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_attention_prefill(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_size, int32_t pos, int32_t n_tokens, float* d_out,
+                            void* hip_stream) {
+    if (!d_q || !d_kc || !d_vc || !d_out) return LD_E_NULL;
+    if (n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || head_size <= 0 || head_size % 2)
+        return LD_E_CONFIG;
+    if (!attn_prefill_supported(head_size)) return LD_E_UNSUPPORTED;
+    if (pos < 0 || n_tokens < 1) return LD_E_RANGE;
+    if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc)) return LD_E_ALIGN;
+    AttnPrefillParams a{};
+    a.q = d_q;
+    a.ldq = n_heads * head_size;
+    a.kc = d_kc;
+    a.vc = d_vc;
+    a.kv_stride = n_kv_heads * head_size;
+    a.out = d_out;
+    a.ldo = n_heads * head_size;
+    a.t = n_tokens;
+    a.pos0 = pos;
+    a.n_heads = n_heads;
+    a.n_kv_heads = n_kv_heads;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    HIP_TRY(attn_prefill_launch(head_size, a, s));
     HIP_TRY(hipStreamSynchronize(s));
     return LD_OK;
 }

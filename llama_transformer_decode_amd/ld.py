@@ -27,9 +27,9 @@ LD_OPT_NO_GRAPH = 1
 # Every symbol include/ld.h declares.
 EXPORTS = (
     "ld_weights_size", "ld_create", "ld_reset", "ld_forward", "ld_argmax_last", "ld_generate_greedy",
-    "ld_generate", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail", "ld_profile_steps",
-    "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope", "ld_op_attention",
-    "ld_op_argmax", "ld_op_sample",
+    "ld_generate", "ld_prefill", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
+    "ld_profile_steps", "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope",
+    "ld_op_attention", "ld_op_gemm", "ld_op_attention_prefill", "ld_op_argmax", "ld_op_sample",
 )
 
 
@@ -89,6 +89,7 @@ def library():
             "ld_argmax_last": ([_P, ctypes.POINTER(_I)], ctypes.c_int),
             "ld_generate_greedy": ([_P, _I, _I, _I, _P], ctypes.c_int),
             "ld_generate": ([_P, _P, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I)], ctypes.c_int),
+            "ld_prefill": ([_P, _P, _I, _I, ctypes.POINTER(_P)], ctypes.c_int),
             "ld_kv_cache": ([_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t)],
                             ctypes.c_int),
             "ld_destroy": ([_P], None),
@@ -100,6 +101,8 @@ def library():
             "ld_op_swiglu": ([_P, _P, _F, _P, _P, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_qkv_rope": ([_P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P], ctypes.c_int),
             "ld_op_attention": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], ctypes.c_int),
+            "ld_op_gemm": ([_P, _P, _I, _I, _I, _P, _P], ctypes.c_int),
+            "ld_op_attention_prefill": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_argmax": ([_P, _I, ctypes.POINTER(_I), _P], ctypes.c_int),
             "ld_op_sample": ([_P, _I, _F, _F, _F, ctypes.POINTER(_I), _P], ctypes.c_int),
         }
@@ -186,6 +189,13 @@ def ld_generate(h: int, prompt, pos: int, n_steps: int, temperature: float = 0.0
     return out[:n_out.value]
 
 
+def ld_prefill(h: int, tokens, pos: int) -> int:
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = _P()
+    _check(library().ld_prefill(h, t.ctypes.data if t.size else None, t.size, pos, ctypes.byref(out)), "ld_prefill")
+    return out.value
+
+
 def ld_kv_cache(h: int):
     k, v, n = _P(), _P(), ctypes.c_size_t(0)
     _check(library().ld_kv_cache(h, ctypes.byref(k), ctypes.byref(v), ctypes.byref(n)), "ld_kv_cache")
@@ -241,3 +251,12 @@ def ld_op_sample(d_logits, n, temperature, topp, coin, stream=0) -> int:
     _check(library().ld_op_sample(d_logits, n, temperature, topp, coin, ctypes.byref(out), stream or None),
            "ld_op_sample")
     return out.value
+
+
+def ld_op_gemm(d_a, d_w, m, n, k, d_out, stream=0):
+    _check(library().ld_op_gemm(d_a, d_w, m, n, k, d_out, stream or None), "ld_op_gemm")
+
+
+def ld_op_attention_prefill(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, n_tokens, d_out, stream=0):
+    _check(library().ld_op_attention_prefill(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, n_tokens, d_out,
+                                             stream or None), "ld_op_attention_prefill")

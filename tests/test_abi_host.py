@@ -129,3 +129,19 @@ def test_generate_and_sample_argument_checks_come_first():
         assert lib.ld_op_sample(fake, 8, t, 0.0, 0.5, ctypes.byref(tok), None) == ld.LD_E_RANGE
     assert lib.ld_op_sample(fake, 8, 1.0, float("nan"), 0.5, ctypes.byref(tok), None) == ld.LD_E_RANGE
     assert lib.ld_op_sample(fake, 40000, 1.0, 0.9, 0.5, ctypes.byref(tok), None) == ld.LD_E_UNSUPPORTED
+
+
+def test_prefill_and_gemm_argument_checks_come_first():
+    lib = pkg.library()
+    fake = 0x10000  # never dereferenced: every case fails its argument check first
+    toks = (ctypes.c_int32 * 2)(1, 2)
+    out = ctypes.c_void_p()
+    assert lib.ld_prefill(None, toks, 2, 0, ctypes.byref(out)) == ld.LD_E_NULL
+    assert lib.ld_op_gemm(None, fake, 4, 4, 4, fake, None) == ld.LD_E_NULL
+    assert lib.ld_op_gemm(fake, fake, 0, 4, 4, fake, None) == ld.LD_E_RANGE
+    assert lib.ld_op_gemm(fake, fake, 4, 4, 6, fake, None) == ld.LD_E_CONFIG
+    assert lib.ld_op_gemm(fake + 4, fake, 4, 4, 4, fake, None) == ld.LD_E_ALIGN
+    assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 4, 24, 0, 2, fake, None) == ld.LD_E_UNSUPPORTED
+    assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 8, 16, 0, 2, fake, None) == ld.LD_E_CONFIG
+    assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 4, 16, 0, 0, fake, None) == ld.LD_E_RANGE
+    assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 4, 16, -1, 2, fake, None) == ld.LD_E_RANGE
