@@ -28,6 +28,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+
+
+def prefill_flops(c, n: int) -> int:
+    """Algorithmic flops of a prefill of n tokens from position 0: 2 per weight
+    of every layer projection per token, 4 per head dimension per (query, key)
+    pair of the causal attention (scores and the weighted sum), and the
+    classifier for the last token."""
+    kv = c.dim * c.n_kv_heads // c.n_heads
+    proj = 2 * c.dim * c.dim + 2 * kv * c.dim + 3 * c.dim * c.hidden_dim
+    pairs = n * (n + 1) // 2
+    return 2 * c.n_layers * proj * n + 4 * c.n_layers * c.dim * pairs + 2 * c.vocab_size * c.dim
 
 
 def bytes_per_token(c, pos: int) -> int:
@@ -113,6 +125,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle decode steps timed for the CPU baseline")
+    ap.add_argument("--prefill-tokens", type=int, default=None,
+                    help="prompt length of the timed batched prefill (default: the workload's prompt, else 2048; "
+                         "0: skip)")
     ap.add_argument("--sampled-steps", type=int, default=256,
                     help="steps of the temperature / top-p generation loop timed beside greedy decode (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -259,6 +274,31 @@ def main() -> int:
             v["us_over_greedy"] = round(1e3 * (v["ms_per_step"] - g), 2)
         print(f"# generation loop: {json.dumps(sampled)}", file=sys.stderr, flush=True)
 
+    # ---- batched prompt prefill on the matrix cores (overwrites the cache) ----
+    prefill = None
+    n_pf = args.prefill_tokens if args.prefill_tokens is not None else (start or min(S, 2048))
+    if n_pf > 0:
+        n_pf = min(n_pf, S)
+        ptoks = synth.prefill_tokens(cfg, n_pf).copy()
+        ptoks[0] = 1
+        times = []
+        for _ in range(3):
+            model.reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            model.prefill_async(ptoks, 0)
+            model.argmax_last()  # synchronises the stream
+            times.append(time.perf_counter() - t0)
+        dt = min(times)
+        fl = prefill_flops(cfg, n_pf)
+        tf = fl / dt / 1e12
+        prefill = {"tokens": n_pf, "ms": round(1e3 * dt, 2), "tok_s": round(n_pf / dt, 1),
+                   "flops": fl, "TFLOPs": round(tf, 1),
+                   "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP32_MFMA_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)},
+                   "vs_token_by_token": round((n_pf / dt) / tok_s, 1)}
+        print(f"# prefill: {json.dumps(prefill)}", file=sys.stderr, flush=True)
+
     model.close()
     del weights
     torch.cuda.empty_cache()
@@ -309,6 +349,7 @@ def main() -> int:
         "roofline": roofline,
         "kernels": kernels,
         "generation_loop": sampled,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -126,33 +126,46 @@ constexpr int kArgmaxThreads = 256;
 // ---------------------------------------------------------------------------
 // The next token ("run.c 逐行解讀" §6 sample() and §7 generate()).
 //
-// One block of NT threads.  A forced prompt token is taken as is.
-// Otherwise the per-block bests of the logits give the greedy choice and the
-// maximum logit; at a positive temperature the threads then hold the softmax
-// numerators e_i = exp((l_i - max) / T) in registers, and the draw is the
-// cumulative walk of the "run.c" sample(): the first token, in walk order,
-// whose cumulative mass exceeds coin * (mass of the candidates).  Masses are
-// summed in double, every block sum in one fixed order, so every thread holds
-// the same bits and takes the same branch.  No sort and no scan: each search
-// below is a bisection whose test is one block sum.
-//  * Without top-p the walk runs in index order: the token is the first i
-//    whose prefix mass exceeds coin * S (bisection over i).
-//  * With top-p it runs in descending probability, ties to the lower index.
-//    Bisections over fp32 bit patterns (the integer order of positive floats
-//    is their numeric order) find
+// One block of NT threads.  A forced prompt token is taken as is.  Otherwise
+// the per-block bests of the logits give the greedy choice and the maximum
+// logit; at a positive temperature thread t then holds the softmax numerators
+// e_i = exp((l_i - max) / T) of tokens i = t + k NT (k < E) in registers, and
+// the draw is the cumulative walk of the "run.c" sample(): the first token,
+// in walk order, whose cumulative mass exceeds coin * (mass of the
+// candidates).  A thread sums its own numerators in fp32 (at most E terms),
+// the block sums those partials in double, every sum in one fixed order, so
+// every thread holds the same bits and takes the same branch.
+// One CU does all of this, so the cost is counted in passes over the E
+// registers of every thread (one block sum each); the searches below keep
+// the passes few.
+//  * Without top-p the walk runs in index order.  Token i = t + k NT lies in
+//    "row" k: a bisection over rows on the threads' running sums finds the
+//    row whose prefix mass brackets coin * S (log2 E passes of one select and
+//    one block sum), one scan over the row's threads the token.
+//  * With top-p the walk runs in descending probability, ties to the lower
+//    index.  Searches over fp32 bit patterns (the integer order of positive
+//    floats is their numeric order) find
 //    (a) v_k, the value of the last candidate: the largest v whose mass
 //        G(v) = sum of e_i >= v reaches topp * S.  The candidates are every
 //        e_i > v_k and the first j tokens (index order) equal to v_k, j the
 //        fewest that bring the candidate mass M to topp * S;
 //    (b) u, the value of the drawn token: the largest candidate value with
 //        G(u) > coin * M.  Among the tokens equal to u the draw takes the
-//        (q+1)-th in index order, q = floor((coin * M - G(> u)) / u), found by
-//        (c) a bisection over i on the count of those tokens up to i.
+//        (q+1)-th in index order, q = floor((coin * M - G(> u)) / u).
+//    Each search bisects a bracket [lo, hi) of bit patterns; once at most
+//    kCap values lie inside it, they are compacted into LDS and one wave
+//    finishes the bisection over that list alone, with no block barrier.
+
+constexpr int kCap = 512;
 
 template <int NW>
 struct SampleShared {
     double red[2][NW];
     int ired[2][NW];
+    int imin[2][NW];
+    float cv[kCap];
+    double bd[2];
+    int bi[4];
 };
 
 template <int CTRL, int ROW_MASK = 0xf>
@@ -160,6 +173,11 @@ __device__ __forceinline__ double dpp_d(double v) {
     const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xf, false);
     const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xf, false);
     return __hiloint2double(hi, lo);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
 }
 
 // the wave's total, the same bits in every lane (the wave_sum pattern in double)
@@ -175,153 +193,314 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return __hiloint2double(hi, lo);
 }
 
-// Block reductions alternate between two LDS slots, so one barrier per call
-// suffices: a slot is rewritten two calls later, after every thread has
-// passed the barrier of the call in between and so has read it.
-template <int NW>
-__device__ double block_sum_d(double v, SampleShared<NW>& sh, int& ph) {
-    v = wave_sum_d(v);
-    if ((threadIdx.x & 63) == 0) sh.red[ph][threadIdx.x >> 6] = v;
-    __syncthreads();
-    double t = 0.0;
+__device__ __forceinline__ int wave_sum_i(int v) {
+    v += dpp_i<kQuadSwap1>(v);
+    v += dpp_i<kQuadSwap2>(v);
+    v += dpp_i<kRowHalfMirror>(v);
+    v += dpp_i<kRowMirror>(v);
+    v += dpp_i<kRowBcast15, 0xa>(v);
+    v += dpp_i<kRowBcast31, 0xc>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) t += sh.red[ph][w];
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Block sums of a double and an int in one barrier.  Reductions alternate
+// between two LDS slots: a slot is rewritten two calls later, after every
+// thread has passed the barrier of the call in between and so has read it.
+template <int NW>
+__device__ double block_sum_dc(double a, int& c, SampleShared<NW>& sh, int& ph) {
+    a = wave_sum_d(a);
+    c = wave_sum_i(c);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sh.red[ph][w] = a;
+        sh.ired[ph][w] = c;
+    }
+    __syncthreads();
+    double ta = 0.0;
+    int tc = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        ta += sh.red[ph][i];
+        tc += sh.ired[ph][i];
+    }
+    ph ^= 1;
+    c = tc;
+    return ta;
+}
+
+// the same, with c already the wave's total (the same in every lane)
+template <int NW>
+__device__ double block_sum_dc_wave(double a, int& c, SampleShared<NW>& sh, int& ph) {
+    a = wave_sum_d(a);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sh.red[ph][w] = a;
+        sh.ired[ph][w] = c;
+    }
+    __syncthreads();
+    double ta = 0.0;
+    int tc = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        ta += sh.red[ph][i];
+        tc += sh.ired[ph][i];
+    }
+    ph ^= 1;
+    c = tc;
+    return ta;
+}
+
+template <int NW>
+__device__ int block_min_i(int v, SampleShared<NW>& sh, int& ph) {
+    v = wave_min_i(v);
+    if ((threadIdx.x & 63) == 0) sh.imin[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    int t = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t = min(t, sh.imin[ph][i]);
     ph ^= 1;
     return t;
 }
 
-template <int NW>
-__device__ int block_sum_i(int v, SampleShared<NW>& sh, int& ph) {
+// exclusive prefix of v over the threads in thread order; *total = the block sum
+template <int NW, class T>
+__device__ T block_excl_scan(T v, T* total, T (*slot)[NW], int& ph) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    T inc = v;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) sh.ired[ph][threadIdx.x >> 6] = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const T o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    T ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = T(0);
+    if (lane == 63) slot[ph][wave] = inc;
     __syncthreads();
-    int t = 0;
+    T before = T(0), tot = T(0);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) t += sh.ired[ph][w];
+    for (int w = 0; w < NW; ++w) {
+        const T x = slot[ph][w];
+        if (w < wave) before += x;
+        tot += x;
+    }
     ph ^= 1;
-    return t;
+    *total = tot;
+    return before + ex;
+}
+
+// A bracket [lo, hi) of fp32 bit patterns for a search "largest v whose mass
+// G(v) = sum of e_i >= v passes the test": the test holds at lo and fails at
+// hi.  g_hi = G(hi); c_lo, c_hi = the numbers of positive e_i >= lo, >= hi.
+struct Bracket {
+    uint32_t lo, hi;
+    double g_hi;
+    int c_lo, c_hi;
+};
+
+// Bisect b down to hi = lo + 1; STRICT tests G(v) > thr, else G(v) >= thr.
+template <int NT, int E, bool STRICT>
+__device__ void value_search(const float (&e)[E], double thr, Bracket& b, SampleShared<NT / 64>& sh, int& ph) {
+    // over the registers while more than kCap values lie in the bracket
+    while (b.hi - b.lo > 1 && b.c_lo - b.c_hi > kCap) {
+        const uint32_t mid = b.lo + (b.hi - b.lo) / 2;
+        const float v = __uint_as_float(mid);
+        float af = 0.f;
+        int c = 0;  // counted per wave from the compare masks (scalar unit)
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const bool in = e[k] >= v;
+            af += in ? e[k] : 0.f;
+            c += __popcll(__ballot(in));
+        }
+        const double a = block_sum_dc_wave((double)af, c, sh, ph);
+        if (STRICT ? a > thr : a >= thr) {
+            b.lo = mid;
+            b.c_lo = c;
+        } else {
+            b.hi = mid;
+            b.g_hi = a;
+            b.c_hi = c;
+        }
+    }
+    if (b.hi - b.lo <= 1) return;
+    // compact the positive values in [lo, hi) into LDS; wave 0 finishes alone
+    const float flo = __uint_as_float(b.lo), fhi = __uint_as_float(b.hi);
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < E; ++k) mine += (e[k] >= flo) & (e[k] < fhi) & (e[k] > 0.f);
+    int m;
+    int off = block_excl_scan<NT / 64, int>(mine, &m, sh.ired, ph);
+    m = min(m, kCap);  // m = c_lo - c_hi <= kCap; the clamp only guards the LDS list
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+        if ((e[k] >= flo) & (e[k] < fhi) & (e[k] > 0.f)) {
+            if (off < kCap) sh.cv[off] = e[k];
+            ++off;
+        }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const double g0 = b.g_hi;  // mass and count of the values >= hi at compaction
+        const int c0 = b.c_hi;
+        constexpr int L = kCap / 64;
+        float x[L];  // the list, 0 past its end (0 is below every probe)
+#pragma unroll
+        for (int i = 0; i < L; ++i) x[i] = lane + 64 * i < m ? sh.cv[lane + 64 * i] : 0.f;
+        while (b.hi - b.lo > 1) {
+            const uint32_t mid = b.lo + (b.hi - b.lo) / 2;
+            const float v = __uint_as_float(mid);
+            float af = 0.f;
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const bool in = x[i] >= v;
+                af += in ? x[i] : 0.f;
+                c += in;
+            }
+            const double a = wave_sum_d((double)af) + g0;
+            c = wave_sum_i(c) + c0;
+            if (STRICT ? a > thr : a >= thr) {
+                b.lo = mid;
+                b.c_lo = c;
+            } else {
+                b.hi = mid;
+                b.g_hi = a;
+                b.c_hi = c;
+            }
+        }
+        if (lane == 0) {
+            sh.bd[0] = b.g_hi;
+            sh.bi[0] = (int)b.lo;
+            sh.bi[1] = b.c_lo;
+            sh.bi[2] = b.c_hi;
+        }
+    }
+    __syncthreads();
+    b.g_hi = sh.bd[0];
+    b.lo = (uint32_t)sh.bi[0];
+    b.hi = b.lo + 1;
+    b.c_lo = sh.bi[1];
+    b.c_hi = sh.bi[2];
+    __syncthreads();  // sh.bd / sh.bi are read before any later writer
 }
 
 template <int NT, int E>
 __device__ int sample_draw(const float* __restrict__ logits, int n, float lmax, float temperature, float topp,
                            float coin, SampleShared<NT / 64>& sh) {
-    // thread t holds tokens t + k * NT (coalesced loads)
     const int t = threadIdx.x;
-    const double inv_t = 1.0 / (double)temperature;
+    // e = 2^((l - max) * log2(e) / T); w is finite (checked by the caller)
+    const float w = (float)(1.4426950408889634 / (double)temperature);
     float e[E];  // first the logits, then in place their numerators
-    // unconditional loads from a clamped index (no branch per load); tokens
-    // past the end are masked in the next loop
 #pragma unroll
-    for (int k = 0; k < E; ++k) e[k] = logits[(unsigned)min(t + k * NT, n - 1)];
+    for (int k = 0; k < E; ++k) e[k] = logits[(unsigned)min(t + k * NT, n - 1)];  // clamped; masked below
     __builtin_amdgcn_sched_barrier(0);
-    double s = 0.0;
+    float sf = 0.f;
+    int pos = 0;
 #pragma unroll
     for (int k = 0; k < E; ++k) {
-        const float x = expf((float)(((double)e[k] - (double)lmax) * inv_t));
+        const float x = exp2f((e[k] - lmax) * w);
         e[k] = (x == x && k * NT < n - t) ? x : 0.f;  // a NaN logit carries no mass
-        s += (double)e[k];
-        __builtin_amdgcn_sched_barrier(0);  // one exp at a time: E live floats, not E in flight
+        sf += e[k];
+        pos += e[k] > 0.f;
     }
     int ph = 0;
-    const double S = block_sum_d(s, sh, ph);
     const double dcoin = (double)coin;
 
-    // masses and counts, the same bits in every thread; each is monotone in
-    // its argument because every partial sum adds non-negative terms in a
-    // fixed order
-    auto mass_at_least = [&](float v) {  // sum of e_i >= v
-        double a = 0.0;
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            a += (double)(e[k] >= v ? e[k] : 0.f);  // converted after the select: no E doubles held
-            if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-        }
-        return block_sum_d(a, sh, ph);
-    };
-    // (index tests as k * NT <= idx - t: constants against one register, so
-    // no per-element index is kept live)
-    auto mass_upto = [&](int idx) {  // sum of e_i, i <= idx
-        const int rel = idx - t;
-        double a = 0.0;
-#pragma unroll
-        for (int k = 0; k < E; ++k) {
-            a += (double)(k * NT <= rel ? e[k] : 0.f);
-            if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-        }
-        return block_sum_d(a, sh, ph);
-    };
-    auto count_equal_upto = [&](float v, int idx) {  // number of e_i == v, i <= idx
-        const int rel = idx - t;
-        int c = 0;
-#pragma unroll
-        for (int k = 0; k < E; ++k) c += (e[k] == v) & (k * NT <= rel);
-        return block_sum_i(c, sh, ph);
-    };
-
     if (!(topp > 0.f && topp < 1.f)) {
-        // index order: the first i with mass_upto(i) > coin * S.  mass_upto(-1)
-        // = 0 <= r and mass_upto(n - 1) = S > r (coin < 1)
+        // index order.  Row k holds tokens k NT .. k NT + NT - 1, one per thread;
+        // M(k) = mass of rows < k, from each thread's running sums pre[k].
+        // M(0) = 0 <= r < M(E) = S: bisect for the last row k with M(k) <= r,
+        // then scan that row over the threads.
+        float pre[E + 1];
+        pre[0] = 0.f;
+#pragma unroll
+        for (int k = 0; k < E; ++k) pre[k + 1] = pre[k] + e[k];  // pre[E] = sf
+        int c = 0;
+        const double S = block_sum_dc((double)sf, c, sh, ph);
         const double r = dcoin * S;
-        int lo = -1, hi = n - 1;
-        while (hi - lo > 1) {
-            const int mid = lo + (hi - lo) / 2;
-            if (mass_upto(mid) > r)
-                hi = mid;
-            else
-                lo = mid;
+        int klo = 0, khi = E;
+        double m_lo = 0.0;
+        while (khi - klo > 1) {
+            const int mid = (klo + khi) >> 1;
+            float x = 0.f;
+#pragma unroll
+            for (int k = 1; k < E; ++k) x = k == mid ? pre[k] : x;  // mid is the same in every lane
+            const double a = block_sum_dc((double)x, c, sh, ph);
+            if (a <= r) {
+                klo = mid;
+                m_lo = a;
+            } else {
+                khi = mid;
+            }
         }
-        return hi;
+        float x = 0.f;
+#pragma unroll
+        for (int k = 0; k < E; ++k) x = k == klo ? e[k] : x;
+        double row;
+        const double ex = block_excl_scan<NT / 64, double>((double)x, &row, sh.red, ph);
+        const int i = klo * NT + t;
+        int cand = (x > 0.f && m_lo + (ex + (double)x) > r) ? i : INT_MAX;
+        cand = block_min_i(cand, sh, ph);
+        if (cand == INT_MAX) {
+            // rounding left the row's end at or below r: its last token with mass
+            cand = block_min_i(x > 0.f ? -i : INT_MAX, sh, ph);
+            cand = cand == INT_MAX ? n - 1 : -cand;
+        }
+        return cand;
     }
 
+    const double S = block_sum_dc((double)sf, pos, sh, ph);
     constexpr uint32_t kAboveOne = 0x3f800001u;  // the float just above 1 (the largest e_i is exp(0) = 1)
     const double P = (double)topp * S;
-    // (a) G(bits lo) >= P > G(bits hi); G(0) = S > P, G(above 1) = 0
-    uint32_t lo = 0, hi = kAboveOne;
-    double g_hi = 0.0;
-    while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        const double g = mass_at_least(__uint_as_float(mid));
-        if (g >= P) {
-            lo = mid;
-        } else {
-            hi = mid;
-            g_hi = g;
-        }
-    }
-    const float vk = __uint_as_float(lo);  // > 0: G(smallest positive) = S > P
-    const double above_vk = g_hi;          // mass of the e_i > v_k
-    const int n_vk = count_equal_upto(vk, n - 1);
+    int minbits = INT_MAX;  // the smallest positive numerator
+#pragma unroll
+    for (int k = 0; k < E; ++k)
+        if (e[k] > 0.f) minbits = min(minbits, __float_as_int(e[k]));
+    minbits = block_min_i(minbits, sh, ph);
+    // (a) the test G(v) >= P holds at the smallest positive numerator (G = S > P)
+    Bracket a{(uint32_t)minbits, kAboveOne, 0.0, pos, 0};
+    value_search<NT, E, false>(e, P, a, sh, ph);
+    const float vk = __uint_as_float(a.lo);
+    const double above_vk = a.g_hi;  // mass of the e_i > v_k
+    const int n_vk = a.c_lo - a.c_hi;
     int j = (int)ceil((P - above_vk) / (double)vk);
     j = max(1, min(j, n_vk));
     const double M = above_vk + (double)j * (double)vk;
     const double r = dcoin * M;
 
-    // (b) the largest candidate value u with G(u) > r; at v_k the candidate
-    // mass is M > r
-    uint32_t lo2 = lo, hi2 = kAboveOne;
-    double g_hi2 = 0.0;
-    while (hi2 - lo2 > 1) {
-        const uint32_t mid = lo2 + (hi2 - lo2) / 2;
-        const double g = mass_at_least(__uint_as_float(mid));
-        if (g > r) {
-            lo2 = mid;
-        } else {
-            hi2 = mid;
-            g_hi2 = g;
-        }
-    }
-    const float u = __uint_as_float(lo2);
-    const int n_u = lo2 == lo ? j : count_equal_upto(u, n - 1);
-    int q = (int)floor((r - g_hi2) / (double)u);
+    // (b) the test G(u) > r holds at v_k, where the candidate mass is M > r
+    Bracket bb{a.lo, kAboveOne, 0.0, a.c_lo, 0};
+    value_search<NT, E, true>(e, r, bb, sh, ph);
+    const float u = __uint_as_float(bb.lo);
+    const int n_u = bb.lo == a.lo ? j : bb.c_lo - bb.c_hi;
+    int q = (int)floor((r - bb.g_hi) / (double)u);
     q = max(0, min(q, n_u - 1));
 
-    // (c) the (q+1)-th token equal to u in index order: the first i with
-    // count_equal_upto(u, i) >= q + 1
+    // the (q+1)-th token equal to u in index order
+    if (q == 0) {
+        int cand = INT_MAX;
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if (e[k] == u) cand = min(cand, t + k * NT);
+        cand = block_min_i(cand, sh, ph);
+        return cand == INT_MAX ? n - 1 : cand;
+    }
+    // first i with (number of tokens equal to u at indices <= i) >= q + 1
     int ilo = -1, ihi = n - 1;
     while (ihi - ilo > 1) {
         const int mid = ilo + (ihi - ilo) / 2;
-        if (count_equal_upto(u, mid) >= q + 1)
+        const int rel = mid - t;
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) c += (e[k] == u) & (k * NT <= rel);
+        (void)block_sum_dc(0.0, c, sh, ph);
+        if (c >= q + 1)
             ihi = mid;
         else
             ilo = mid;
@@ -352,7 +531,9 @@ __global__ __launch_bounds__(NT) void next_token_kernel(NextTokenParams p) {
         block_best<NT>(v, i);
         next = i == INT_MAX ? 0 : i;  // every value NaN: token 0
         // a non-finite maximum leaves no distribution to draw from: greedy
-        if (c.temperature > 0.f && isfinite(v) && p.n <= E * NT)
+        // (1/T must be finite in fp32: a temperature below ~1e-38 is taken as 0)
+        if (c.temperature > 0.f && isfinite(v) && isfinite((float)(1.4426950408889634 / (double)c.temperature)) &&
+            p.n <= E * NT)
             next = sample_draw<NT, E>(p.logits, p.n, v, c.temperature, c.topp, p.coins[pos], sh);
     }
     __syncthreads();  // every thread has read the state

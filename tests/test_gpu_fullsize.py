@@ -8,6 +8,11 @@ The oracle needs seconds per step at these sizes, so the checks sample:
     the 70B-layer model) on a seeded cache prefix installed in both the GPU
     cache and the oracle's: the step's logits and the cache row it appends.
 Same bar as everywhere: max |d logit| <= 1e-4 * max |logit|.
+
+Prompt prefill is checked at these sizes too: three tokens at once after an
+installed prefix against the oracle, and a long prompt (512 / 1024 tokens)
+against the same prompt decoded one token at a time on the GPU, whose steps
+the checks above tie to the oracle.
 """
 import numpy as np
 import pytest
@@ -93,3 +98,49 @@ def test_graph_replay_matches_direct_launches(big):
     with pkg.Model(cfg, w, graph=True) as g, pkg.Model(cfg, w, graph=False) as e:
         assert np.array_equal(g.generate(1, 0, 3), e.generate(1, 0, 3))
         assert np.array_equal(host(g.forward(7, 3)), host(e.forward(7, 3)))
+
+
+def test_prefill_on_an_installed_cache_against_the_oracle(big):
+    # three prompt tokens at once after a seeded prefix: logits of the last one and the rows written
+    cfg, blob, w = big
+    import torch
+    p0 = {"llama7b": 1000, "llama70b_8l": 3584}[cfg.name]
+    cache = _prefix(cfg, p0, 500)
+    toks = synth.prefill_tokens(cfg, p0 + 3)[p0:]
+    with pkg.Model(cfg, w) as m:
+        m.write_kv_cache(torch.from_numpy(cache.k).cuda(), torch.from_numpy(cache.v).cuda())
+        got = host(m.prefill(toks, p0))
+        k, v = (host(t) for t in m.read_kv_cache())
+    ref = None
+    for i, t in enumerate(toks):
+        ref = oracle.forward(cfg, blob, cache, int(t), p0 + i)
+    ok, err, tol = logits_close(got, ref)
+    print(f"[{cfg.name}] prefill of 3 tokens at {p0}: max |d logit| {err:.3g} (tolerance {tol:.3g})", flush=True)
+    assert ok
+    for g, r in ((k, cache.k), (v, cache.v)):
+        assert np.array_equal(g[:, :p0], r[:, :p0])
+        scale = np.max(np.abs(r[:, p0:p0 + 3]))
+        assert np.max(np.abs(g[:, p0:p0 + 3] - r[:, p0:p0 + 3])) <= 1e-4 * scale
+        assert np.all(g[:, p0 + 3:] == 0)
+
+
+def test_long_prefill_equals_token_by_token_decode(big):
+    # the same prompt through ld_prefill and through ld_forward one token at a time, on the GPU
+    cfg, blob, w = big
+    n = 1024 if cfg.name == "llama70b_8l" else 512
+    toks = synth.prefill_tokens(cfg, n).copy()
+    toks[0] = 1
+    with pkg.Model(cfg, w) as a:
+        got = host(a.prefill(toks, 0))
+        ka, va = (host(t)[:, :n] for t in a.read_kv_cache())
+    with pkg.Model(cfg, w) as b:
+        for p in range(n - 1):
+            b.forward_async(int(toks[p]), p)
+        ref = host(b.forward(int(toks[n - 1]), n - 1))
+        kb, vb = (host(t)[:, :n] for t in b.read_kv_cache())
+    ok, err, tol = logits_close(got, ref.astype(np.float64))
+    print(f"[{cfg.name}] prefill of {n} tokens vs {n} decode steps: max |d logit| {err:.3g} (tolerance {tol:.3g})",
+          flush=True)
+    assert ok
+    for g, r in ((ka, kb), (va, vb)):
+        assert np.max(np.abs(g - r)) <= 1e-4 * np.max(np.abs(r))
