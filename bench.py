@@ -128,6 +128,8 @@ def main() -> int:
     ap.add_argument("--prefill-tokens", type=int, default=None,
                     help="prompt length of the timed batched prefill (default: the workload's prompt, else 2048; "
                          "0: skip)")
+    ap.add_argument("--batch-sizes", default="1,4,16,64",
+                    help="comma-separated batch sizes of the timed batch-decode leg ('' to skip)")
     ap.add_argument("--sampled-steps", type=int, default=256,
                     help="steps of the temperature / top-p generation loop timed beside greedy decode (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -300,6 +302,29 @@ def main() -> int:
         print(f"# prefill: {json.dumps(prefill)}", file=sys.stderr, flush=True)
 
     model.close()
+
+    # ---- batch decode: several sequences per step, each with its own cache ----
+    batch = None
+    sizes = [int(x) for x in args.batch_sizes.split(",") if x.strip()]
+    if sizes:
+        n_b = 32
+        bpos = min(start, S - n_b - 4)
+        batch = {"steps": n_b, "positions": [bpos, bpos + n_b - 1], "sizes": {}}
+        with pkg.Model(cfg, weights, max_batch=max(sizes)) as bm:
+            for B in sizes:
+                starts = synth.prefill_tokens(cfg, B)
+                bm.generate_batch(starts, [bpos] * B, 4)  # captures this size's graph
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                bm.generate_batch(starts, [bpos] * B, n_b)
+                dt = time.perf_counter() - t0
+                kv = cfg.dim * cfg.n_kv_heads // cfg.n_heads
+                step_bytes = sum(bytes_per_token(cfg, p) + (B - 1) * 8 * cfg.n_layers * (p + 1) * kv
+                                 for p in range(bpos, bpos + n_b))
+                batch["sizes"][str(B)] = {"tok_s": round(B * n_b / dt, 1), "ms_per_step": round(1e3 * dt / n_b, 3),
+                                          "GBps": round(step_bytes / dt / 1e9, 1)}
+        print(f"# batch decode: {json.dumps(batch)}", file=sys.stderr, flush=True)
+
     del weights
     torch.cuda.empty_cache()
 
@@ -350,6 +375,7 @@ def main() -> int:
         "kernels": kernels,
         "generation_loop": sampled,
         "prefill": prefill,
+        "batch_decode": batch,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -52,12 +52,16 @@ typedef struct ld_config {
  * (1e-5 on the "run.c" page).  rope_theta is the RoPE base (10000).
  * shared_classifier = 1 makes the classifier the embedding table ("run.c"
  * transformer(); "run.c 逐行解讀" §2 wcls may share the embedding), 0 reads a
- * separate wcls from the end of the blob.  flags: LD_OPT_* bits. */
+ * separate wcls from the end of the blob.  flags: LD_OPT_* bits.
+ * max_batch: the number of sequences with a KV cache of their own (0 or 1:
+ * one), for ld_forward_batch / ld_generate_greedy_batch; the single-sequence
+ * calls use sequence 0. */
 typedef struct ld_options {
     float norm_eps;
     float rope_theta;
     int32_t shared_classifier;
     int32_t flags;
+    int32_t max_batch;
 } ld_options;
 
 /* Replay-free mode: launch every kernel of a step directly instead of
@@ -173,9 +177,26 @@ typedef struct {
 int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t pos, int32_t n_steps,
                 const ld_sampling* sampling, const float* h_coins, int32_t* h_tokens_out, int32_t* n_out);
 
-/* Device pointers of the key and value caches, each (n_layers, seq_len,
- * kv_dim) fp32 row-major, and their size in floats.  The caller may read or
- * overwrite them between calls (e.g. to install a cache prefix). */
+/* Batch decode: one decode step for each of n sequences at once (n <=
+ * max_batch): sequence b runs forward(h_tokens[b], h_pos[b]) on its own KV
+ * cache; the steps share each weight read (the R/Keras page's batch axis).
+ * *d_logits_out receives n rows of vocab_size logits (library-owned device
+ * memory, valid until the next call).  0 <= h_pos[b] < seq_len; ids in
+ * range.  Asynchronous on the model's stream; h_tokens and h_pos are read
+ * before the call returns. */
+int ld_forward_batch(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int32_t n,
+                     const float** d_logits_out);
+
+/* Greedy generation for n sequences in lockstep: sequence b starts from token
+ * h_tokens[b] at position h_pos[b] and runs n_steps steps as
+ * ld_generate_greedy does; h_tokens_out[b * n_steps + i] is its token after
+ * step i.  Needs h_pos[b] + n_steps <= seq_len.  Synchronous. */
+int ld_generate_greedy_batch(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int32_t n,
+                             int32_t n_steps, int32_t* h_tokens_out);
+
+/* Device pointers of the key and value caches, each (max_batch, n_layers,
+ * seq_len, kv_dim) fp32 row-major, and their size in floats.  The caller may
+ * read or overwrite them between calls (e.g. to install a cache prefix). */
 int ld_kv_cache(ld_model* m, float** d_key_out, float** d_value_out, size_t* floats_out);
 
 /* Free everything the model owns.  NULL is accepted. */

@@ -72,7 +72,7 @@ class Model:
     """
 
     def __init__(self, cfg, weights, *, graph: bool = True, shared_classifier=None, norm_eps=None,
-                 rope_theta=None, stream=None):
+                 rope_theta=None, stream=None, max_batch: int = 1):
         import torch
         if not (weights.is_cuda and weights.dtype == torch.float32 and weights.is_contiguous()):
             raise ValueError("weights must be a contiguous float32 CUDA tensor")
@@ -82,7 +82,8 @@ class Model:
         eps = getattr(cfg, "norm_eps", 1e-5) if norm_eps is None else norm_eps
         theta = getattr(cfg, "rope_theta", 10000.0) if rope_theta is None else rope_theta
         self.c = ld.make_config(cfg)
-        self.o = ld.make_options(eps, theta, int(shared), 0 if graph else LD_OPT_NO_GRAPH)
+        self.o = ld.make_options(eps, theta, int(shared), 0 if graph else LD_OPT_NO_GRAPH, int(max_batch))
+        self.max_batch = max(1, int(max_batch))
         self.stream = stream or torch.cuda.current_stream()
         self.kv_dim = cfg.dim * cfg.n_kv_heads // cfg.n_heads
         self.h = 0
@@ -118,6 +119,15 @@ class Model:
         return ld.ld_generate(self.h, prompt, int(pos), int(n), float(temperature), float(topp), int(stop_token),
                               coins)
 
+    def forward_batch(self, tokens, pos):
+        """One decode step for sequences 0..n-1 (token b at position pos[b]); (n, vocab) logits, a copy."""
+        ptr = ld.ld_forward_batch(self.h, tokens, pos)
+        return copy_from_device(ptr, (len(tokens), self.cfg.vocab_size), stream=self.stream)
+
+    def generate_batch(self, tokens, pos, n: int) -> np.ndarray:
+        """Greedy generation of n steps for each sequence in lockstep; (batch, n) tokens."""
+        return ld.ld_generate_greedy_batch(self.h, tokens, pos, int(n))
+
     def reset(self) -> None:
         ld.ld_reset(self.h)
 
@@ -128,6 +138,8 @@ class Model:
         import torch
         k, v, n = ld.ld_kv_cache(self.h)
         shape = (self.cfg.n_layers, self.cfg.seq_len, self.kv_dim)
+        if self.max_batch > 1:
+            shape = (self.max_batch,) + shape
         return (copy_from_device(k, shape, torch.float32, self.stream),
                 copy_from_device(v, shape, torch.float32, self.stream))
 

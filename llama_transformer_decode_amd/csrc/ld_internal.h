@@ -104,6 +104,13 @@ struct AttnParams {
     int kv_dim;
     int nsplit;            // grid.y
     int chunk;             // keys per split (set by the launcher)
+    // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
+    // out and state are b * q_stride floats / b states further, its caches
+    // b * seq_stride floats, its split partials b * (n_heads * nsplit) pairs
+    // and b * (n_heads * nsplit * head_size) floats
+    int batch;
+    int q_stride;
+    size_t seq_stride;
 };
 
 // Prompt prefill (ld_prefill.hip).  C(M x N) = A(M x K) B(N x K)^T on the
@@ -132,6 +139,12 @@ struct GemmParams {
     int head_size;
     const float2* rope;
     int pos0;
+    const StepState* row_state;  // G_QKV of a decode batch: row m is sequence m at row_state[m].pos
+    size_t seq_stride;           //   floats between two sequences' caches
+    float* part;                 // workspace for split-K partials (NULL: no split)
+    size_t part_floats;
+    int splits;                  // set by the launcher
+    int kchunk;
 };
 
 struct AttnPrefillParams {
@@ -149,8 +162,14 @@ struct AttnPrefillParams {
 };
 
 hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s);
+// a decode batch: x[b] = E[st[b].token]; the greedy token of every logits row,
+// tokens_out[b * tokens_stride + pos_b], and each sequence's state advances
+hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s);
+hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* st, int32_t* tokens_out,
+                              int tokens_stride, hipStream_t s);
 hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s);
 hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s);
+int gemm_splits(int m, int n, int k);  // K splits the launcher uses for m rows (workspace: splits * m * n floats)
 bool attn_prefill_supported(int head_size);
 hipError_t attn_prefill_launch(int head_size, const AttnPrefillParams& p, hipStream_t s);
 

@@ -790,6 +790,47 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const fl
 
 __global__ void set_control_kernel(GenControl* dst, GenControl c) { *dst = c; }
 
+// ---------------------------------------------------------------------------
+// A batch of decode steps: row b is sequence b.
+
+// x[b] = E[state[b].token]
+__global__ __launch_bounds__(256) void embed_state_kernel(const float* __restrict__ emb,
+                                                          const StepState* __restrict__ st, int dim,
+                                                          float* __restrict__ x) {
+    const int b = blockIdx.x;
+    const float4* src = reinterpret_cast<const float4*>(emb + (size_t)st[b].token * dim);
+    float4* dst = reinterpret_cast<float4*>(x + (size_t)b * dim);
+    for (int i = threadIdx.x; i < dim / 4; i += 256) dst[i] = src[i];
+}
+
+// The greedy choice of every row of the batch's logits (one block per row, the
+// argmax order of the "run.c" page), then the step state of that sequence
+// advances as a single sequence's does.
+constexpr int kRowsThreads = 1024;
+
+__global__ __launch_bounds__(kRowsThreads) void argmax_rows_kernel(const float* __restrict__ logits, int n,
+                                                                   StepState* st, int32_t* tokens_out,
+                                                                   int tokens_stride) {
+    const int b = blockIdx.x;
+    const float* row = logits + (size_t)b * n;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int i = threadIdx.x; i < n; i += kRowsThreads)
+        if (better(row[i], i, bv, bi)) {
+            bv = row[i];
+            bi = i;
+        }
+    block_best<kRowsThreads>(bv, bi);
+    if (threadIdx.x == 0) {
+        const int next = bi == INT_MAX ? 0 : bi;  // every value NaN: token 0
+        const int pos = st[b].pos;
+        st[b].next = next;
+        tokens_out[(size_t)b * tokens_stride + pos] = next;
+        st[b].token = next;
+        st[b].pos = pos + 1;
+    }
+}
+
 __global__ void set_state_kernel(StepState* st, int token, int pos) {
     st->token = token;
     st->pos = pos;
@@ -835,8 +876,25 @@ __device__ __forceinline__ void split_of(int n, int ch, int nsplit, int& tiles, 
     nact = (tiles + per - 1) / per;
 }
 
+// Sequence blockIdx.z of a decode batch: its q, output, caches, split
+// partials and state (the identity for a single sequence).
+template <int HS>
+__device__ __forceinline__ AttnParams seq_view(const AttnParams& p) {
+    AttnParams v = p;
+    const int b = blockIdx.z;
+    v.q += (size_t)b * p.q_stride;
+    v.out += (size_t)b * p.q_stride;
+    v.kc += (size_t)b * p.seq_stride;
+    v.vc += (size_t)b * p.seq_stride;
+    v.part_ml += (size_t)b * p.n_heads * p.nsplit;
+    v.part_acc += (size_t)b * p.n_heads * p.nsplit * HS;
+    v.state += b;
+    return v;
+}
+
 template <int HS, int CH>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
+    const AttnParams p = seq_view<HS>(pb);
     constexpr int H4 = HS / 4;
     constexpr int KP = HS + 4;  // padded LDS row
     constexpr int NLOAD = (CH * H4 + kAttnThreads - 1) / kAttnThreads;
@@ -1026,8 +1084,9 @@ __device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
 }
 
 template <int GMAX, int U>
-__global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams pb) {
     constexpr int HS = 128, CH = 32, NW = kAttnThreads / 64;
+    const AttnParams p = seq_view<HS>(pb);
     __shared__ float ms_s[NW][GMAX], ls_s[NW][GMAX];
     __shared__ float4 acc_s[NW][GMAX][32];
     const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
@@ -1153,7 +1212,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams p) {
 // loads); then every column's float4 is summed over split groups, 8 loads in
 // flight per thread, and the groups are added through LDS.
 template <int HS>
-__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb) {
+    const AttnParams p = seq_view<HS>(pb);
     constexpr int H4 = HS / 4;
     constexpr int KG = kAttnThreads / H4;  // split groups (H4 <= 64, so at least 4)
     __shared__ float M_s, L_s;
@@ -1361,7 +1421,8 @@ int attn_splits(int hs, int seq_len, int n_kv_heads) {
 hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     AttnParams p = p0;
     p.chunk = attn_chunk(hs);
-    const dim3 grid(p.n_kv_heads, p.nsplit), block(kAttnThreads);
+    const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
+    const dim3 grid(p.n_kv_heads, p.nsplit, nb), block(kAttnThreads), mgrid(p.n_heads, 1, nb);
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
     if (hs == 128 && LD_ATTN_REG128) {
         // 4 key pairs per wave batch for one or two heads per kv head, 2 for
@@ -1374,14 +1435,14 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
             hipLaunchKernelGGL((attn128_kernel<4, 2>), grid, block, 0, s, p);
         else
             hipLaunchKernelGGL((attn128_kernel<8, 2>), grid, block, 0, s, p);
-        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.n_heads), block, 0, s, p);
+        hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
         return hipGetLastError();
     }
     switch (hs) {
 #define LD_ATTN_CASE(HS, CH)                                                               \
     case HS:                                                                               \
         hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);                   \
-        hipLaunchKernelGGL((attn_merge_kernel<HS>), dim3(p.n_heads), block, 0, s, p);      \
+        hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p);                \
         break;
         LD_ATTN_CASE(16, 64)
         LD_ATTN_CASE(32, 64)
@@ -1394,6 +1455,18 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
 #undef LD_ATTN_CASE
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s) {
+    hipLaunchKernelGGL(embed_state_kernel, dim3(batch), dim3(256), 0, s, emb, st, dim, x);
+    return hipGetLastError();
+}
+
+hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* st, int32_t* tokens_out,
+                              int tokens_stride, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_rows_kernel, dim3(batch), dim3(kRowsThreads), 0, s, logits, n, st, tokens_out,
+                       tokens_stride);
     return hipGetLastError();
 }
 

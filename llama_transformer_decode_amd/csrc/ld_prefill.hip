@@ -70,8 +70,9 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // C = A * B^T on the matrix cores.
 //
-// A block of 256 threads computes a 128 x 128 tile of C: 4 waves in 2 x 2,
-// each a 64 x 64 quarter as 2 x 2 tiles of v_mfma_f32_32x32x2f32.  K is
+// A block of 256 threads computes a BM x 128 tile of C with
+// v_mfma_f32_32x32x2f32 (4 waves; BM = 128 for prompts, 32 for a batch of
+// decode steps, see gemm_kernel).  K is
 // walked in slabs of 16: both operand slabs go global -> registers -> LDS
 // (row-major, K contiguous, rows padded to 20 floats), double-buffered with
 // one barrier per slab; the next slab's global loads are in flight while the
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
 // is still used exactly once.  Rows of A past M and of B past N are clamped
 // (their results are not stored); k past K reads as zero.
 
-constexpr int kBM = 128, kBN = 128, kBK = 16, kRow = kBK + 4, kGemmThreads = 256;
+constexpr int kBN = 128, kBK = 16, kRow = kBK + 4, kGemmThreads = 256;
 
 template <int KIND>
 __device__ __forceinline__ const float* b_row(const GemmParams& p, int r) {
@@ -94,9 +95,10 @@ __device__ __forceinline__ const float* b_row(const GemmParams& p, int r) {
     return p.w0 + (size_t)r * p.k;
 }
 
-__device__ __forceinline__ float4 load_k4(const float* row, int k, int K) {
+// 4 floats of a row at k (zero from kend on; the address stays inside the row)
+__device__ __forceinline__ float4 load_k4(const float* row, int k, int kend, int K) {
     const float4 v = *reinterpret_cast<const float4*>(row + min(k, K - 4));
-    return k < K ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    return k < kend ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
@@ -106,38 +108,97 @@ __device__ __forceinline__ int xcd_local_block(int b, int nb) {
     return x * q + min(x, r) + b / 8;
 }
 
+// C(gm, gn) = v, with other = C(gm, gn ^ 1), the pair partner.
 template <int KIND>
+__device__ __forceinline__ void epilogue(const GemmParams& p, int gm, int gn, float v, float other) {
+    if constexpr (KIND == G_SWIGLU) {
+        // hb = silu(w1 x) * (w3 x), silu(u) = u * 1/(1 + e^-u)
+        if (!(gn & 1)) {
+            float a = v;
+            a *= 1.0f / (1.0f + expf(-a));
+            a *= other;
+            p.out[(size_t)gm * p.ldo + (gn >> 1)] = a;
+        }
+    } else if constexpr (KIND == G_QKV) {
+        // prompt: position pos0 + m of one sequence; batch: row m is sequence m
+        // at its own position
+        const bool odd = gn & 1;
+        const int pos = p.row_state ? p.row_state[gm].pos : p.pos0 + gm;
+        const size_t seq = p.row_state ? (size_t)gm * p.seq_stride : 0;
+        if (gn < p.seg2) {
+            const bool is_q = gn < p.seg1;
+            const int local = is_q ? gn : gn - p.seg1;
+            const int hs = p.head_size;
+            const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + ((local % hs) >> 1)];
+            const float a = odd ? other : v;  // element 2j
+            const float b = odd ? v : other;  // element 2j+1
+            const float rv = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
+            if (is_q)
+                p.out[(size_t)gm * p.ldo + gn] = rv;
+            else
+                p.kc[seq + (size_t)pos * p.kv_stride + local] = rv;
+        } else {
+            p.vc[seq + (size_t)pos * p.kv_stride + (gn - p.seg2)] = v;
+        }
+    } else if constexpr (KIND == G_RESID) {
+        p.out[(size_t)gm * p.ldo + gn] += v;
+    } else {
+        p.out[(size_t)gm * p.ldo + gn] = v;
+    }
+}
+
+// BM = 128 rows (prompt prefill): 2 x 2 waves of 64 x 64.  BM = 32 rows
+// (a batch of decode steps, where the weight stream is the cost): 1 x 4
+// waves of 32 x 32, a quarter of the matrix-core work per weight byte.
+template <int KIND, int BM>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) float As[2][kBM][kRow];
+    constexpr int WAVES_M = BM == 128 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+    constexpr int TM = BM / (32 * WAVES_M), TN = kBN / (32 * WAVES_N);  // 32 x 32 tiles per wave
+    constexpr int A_PER = (BM * 4 + kGemmThreads - 1) / kGemmThreads;   // A float4 loads per thread and slab
+    __shared__ __attribute__((aligned(16))) float As[2][BM][kRow];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBN][kRow];
 
-    const int mtiles = (p.m + kBM - 1) / kBM;
-    const int tile = xcd_local_block(blockIdx.x, gridDim.x);
-    const int m0 = (tile % mtiles) * kBM, n0 = (tile / mtiles) * kBN;
+    const int mtiles = (p.m + BM - 1) / BM;
+    const int lb = xcd_local_block(blockIdx.x, gridDim.x);
+    const int ks = lb % p.splits, tile = lb / p.splits;  // split ks of K for this tile
+    const int m0 = (tile % mtiles) * BM, n0 = (tile / mtiles) * kBN;
+    const int kbeg = ks * p.kchunk, kend = min(p.k, kbeg + p.kchunk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const int wm = (wave % WAVES_M) * (TM * 32), wn = (wave / WAVES_M) * (TN * 32);
 
-    // this thread's two A rows and two B rows of every slab, and its k quad
-    const int lrow0 = tid >> 2, lrow1 = (tid >> 2) + 64, lk = (tid & 3) * 4;
-    const float* arow0 = p.a + (size_t)min(m0 + lrow0, p.m - 1) * p.lda;
-    const float* arow1 = p.a + (size_t)min(m0 + lrow1, p.m - 1) * p.lda;
+    // this thread's A rows and two B rows of every slab, and its k quad
+    const int lk = (tid & 3) * 4;
+    const float* arow[A_PER];
+    int alrow[A_PER];
+    bool aon[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int q = tid + kGemmThreads * i;
+        aon[i] = q < BM * 4;
+        alrow[i] = min(q >> 2, BM - 1);
+        arow[i] = p.a + (size_t)min(m0 + alrow[i], p.m - 1) * p.lda;
+    }
+    const int lrow0 = tid >> 2, lrow1 = (tid >> 2) + 64;
     const float* brow0 = b_row<KIND>(p, min(n0 + lrow0, p.n - 1));
     const float* brow1 = b_row<KIND>(p, min(n0 + lrow1, p.n - 1));
 
-    v16f acc[2][2];
+    v16f acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = (p.k + kBK - 1) / kBK;
-    float4 ra0 = load_k4(arow0, lk, p.k), ra1 = load_k4(arow1, lk, p.k);
-    float4 rb0 = load_k4(brow0, lk, p.k), rb1 = load_k4(brow1, lk, p.k);
-    *reinterpret_cast<float4*>(&As[0][lrow0][lk]) = ra0;
-    *reinterpret_cast<float4*>(&As[0][lrow1][lk]) = ra1;
+    const int nk = (kend - kbeg + kBK - 1) / kBK;
+    float4 ra[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) ra[i] = load_k4(arow[i], kbeg + lk, kend, p.k);
+    float4 rb0 = load_k4(brow0, kbeg + lk, kend, p.k), rb1 = load_k4(brow1, kbeg + lk, kend, p.k);
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i)
+        if (aon[i]) *reinterpret_cast<float4*>(&As[0][alrow[i]][lk]) = ra[i];
     *reinterpret_cast<float4*>(&Bs[0][lrow0][lk]) = rb0;
     *reinterpret_cast<float4*>(&Bs[0][lrow1][lk]) = rb1;
     __syncthreads();
@@ -146,34 +207,38 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
         const int buf = kt & 1;
         const bool more = kt + 1 < nk;
         if (more) {
-            const int k = (kt + 1) * kBK + lk;
-            ra0 = load_k4(arow0, k, p.k);
-            ra1 = load_k4(arow1, k, p.k);
-            rb0 = load_k4(brow0, k, p.k);
-            rb1 = load_k4(brow1, k, p.k);
-        }
-        float av[2][8], bv[2][8];
+            const int k = kbeg + (kt + 1) * kBK + lk;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < A_PER; ++i) ra[i] = load_k4(arow[i], k, kend, p.k);
+            rb0 = load_k4(brow0, k, kend, p.k);
+            rb1 = load_k4(brow1, k, kend, p.k);
+        }
+        float av[TM][8], bv[TN][8];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
             const float4 x0 = *reinterpret_cast<const float4*>(&As[buf][wm + i * 32 + li][lh * 8]);
             const float4 x1 = *reinterpret_cast<const float4*>(&As[buf][wm + i * 32 + li][lh * 8 + 4]);
             av[i][0] = x0.x; av[i][1] = x0.y; av[i][2] = x0.z; av[i][3] = x0.w;
             av[i][4] = x1.x; av[i][5] = x1.y; av[i][6] = x1.z; av[i][7] = x1.w;
-            const float4 y0 = *reinterpret_cast<const float4*>(&Bs[buf][wn + i * 32 + li][lh * 8]);
-            const float4 y1 = *reinterpret_cast<const float4*>(&Bs[buf][wn + i * 32 + li][lh * 8 + 4]);
-            bv[i][0] = y0.x; bv[i][1] = y0.y; bv[i][2] = y0.z; bv[i][3] = y0.w;
-            bv[i][4] = y1.x; bv[i][5] = y1.y; bv[i][6] = y1.z; bv[i][7] = y1.w;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const float4 y0 = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * 32 + li][lh * 8]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * 32 + li][lh * 8 + 4]);
+            bv[j][0] = y0.x; bv[j][1] = y0.y; bv[j][2] = y0.z; bv[j][3] = y0.w;
+            bv[j][4] = y1.x; bv[j][5] = y1.y; bv[j][6] = y1.z; bv[j][7] = y1.w;
         }
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][s], bv[j][s], acc[i][j], 0, 0, 0);
         if (more) {
-            *reinterpret_cast<float4*>(&As[buf ^ 1][lrow0][lk]) = ra0;
-            *reinterpret_cast<float4*>(&As[buf ^ 1][lrow1][lk]) = ra1;
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i)
+                if (aon[i]) *reinterpret_cast<float4*>(&As[buf ^ 1][alrow[i]][lk]) = ra[i];
             *reinterpret_cast<float4*>(&Bs[buf ^ 1][lrow0][lk]) = rb0;
             *reinterpret_cast<float4*>(&Bs[buf ^ 1][lrow1][lk]) = rb1;
         }
@@ -183,55 +248,45 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
     // Epilogue.  Register r of tile (i, j) holds C(row, col) with
     // row = wm + 32i + 8(r/4) + 4h + r%4 and col = wn + 32j + (lane % 32):
     // lanes 2c and 2c+1 hold the adjacent columns (2c, 2c+1) of one row, the
-    // pair RoPE rotates and the (w1, w3) pair SwiGLU combines.
+    // pair RoPE rotates and the (w1, w3) pair SwiGLU combines.  With split K
+    // the block stores its partial tile instead; gemm_reduce_kernel sums the
+    // splits in order and applies the epilogue.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int gm = m0 + wm + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
                 const int gn = n0 + wn + j * 32 + li;
                 const float v = acc[i][j][r];
-                if constexpr (KIND == G_QKV || KIND == G_SWIGLU) {
-                    const float other = __shfl_xor(v, 1);
-                    if (gm < p.m && gn < p.n) {
-                        const bool odd = gn & 1;
-                        if constexpr (KIND == G_SWIGLU) {
-                            // hb = silu(w1 x) * (w3 x), silu(u) = u * 1/(1 + e^-u)
-                            if (!odd) {
-                                float a = v;
-                                a *= 1.0f / (1.0f + expf(-a));
-                                a *= other;
-                                p.out[(size_t)gm * p.ldo + (gn >> 1)] = a;
-                            }
-                        } else {
-                            const int pos = p.pos0 + gm;
-                            if (gn < p.seg2) {
-                                const bool is_q = gn < p.seg1;
-                                const int local = is_q ? gn : gn - p.seg1;
-                                const int hs = p.head_size;
-                                const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + ((local % hs) >> 1)];
-                                const float a = odd ? other : v;  // element 2j
-                                const float b = odd ? v : other;  // element 2j+1
-                                const float rv = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
-                                if (is_q)
-                                    p.out[(size_t)gm * p.ldo + gn] = rv;
-                                else
-                                    p.kc[(size_t)pos * p.kv_stride + local] = rv;
-                            } else {
-                                p.vc[(size_t)pos * p.kv_stride + (gn - p.seg2)] = v;
-                            }
-                        }
-                    }
-                } else if (gm < p.m && gn < p.n) {
-                    float* o = p.out + (size_t)gm * p.ldo + gn;
-                    if constexpr (KIND == G_RESID)
-                        *o += v;
-                    else
-                        *o = v;
+                if (p.splits > 1) {
+                    if (gm < p.m && gn < p.n) p.part[((size_t)ks * p.m + gm) * p.n + gn] = v;
+                    continue;
                 }
+                const float other = (KIND == G_QKV || KIND == G_SWIGLU) ? __shfl_xor(v, 1) : 0.f;
+                if (gm < p.m && gn < p.n) epilogue<KIND>(p, gm, gn, v, other);
             }
+}
+
+// Sum of the split partials of C, in split order, then the epilogue: one
+// thread per (row, column pair).
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
+    const int pairs = (p.n + 1) / 2;
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long long)p.m * pairs) return;
+    const int gm = (int)(e / pairs), c = (int)(e % pairs), gn = 2 * c;
+    const bool two = gn + 1 < p.n;
+    float v0 = 0.f, v1 = 0.f;
+    const size_t stride = (size_t)p.m * p.n;
+    const float* src = p.part + (size_t)gm * p.n + gn;
+    for (int ks = 0; ks < p.splits; ++ks) {
+        v0 += src[ks * stride];
+        if (two) v1 += src[ks * stride + 1];
+    }
+    epilogue<KIND>(p, gm, gn, v0, v1);
+    if (two) epilogue<KIND>(p, gm, gn + 1, v1, v0);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,19 +434,63 @@ hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t,
     return hipGetLastError();
 }
 
-hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s) {
-    if (p.m <= 0 || p.n <= 0 || p.k < 4 || (p.k % 4)) return hipErrorInvalidValue;
-    const long long tiles = (long long)((p.m + kBM - 1) / kBM) * ((p.n + kBN - 1) / kBN);
-    if (tiles > INT_MAX) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)tiles), block(kGemmThreads);
+namespace {
+
+template <int BM>
+hipError_t gemm_launch_bm(int kind, const GemmParams& p, hipStream_t s) {
+    const long long blocks = (long long)((p.m + BM - 1) / BM) * ((p.n + kBN - 1) / kBN) * p.splits;
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks), block(kGemmThreads);
     switch (kind) {
-        case G_PLAIN: hipLaunchKernelGGL(gemm_kernel<G_PLAIN>, grid, block, 0, s, p); break;
-        case G_RESID: hipLaunchKernelGGL(gemm_kernel<G_RESID>, grid, block, 0, s, p); break;
-        case G_QKV: hipLaunchKernelGGL(gemm_kernel<G_QKV>, grid, block, 0, s, p); break;
-        case G_SWIGLU: hipLaunchKernelGGL(gemm_kernel<G_SWIGLU>, grid, block, 0, s, p); break;
+        case G_PLAIN: hipLaunchKernelGGL((gemm_kernel<G_PLAIN, BM>), grid, block, 0, s, p); break;
+        case G_RESID: hipLaunchKernelGGL((gemm_kernel<G_RESID, BM>), grid, block, 0, s, p); break;
+        case G_QKV: hipLaunchKernelGGL((gemm_kernel<G_QKV, BM>), grid, block, 0, s, p); break;
+        case G_SWIGLU: hipLaunchKernelGGL((gemm_kernel<G_SWIGLU, BM>), grid, block, 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
+    if (p.splits > 1) {
+        const long long threads = (long long)p.m * ((p.n + 1) / 2);
+        const dim3 rgrid((unsigned)((threads + 255) / 256));
+        switch (kind) {
+            case G_PLAIN: hipLaunchKernelGGL(gemm_reduce_kernel<G_PLAIN>, rgrid, block, 0, s, p); break;
+            case G_RESID: hipLaunchKernelGGL(gemm_reduce_kernel<G_RESID>, rgrid, block, 0, s, p); break;
+            case G_QKV: hipLaunchKernelGGL(gemm_reduce_kernel<G_QKV>, rgrid, block, 0, s, p); break;
+            case G_SWIGLU: hipLaunchKernelGGL(gemm_reduce_kernel<G_SWIGLU>, rgrid, block, 0, s, p); break;
+        }
+    }
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Splits of K for a product with few row tiles (a decode batch): with whole K
+// each block would stream its weight rows alone, and a few hundred blocks
+// leave most of the chip idle; splitting K gives about 1024 blocks (at least
+// 256 of K each), so every CU has several weight streams in flight.  Used
+// only where the caller provides the partials' workspace.
+// Row tile of a product of m rows: 32 for a decode batch (m <= 64, where the
+// weight stream is the cost and a 128-row tile would be matrix-core bound)
+// and for short prompts, 128 above.
+int gemm_tile_rows(int m) { return m <= 64 ? 32 : 128; }
+
+int gemm_splits(int m, int n, int k) {
+    const int bm = gemm_tile_rows(m);
+    const long long tiles = (long long)((m + bm - 1) / bm) * ((n + kBN - 1) / kBN);
+    if (tiles >= 1024) return 1;
+    const int sp = (int)((1024 + tiles - 1) / tiles);
+    return max(1, min(sp, k / 256));
+}
+
+// 32- or 128-row tiles (gemm_tile_rows); split K when a workspace is given
+hipError_t gemm_launch(int kind, const GemmParams& p0, hipStream_t s) {
+    GemmParams p = p0;
+    if (p.m <= 0 || p.n <= 0 || p.k < 4 || (p.k % 4)) return hipErrorInvalidValue;
+    p.splits = p.part ? gemm_splits(p.m, p.n, p.k) : 1;
+    const int chunk = (p.k + p.splits - 1) / p.splits;
+    p.kchunk = (chunk + kBK - 1) / kBK * kBK;
+    p.splits = (p.k + p.kchunk - 1) / p.kchunk;
+    if (p.splits > 1 && (size_t)p.splits * p.m * p.n > p.part_floats) return hipErrorInvalidValue;
+    return gemm_tile_rows(p.m) == 32 ? gemm_launch_bm<32>(kind, p, s) : gemm_launch_bm<128>(kind, p, s);
 }
 
 bool attn_prefill_supported(int hs) {

@@ -20,6 +20,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <map>
 #include <new>
 #include <vector>
 
@@ -59,6 +60,7 @@ int validate(const ld_config* c, const ld_options* o) {
     if ((c->dim % 4) || (c->hidden_dim % 4) || (kv % 4)) return LD_E_CONFIG;
     if (!(o->norm_eps >= 0.f) || !(o->rope_theta > 0.f) || !std::isfinite(o->rope_theta)) return LD_E_CONFIG;
     if (o->shared_classifier != 0 && o->shared_classifier != 1) return LD_E_CONFIG;
+    if (o->max_batch < 0) return LD_E_CONFIG;
     if (!supported_head_size(hs)) return LD_E_UNSUPPORTED;
     const int group = (c->n_heads + c->n_kv_heads - 1) / c->n_kv_heads;
     if (group > kMaxGroup) return LD_E_UNSUPPORTED;
@@ -124,6 +126,22 @@ struct ld_model {
     bool ptok_pending = false;
     int pf_cap = 0;
     float *pf_x = nullptr, *pf_xn = nullptr, *pf_q = nullptr, *pf_att = nullptr, *pf_hb = nullptr;
+    // decode batch: max_batch sequences, each with its own cache (caches are
+    // (max_batch, L, S, kv_dim)), their activations, states and tokens, and
+    // one captured graph per batch size
+    int max_batch = 1;
+    float *bx = nullptr, *bxn = nullptr, *bq = nullptr, *batt = nullptr, *bhb = nullptr, *blogits = nullptr;
+    float2* bpart_ml = nullptr;
+    float* bpart_acc = nullptr;
+    float* bsplit = nullptr;         // split-K partials of the batch products
+    size_t bsplit_floats = 0;
+    StepState* bstate = nullptr;
+    int32_t* btokens = nullptr;      // (max_batch, S): the token chosen at each position
+    StepState* h_bstate = nullptr;   // pinned staging
+    int32_t* h_btokens = nullptr;
+    hipEvent_t ev_bstate = nullptr;
+    bool bstate_pending = false;
+    std::map<int, std::pair<hipGraph_t, hipGraphExec_t>> batch_graphs;
     GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
@@ -151,6 +169,13 @@ void release(ld_model* m) {
     if (m->stream) (void)hipStreamSynchronize(m->stream);
     if (m->exec) (void)hipGraphExecDestroy(m->exec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
+    for (auto& g : m->batch_graphs) {
+        if (g.second.second) (void)hipGraphExecDestroy(g.second.second);
+        if (g.second.first) (void)hipGraphDestroy(g.second.first);
+    }
+    if (m->h_bstate) (void)hipHostFree(m->h_bstate);
+    if (m->h_btokens) (void)hipHostFree(m->h_btokens);
+    if (m->ev_bstate) (void)hipEventDestroy(m->ev_bstate);
     for (void* p : m->dev_allocs) (void)hipFree(p);
     for (float* p : {m->pf_x, m->pf_xn, m->pf_q, m->pf_att, m->pf_hb})
         if (p) (void)hipFree(p);
@@ -469,6 +494,170 @@ int prefill_chunk(ld_model* m, int p0, int T) {
     return LD_OK;
 }
 
+// One decode step of sequences 0..n-1 of the batch, each reading (token, pos)
+// from m->bstate[b]: the single step's sequence of operations with the weight
+// matrices as 32-row matrix-core products, so every weight is read once for
+// the whole batch.
+int launch_batch_step(ld_model* m, int n) {
+    const ld_config& c = m->cfg;
+    const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
+    const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
+    hipStream_t s = m->stream;
+    HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_att + (size_t)l * d, m->opt.norm_eps, n, c.dim, m->bxn, s));
+        {
+            GemmParams g{};
+            g.a = m->bxn;
+            g.lda = c.dim;
+            g.m = n;
+            g.part = m->bsplit;
+            g.part_floats = m->bsplit_floats;
+            g.n = c.dim + 2 * m->kv_dim;
+            g.k = c.dim;
+            g.w0 = m->wq + (size_t)l * d * d;
+            g.w1 = m->wk + (size_t)l * kv * d;
+            g.w2 = m->wv + (size_t)l * kv * d;
+            g.seg1 = c.dim;
+            g.seg2 = c.dim + m->kv_dim;
+            g.out = m->bq;
+            g.ldo = c.dim;
+            g.kc = m->kc + (size_t)l * cache_layer;
+            g.vc = m->vc + (size_t)l * cache_layer;
+            g.kv_stride = m->kv_dim;
+            g.head_size = m->hs;
+            g.rope = m->rope;
+            g.row_state = m->bstate;
+            g.seq_stride = seq_stride;
+            HIP_TRY(gemm_launch(G_QKV, g, s));
+        }
+        {
+            AttnParams a{};
+            a.q = m->bq;
+            a.kc = m->kc + (size_t)l * cache_layer;
+            a.vc = m->vc + (size_t)l * cache_layer;
+            a.out = m->batt;
+            a.part_ml = m->bpart_ml;
+            a.part_acc = m->bpart_acc;
+            a.state = m->bstate;
+            a.n_heads = c.n_heads;
+            a.n_kv_heads = c.n_kv_heads;
+            a.kv_dim = m->kv_dim;
+            a.nsplit = m->nsplit;
+            a.batch = n;
+            a.q_stride = c.dim;
+            a.seq_stride = seq_stride;
+            HIP_TRY(attn_launch(m->hs, a, s));
+        }
+        {
+            GemmParams g{};
+            g.a = m->batt;
+            g.lda = c.dim;
+            g.m = n;
+            g.part = m->bsplit;
+            g.part_floats = m->bsplit_floats;
+            g.n = c.dim;
+            g.k = c.dim;
+            g.w0 = m->wo + (size_t)l * d * d;
+            g.out = m->bx;
+            g.ldo = c.dim;
+            HIP_TRY(gemm_launch(G_RESID, g, s));
+        }
+        HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_ffn + (size_t)l * d, m->opt.norm_eps, n, c.dim, m->bxn, s));
+        {
+            GemmParams g{};
+            g.a = m->bxn;
+            g.lda = c.dim;
+            g.m = n;
+            g.part = m->bsplit;
+            g.part_floats = m->bsplit_floats;
+            g.n = 2 * c.hidden_dim;
+            g.k = c.dim;
+            g.w0 = m->w1 + (size_t)l * h * d;
+            g.w1 = m->w3 + (size_t)l * h * d;
+            g.out = m->bhb;
+            g.ldo = c.hidden_dim;
+            HIP_TRY(gemm_launch(G_SWIGLU, g, s));
+        }
+        {
+            GemmParams g{};
+            g.a = m->bhb;
+            g.lda = c.hidden_dim;
+            g.m = n;
+            g.part = m->bsplit;
+            g.part_floats = m->bsplit_floats;
+            g.n = c.dim;
+            g.k = c.hidden_dim;
+            g.w0 = m->w2 + (size_t)l * d * h;
+            g.out = m->bx;
+            g.ldo = c.dim;
+            HIP_TRY(gemm_launch(G_RESID, g, s));
+        }
+    }
+    HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_final, m->opt.norm_eps, n, c.dim, m->bxn, s));
+    {
+        GemmParams g{};
+        g.a = m->bxn;
+        g.lda = c.dim;
+        g.m = n;
+        g.part = m->bsplit;
+        g.part_floats = m->bsplit_floats;
+        g.n = c.vocab_size;
+        g.k = c.dim;
+        g.w0 = m->wcls;
+        g.out = m->blogits;
+        g.ldo = c.vocab_size;
+        HIP_TRY(gemm_launch(G_PLAIN, g, s));
+    }
+    HIP_TRY(argmax_rows_launch(m->blogits, n, c.vocab_size, m->bstate, m->btokens, c.seq_len, s));
+    return LD_OK;
+}
+
+int run_batch_step(ld_model* m, int n) {
+    if (!m->use_graph) return launch_batch_step(m, n);
+    auto it = m->batch_graphs.find(n);
+    if (it == m->batch_graphs.end()) {
+        HIP_TRY(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+        int rc = launch_batch_step(m, n);
+        hipGraph_t g = nullptr;
+        hipError_t e = hipStreamEndCapture(m->stream, &g);
+        if (rc != LD_OK) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc;
+        }
+        if (e != hipSuccess) return fail_hip(e, "hipStreamEndCapture");
+        hipGraphExec_t x = nullptr;
+        e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            (void)hipGraphDestroy(g);
+            return fail_hip(e, "hipGraphInstantiate");
+        }
+        it = m->batch_graphs.emplace(n, std::make_pair(g, x)).first;
+    }
+    HIP_TRY(hipGraphLaunch(it->second.second, m->stream));
+    return LD_OK;
+}
+
+// Stage the batch's (token, pos) pairs into the device states.
+int set_batch_states(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int n) {
+    if (m->bstate_pending) HIP_TRY(hipEventSynchronize(m->ev_bstate));
+    for (int b = 0; b < n; ++b) m->h_bstate[b] = StepState{h_tokens[b], h_pos[b], -1, 0};
+    HIP_TRY(hipMemcpyAsync(m->bstate, m->h_bstate, sizeof(StepState) * (size_t)n, hipMemcpyHostToDevice,
+                           m->stream));
+    HIP_TRY(hipEventRecord(m->ev_bstate, m->stream));
+    m->bstate_pending = true;
+    return LD_OK;
+}
+
+int check_batch(const ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int n, int n_steps) {
+    if (n < 1 || n > m->max_batch || n_steps < 0) return LD_E_RANGE;
+    for (int b = 0; b < n; ++b) {
+        if (h_tokens[b] < 0 || h_tokens[b] >= m->cfg.vocab_size) return LD_E_RANGE;
+        if (h_pos[b] < 0 || (long long)h_pos[b] + (n_steps > 0 ? n_steps : 1) > m->cfg.seq_len) return LD_E_RANGE;
+    }
+    return LD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -514,6 +703,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         m->cfg = *cfg;
         m->opt = *opt;
         m->use_graph = !(opt->flags & LD_OPT_NO_GRAPH);
+        m->max_batch = opt->max_batch > 1 ? opt->max_batch : 1;
         m->user = static_cast<hipStream_t>(hip_stream);
         hipError_t e = hipGetDevice(&m->device);
         if (e != hipSuccess) { rc = fail_hip(e, "hipGetDevice"); break; }
@@ -546,9 +736,10 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[0], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_poll[1], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_ptok, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&m->ev_bstate, hipEventDisableTiming);
         if (e != hipSuccess) { rc = fail_hip(e, "hipEventCreate"); break; }
 
-        const size_t cache = (size_t)cfg->n_layers * cfg->seq_len * kv;
+        const size_t cache = (size_t)m->max_batch * cfg->n_layers * cfg->seq_len * kv;
         if ((rc = dalloc(m, &m->kc, cache)) || (rc = dalloc(m, &m->vc, cache)) || (rc = dalloc(m, &m->x, d)) ||
             (rc = dalloc(m, &m->xb, d)) || (rc = dalloc(m, &m->q, d)) || (rc = dalloc(m, &m->hb, h)) ||
             (rc = dalloc(m, &m->logits, V)) ||
@@ -578,6 +769,32 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             break;
         rc = dalloc(m, &m->best, (size_t)m->pcls.grid);
         if (rc) break;
+        {  // batch buffers (also for max_batch 1, so a batch of one runs)
+            const size_t B = m->max_batch;
+            if ((rc = dalloc(m, &m->bx, B * d)) || (rc = dalloc(m, &m->bxn, B * d)) || (rc = dalloc(m, &m->bq, B * d)) ||
+                (rc = dalloc(m, &m->batt, B * d)) || (rc = dalloc(m, &m->bhb, B * h)) ||
+                (rc = dalloc(m, &m->blogits, B * V)) ||
+                (rc = dalloc(m, &m->bpart_ml, B * cfg->n_heads * m->nsplit)) ||
+                (rc = dalloc(m, &m->bpart_acc, B * cfg->n_heads * m->nsplit * m->hs)) ||
+                (rc = dalloc(m, &m->bstate, B)) || (rc = dalloc(m, &m->btokens, B * cfg->seq_len)))
+                break;
+            // the largest split-K workspace any batch size up to B needs
+            const int shapes[5][2] = {{cfg->dim + 2 * m->kv_dim, cfg->dim}, {cfg->dim, cfg->dim},
+                                      {2 * cfg->hidden_dim, cfg->dim}, {cfg->dim, cfg->hidden_dim},
+                                      {cfg->vocab_size, cfg->dim}};
+            size_t ws = 0;
+            for (int nb = 1; nb <= m->max_batch; ++nb)
+                for (const auto& sh : shapes) {
+                    const size_t need = (size_t)gemm_splits(nb, sh[0], sh[1]) * nb * sh[0];
+                    if (need > ws) ws = need;
+                }
+            m->bsplit_floats = ws;
+            if ((rc = dalloc(m, &m->bsplit, ws))) break;
+            e = hipHostMalloc((void**)&m->h_bstate, sizeof(StepState) * B, hipHostMallocDefault);
+            if (e == hipSuccess)
+                e = hipHostMalloc((void**)&m->h_btokens, sizeof(int32_t) * B * cfg->seq_len, hipHostMallocDefault);
+            if (e != hipSuccess) { rc = fail_hip(e, "hipHostMalloc"); break; }
+        }
 
         std::vector<float2> rt = rope_table(cfg->seq_len, m->hs, (double)opt->rope_theta);
         e = hipMemcpy(m->rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice);
@@ -605,7 +822,7 @@ int ld_reset(ld_model* m) {
     if (!m) return LD_E_NULL;
     int rc = enter(m);
     if (rc) return rc;
-    const size_t cache = (size_t)m->cfg.n_layers * m->cfg.seq_len * m->kv_dim * sizeof(float);
+    const size_t cache = (size_t)m->max_batch * m->cfg.n_layers * m->cfg.seq_len * m->kv_dim * sizeof(float);
     HIP_TRY(hipMemsetAsync(m->kc, 0, cache, m->stream));
     HIP_TRY(hipMemsetAsync(m->vc, 0, cache, m->stream));
     return leave(m);
@@ -776,11 +993,43 @@ int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t p
     return leave(m);
 }
 
+int ld_forward_batch(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int32_t n,
+                     const float** d_logits_out) {
+    if (!m || !h_tokens || !h_pos || !d_logits_out) return LD_E_NULL;
+    int rc = check_batch(m, h_tokens, h_pos, n, 0);
+    if (rc) return rc;
+    if ((rc = enter(m))) return rc;
+    if ((rc = set_batch_states(m, h_tokens, h_pos, n))) return rc;
+    if ((rc = run_batch_step(m, n))) return rc;
+    *d_logits_out = m->blogits;
+    return leave(m);
+}
+
+int ld_generate_greedy_batch(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int32_t n,
+                             int32_t n_steps, int32_t* h_tokens_out) {
+    if (!m || !h_tokens || !h_pos || (!h_tokens_out && n_steps > 0)) return LD_E_NULL;
+    int rc = check_batch(m, h_tokens, h_pos, n, n_steps);
+    if (rc) return rc;
+    if (n_steps == 0) return LD_OK;
+    if ((rc = enter(m))) return rc;
+    if ((rc = set_batch_states(m, h_tokens, h_pos, n))) return rc;
+    for (int i = 0; i < n_steps; ++i)
+        if ((rc = run_batch_step(m, n))) return rc;
+    const int S = m->cfg.seq_len;
+    HIP_TRY(hipMemcpyAsync(m->h_btokens, m->btokens, sizeof(int32_t) * (size_t)n * S, hipMemcpyDeviceToHost,
+                           m->stream));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    for (int b = 0; b < n; ++b)
+        std::memcpy(h_tokens_out + (size_t)b * n_steps, m->h_btokens + (size_t)b * S + h_pos[b],
+                    sizeof(int32_t) * (size_t)n_steps);
+    return leave(m);
+}
+
 int ld_kv_cache(ld_model* m, float** d_key_out, float** d_value_out, size_t* floats_out) {
     if (!m || !d_key_out || !d_value_out || !floats_out) return LD_E_NULL;
     *d_key_out = m->kc;
     *d_value_out = m->vc;
-    *floats_out = (size_t)m->cfg.n_layers * m->cfg.seq_len * m->kv_dim;
+    *floats_out = (size_t)m->max_batch * m->cfg.n_layers * m->cfg.seq_len * m->kv_dim;
     return LD_OK;
 }
 
@@ -1076,6 +1325,12 @@ int ld_op_gemm(const float* d_a, const float* d_w, int32_t m, int32_t n, int32_t
     g.out = d_out;
     g.ldo = n;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    Temps tmp;
+    const int splits = gemm_splits(m, n, k);
+    if (splits > 1) {  // split K, as a decode batch runs it
+        g.part_floats = (size_t)splits * m * n;
+        HIP_TRY(tmp.get(&g.part, g.part_floats));
+    }
     HIP_TRY(gemm_launch(G_PLAIN, g, s));
     HIP_TRY(hipStreamSynchronize(s));
     return LD_OK;

@@ -27,7 +27,7 @@ LD_OPT_NO_GRAPH = 1
 # Every symbol include/ld.h declares.
 EXPORTS = (
     "ld_weights_size", "ld_create", "ld_reset", "ld_forward", "ld_argmax_last", "ld_generate_greedy",
-    "ld_generate", "ld_prefill", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
+    "ld_generate", "ld_prefill", "ld_forward_batch", "ld_generate_greedy_batch", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
     "ld_profile_steps", "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope",
     "ld_op_attention", "ld_op_gemm", "ld_op_attention_prefill", "ld_op_argmax", "ld_op_sample",
 )
@@ -49,7 +49,7 @@ class ld_config(ctypes.Structure):
 
 class ld_options(ctypes.Structure):
     _fields_ = [("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("shared_classifier", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("shared_classifier", ctypes.c_int32), ("flags", ctypes.c_int32), ("max_batch", ctypes.c_int32)]
 
 
 class ld_sampling(ctypes.Structure):
@@ -90,6 +90,8 @@ def library():
             "ld_generate_greedy": ([_P, _I, _I, _I, _P], ctypes.c_int),
             "ld_generate": ([_P, _P, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I)], ctypes.c_int),
             "ld_prefill": ([_P, _P, _I, _I, ctypes.POINTER(_P)], ctypes.c_int),
+            "ld_forward_batch": ([_P, _P, _P, _I, ctypes.POINTER(_P)], ctypes.c_int),
+            "ld_generate_greedy_batch": ([_P, _P, _P, _I, _I, _P], ctypes.c_int),
             "ld_kv_cache": ([_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t)],
                             ctypes.c_int),
             "ld_destroy": ([_P], None),
@@ -126,8 +128,8 @@ def make_config(cfg) -> ld_config:
 
 
 def make_options(norm_eps: float = 1e-5, rope_theta: float = 10000.0, shared_classifier: int = 0,
-                 flags: int = 0) -> ld_options:
-    return ld_options(norm_eps, rope_theta, shared_classifier, flags)
+                 flags: int = 0, max_batch: int = 1) -> ld_options:
+    return ld_options(norm_eps, rope_theta, shared_classifier, flags, max_batch)
 
 
 # --------------------------------------------------------------------------- entry points
@@ -194,6 +196,29 @@ def ld_prefill(h: int, tokens, pos: int) -> int:
     out = _P()
     _check(library().ld_prefill(h, t.ctypes.data if t.size else None, t.size, pos, ctypes.byref(out)), "ld_prefill")
     return out.value
+
+
+def ld_forward_batch(h: int, tokens, pos) -> int:
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if t.size != p.size:
+        raise ValueError("one position per token")
+    out = _P()
+    _check(library().ld_forward_batch(h, t.ctypes.data if t.size else None, p.ctypes.data if p.size else None,
+                                      t.size, ctypes.byref(out)), "ld_forward_batch")
+    return out.value
+
+
+def ld_generate_greedy_batch(h: int, tokens, pos, n_steps: int) -> np.ndarray:
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    if t.size != p.size:
+        raise ValueError("one position per token")
+    out = np.zeros(max(t.size * n_steps, 1), np.int32)
+    _check(library().ld_generate_greedy_batch(h, t.ctypes.data if t.size else None,
+                                              p.ctypes.data if p.size else None, t.size, n_steps, out.ctypes.data),
+           "ld_generate_greedy_batch")
+    return out[:t.size * n_steps].reshape(t.size, n_steps)
 
 
 def ld_kv_cache(h: int):

@@ -144,3 +144,26 @@ def test_long_prefill_equals_token_by_token_decode(big):
     assert ok
     for g, r in ((ka, kb), (va, vb)):
         assert np.max(np.abs(g - r)) <= 1e-4 * np.max(np.abs(r))
+
+
+def test_batch_step_at_full_size(big):
+    # one batched step of several sequences at different installed prefixes, each row against the oracle
+    cfg, blob, w = big
+    lengths = {"llama7b": [0, 700, 2000, 33], "llama70b_8l": [4000, 1500]}[cfg.name]
+    B = len(lengths)
+    caches = [(_prefix(cfg, p, 900 + 50 * b) if p else oracle.KVCache(cfg)) for b, p in enumerate(lengths)]
+    toks = synth.prefill_tokens(cfg, B)
+    import torch
+    with pkg.Model(cfg, w, max_batch=B) as m:
+        kv = cfg.dim * cfg.n_kv_heads // cfg.n_heads
+        k = np.stack([c.k for c in caches])
+        v = np.stack([c.v for c in caches])
+        m.write_kv_cache(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+        del k, v
+        got = host(m.forward_batch(toks, lengths))
+    for b in range(B):
+        ref = oracle.forward(cfg, blob, caches[b], int(toks[b]), lengths[b])
+        ok, err, tol = logits_close(got[b], ref)
+        print(f"[{cfg.name}] batch row {b} at {lengths[b]}: max |d logit| {err:.3g} (tolerance {tol:.3g})",
+              flush=True)
+        assert ok
