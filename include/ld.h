@@ -139,6 +139,12 @@ int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps,
  * a head size the prefill attention kernel has no instance for. */
 int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t pos, const float** d_logits_out);
 
+/* ld_prefill into the KV cache of sequence seq (0 <= seq < max_batch, else
+ * LD_E_RANGE) of a batch model, e.g. each prompt of a batch before
+ * ld_generate_greedy_batch; ld_prefill is ld_prefill_seq with seq 0. */
+int ld_prefill_seq(ld_model* m, int32_t seq, const int32_t* h_tokens, int32_t n_tokens, int32_t pos,
+                   const float** d_logits_out);
+
 /* How the generation loop chooses tokens after the prompt ("run.c 逐行解讀"
  * §6, sample(), three modes):
  *   temperature <= 0: the argmax (greedy, as above);

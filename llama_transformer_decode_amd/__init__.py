@@ -94,14 +94,15 @@ class Model:
         ptr = ld.ld_forward(self.h, int(token), int(pos))
         return copy_from_device(ptr, (self.cfg.vocab_size,), stream=self.stream)
 
-    def prefill(self, tokens, pos: int):
+    def prefill(self, tokens, pos: int, seq: int = 0):
         """All prompt tokens at positions pos.. at once; returns the last token's logits (a copy)."""
-        ptr = self.prefill_async(tokens, pos)
+        ptr = self.prefill_async(tokens, pos, seq)
         return copy_from_device(ptr, (self.cfg.vocab_size,), stream=self.stream)
 
-    def prefill_async(self, tokens, pos: int) -> int:
-        """Queue a prompt prefill; returns the library-owned device logits pointer."""
-        return ld.ld_prefill(self.h, tokens, int(pos))
+    def prefill_async(self, tokens, pos: int, seq: int = 0) -> int:
+        """Queue a prompt prefill (into sequence seq of a batch model); returns the
+        library-owned device logits pointer."""
+        return ld.ld_prefill_seq(self.h, int(seq), tokens, int(pos))
 
     def forward_async(self, token: int, pos: int) -> int:
         """Queue one decode step; returns the library-owned device logits pointer."""

@@ -404,13 +404,15 @@ int prefill_workspace(ld_model* m, int tokens) {
     return LD_OK;
 }
 
-// One chunk of T prompt tokens at positions p0 .. p0 + T - 1 (their ids in
-// m->ptok[p0 ..]): every layer of the step over all T tokens at once; leaves
-// the final residual stream in pf_x.
-int prefill_chunk(ld_model* m, int p0, int T) {
+// One chunk of T prompt tokens of sequence seq at positions p0 .. p0 + T - 1
+// (their ids in m->ptok[p0 ..]): every layer of the step over all T tokens at
+// once; leaves the final residual stream in pf_x.
+int prefill_chunk(ld_model* m, int seq, int p0, int T) {
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
     const size_t cache_layer = (size_t)c.seq_len * kv;
+    float* kc = m->kc + (size_t)seq * c.n_layers * cache_layer;  // this sequence's caches
+    float* vc = m->vc + (size_t)seq * c.n_layers * cache_layer;
     hipStream_t s = m->stream;
     HIP_TRY(embed_launch(m->emb, m->ptok + p0, T, c.dim, m->pf_x, s));
     for (int l = 0; l < c.n_layers; ++l) {
@@ -429,8 +431,8 @@ int prefill_chunk(ld_model* m, int p0, int T) {
             g.seg2 = c.dim + m->kv_dim;
             g.out = m->pf_q;
             g.ldo = c.dim;
-            g.kc = m->kc + (size_t)l * cache_layer;
-            g.vc = m->vc + (size_t)l * cache_layer;
+            g.kc = kc + (size_t)l * cache_layer;
+            g.vc = vc + (size_t)l * cache_layer;
             g.kv_stride = m->kv_dim;
             g.head_size = m->hs;
             g.rope = m->rope;
@@ -441,8 +443,8 @@ int prefill_chunk(ld_model* m, int p0, int T) {
             AttnPrefillParams a{};
             a.q = m->pf_q;
             a.ldq = c.dim;
-            a.kc = m->kc + (size_t)l * cache_layer;
-            a.vc = m->vc + (size_t)l * cache_layer;
+            a.kc = kc + (size_t)l * cache_layer;
+            a.vc = vc + (size_t)l * cache_layer;
             a.kv_stride = m->kv_dim;
             a.out = m->pf_att;
             a.ldo = c.dim;
@@ -943,8 +945,14 @@ int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t 
 }
 
 int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t pos, const float** d_logits_out) {
+    return ld_prefill_seq(m, 0, h_tokens, n_tokens, pos, d_logits_out);
+}
+
+int ld_prefill_seq(ld_model* m, int32_t seq, const int32_t* h_tokens, int32_t n_tokens, int32_t pos,
+                   const float** d_logits_out) {
     if (!m || !h_tokens || !d_logits_out) return LD_E_NULL;
     const ld_config& c = m->cfg;
+    if (seq < 0 || seq >= m->max_batch) return LD_E_RANGE;
     if (n_tokens < 1 || pos < 0 || (long long)pos + n_tokens > c.seq_len) return LD_E_RANGE;
     for (int i = 0; i < n_tokens; ++i)
         if (h_tokens[i] < 0 || h_tokens[i] >= c.vocab_size) return LD_E_RANGE;
@@ -964,7 +972,7 @@ int ld_prefill(ld_model* m, const int32_t* h_tokens, int32_t n_tokens, int32_t p
     int last = 0;
     for (int c0 = 0; c0 < n_tokens; c0 += chunk) {
         const int T = n_tokens - c0 < chunk ? n_tokens - c0 : chunk;
-        if ((rc = prefill_chunk(m, pos + c0, T))) return rc;
+        if ((rc = prefill_chunk(m, seq, pos + c0, T))) return rc;
         last = T - 1;
     }
     // classifier and next token for the last prompt token, as a decode step ends

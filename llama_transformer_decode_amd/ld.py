@@ -27,7 +27,7 @@ LD_OPT_NO_GRAPH = 1
 # Every symbol include/ld.h declares.
 EXPORTS = (
     "ld_weights_size", "ld_create", "ld_reset", "ld_forward", "ld_argmax_last", "ld_generate_greedy",
-    "ld_generate", "ld_prefill", "ld_forward_batch", "ld_generate_greedy_batch", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
+    "ld_generate", "ld_prefill", "ld_prefill_seq", "ld_forward_batch", "ld_generate_greedy_batch", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
     "ld_profile_steps", "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope",
     "ld_op_attention", "ld_op_gemm", "ld_op_attention_prefill", "ld_op_argmax", "ld_op_sample",
 )
@@ -90,6 +90,7 @@ def library():
             "ld_generate_greedy": ([_P, _I, _I, _I, _P], ctypes.c_int),
             "ld_generate": ([_P, _P, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I)], ctypes.c_int),
             "ld_prefill": ([_P, _P, _I, _I, ctypes.POINTER(_P)], ctypes.c_int),
+            "ld_prefill_seq": ([_P, _I, _P, _I, _I, ctypes.POINTER(_P)], ctypes.c_int),
             "ld_forward_batch": ([_P, _P, _P, _I, ctypes.POINTER(_P)], ctypes.c_int),
             "ld_generate_greedy_batch": ([_P, _P, _P, _I, _I, _P], ctypes.c_int),
             "ld_kv_cache": ([_P, ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t)],
@@ -219,6 +220,14 @@ def ld_generate_greedy_batch(h: int, tokens, pos, n_steps: int) -> np.ndarray:
                                               p.ctypes.data if p.size else None, t.size, n_steps, out.ctypes.data),
            "ld_generate_greedy_batch")
     return out[:t.size * n_steps].reshape(t.size, n_steps)
+
+
+def ld_prefill_seq(h: int, seq: int, tokens, pos: int) -> int:
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = _P()
+    _check(library().ld_prefill_seq(h, seq, t.ctypes.data if t.size else None, t.size, pos, ctypes.byref(out)),
+           "ld_prefill_seq")
+    return out.value
 
 
 def ld_kv_cache(h: int):

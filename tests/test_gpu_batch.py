@@ -130,3 +130,41 @@ def test_batch_range_errors():
     with pkg.Model(cfg, w) as m:  # max_batch 1
         with pytest.raises(ld.LdError):
             m.forward_batch([1, 2], [0, 0])
+
+
+@pytest.mark.parametrize("name", ["stories15m", "gqa_small"])
+def test_prompts_prefilled_per_sequence_then_decoded_as_a_batch(name):
+    # each sequence's prompt through ld_prefill_seq (lengths differ), then batched steps
+    cfg, blob, w = blob_of(name)
+    lengths = [37, 5, 64]
+    B = len(lengths)
+    prompts = [synth.prefill_tokens(cfg, 200)[10 * b:10 * b + n] for b, n in enumerate(lengths)]
+    caches, nexts = [], []
+    for pr in prompts:
+        c = oracle.KVCache(cfg)
+        for i, t in enumerate(pr):
+            lg = oracle.forward(cfg, blob, c, int(t), i)
+        caches.append(c)
+        nexts.append(oracle.argmax(lg))
+    with pkg.Model(cfg, w, max_batch=B) as m:
+        for b, pr in enumerate(prompts):
+            m.prefill(pr, 0, seq=b)
+        got = host(m.forward_batch(nexts, lengths))
+        k, _ = (host(t) for t in m.read_kv_cache())
+    for b in range(B):
+        ref = oracle.forward(cfg, blob, caches[b], nexts[b], lengths[b])
+        ok, err, tol = logits_close(got[b], ref)
+        assert ok, (b, err, tol)
+        n = lengths[b] + 1
+        scale = np.max(np.abs(caches[b].k[:, :n]))
+        assert np.max(np.abs(k[b][:, :n] - caches[b].k[:, :n])) <= 1e-4 * scale
+        assert np.all(k[b][:, n:] == 0)
+
+
+def test_prefill_seq_range():
+    cfg, blob, w = blob_of("tiny")
+    with pkg.Model(cfg, w, max_batch=2) as m:
+        for seq in (-1, 2):
+            with pytest.raises(ld.LdError) as e:
+                m.prefill([1, 2], 0, seq=seq)
+            assert e.value.status == ld.LD_E_RANGE
