@@ -63,8 +63,8 @@ def install(m, cfg, caches):
 
 
 @pytest.mark.parametrize("graph", [True, False])
-@pytest.mark.parametrize("name,lengths", [("tiny", [0, 5, 17, 40]), ("stories15m", [3, 0, 100, 31, 64]),
-                                          ("gqa_small", [200, 7, 0])])
+@pytest.mark.parametrize("name,lengths", [("tiny", [0, 5, 17, 40]), ("tiny", [60, 0, 59]),
+                                          ("stories15m", [3, 0, 100, 31, 64]), ("gqa_small", [200, 7, 0, 508])])
 def test_batch_steps_at_mixed_positions(name, lengths, graph):
     cfg, blob, w = blob_of(name)
     B = len(lengths)

@@ -286,3 +286,14 @@ def test_generate_range_errors():
         assert np.array_equal(got, [2, 3, 4, 5])
         # the model still works after the rejected calls
         assert m.generate_sampled([1], 0, 3, 0.0, 0.0, -1, None).size == 3
+
+
+def test_generation_up_to_the_last_position():
+    # the loop runs to the end of the cache; the last step's draw is still made
+    cfg, b, w = blob_of("tiny")
+    coins = synth.coins(cfg.seq_len, cfg.seed, 21)
+    with pkg.Model(cfg, w) as m:
+        got = m.generate_sampled([1, 9], 0, cfg.seq_len, 1.1, 0.8, -1, coins)
+    assert got.size == cfg.seq_len
+    matched, _ = compare_generation(cfg, b, got, [1, 9], 0, 1.1, 0.8, coins)
+    assert matched >= 1
