@@ -5,8 +5,9 @@ draws (ld_op_sample) and the prompt-forcing, stop-token generation loop
 A draw is a step function of the coin, so the device and the oracle agree
 except where the coin sits within rounding of a step.  The bar:
   * on the same logits, the device's token equals the oracle's, or equals the
-    oracle's for a coin (or topp) moved by at most 1e-5 (the device sums its
-    masses in double from fp32 numerators);
+    oracle's for a coin (or topp) moved by at most 1e-5 (the device sums fp32
+    numerators, 32 per thread in fp32 and across threads in double: a relative
+    error near 1e-6);
   * in a generation, whose logits differ from the oracle's by up to the decode
     step's parity bar (1e-4 * max |logit|), the coin moves by at most
     2 * (that bar) / temperature + 1e-5, the most the move of the logits can
