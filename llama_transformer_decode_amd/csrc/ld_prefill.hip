@@ -498,12 +498,19 @@ hipError_t gemm_launch_bm(int kind, const GemmParams& p, hipStream_t s) {
 // and for short prompts, 128 above.
 int gemm_tile_rows(int m) { return m <= 64 ? 32 : 128; }
 
+#ifndef LD_GEMM_SPLIT_BLOCKS
+#define LD_GEMM_SPLIT_BLOCKS 1024
+#endif
+#ifndef LD_GEMM_SPLIT_MINK
+#define LD_GEMM_SPLIT_MINK 256
+#endif
+
 int gemm_splits(int m, int n, int k) {
     const int bm = gemm_tile_rows(m);
     const long long tiles = (long long)((m + bm - 1) / bm) * ((n + kBN - 1) / kBN);
-    if (tiles >= 1024) return 1;
-    const int sp = (int)((1024 + tiles - 1) / tiles);
-    return max(1, min(sp, k / 256));
+    if (tiles >= LD_GEMM_SPLIT_BLOCKS) return 1;
+    const int sp = (int)((LD_GEMM_SPLIT_BLOCKS + tiles - 1) / tiles);
+    return max(1, min(sp, k / LD_GEMM_SPLIT_MINK));
 }
 
 // 32- or 128-row tiles (gemm_tile_rows); split K when a workspace is given
