@@ -124,7 +124,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=2, help="oracle decode steps timed for the CPU baseline")
+    ap.add_argument("--cpu-steps", type=int, default=4,
+                    help="oracle decode steps timed for the CPU baseline (about 13 s on the 7B shape)")
     ap.add_argument("--prefill-tokens", type=int, default=None,
                     help="prompt length of the timed batched prefill (default: the workload's prompt, else 2048; "
                          "0: skip)")
