@@ -12,6 +12,12 @@
  * pos) returns logits, and the greedy loop is the generate loop of "run.c"
  * at temperature 0.
  *
+ * Around that step: the generation loop with temperature / top-p sampling,
+ * prompt forcing and a stop token ("run.c 逐行解讀" §6-§7, ld_generate), a
+ * prompt prefilled in one pass (ld_prefill), and several sequences decoded
+ * per step, each on its own KV cache (ld_forward_batch,
+ * ld_generate_greedy_batch).
+ *
  * Conventions for every call:
  *   - Every call returns an int status: LD_OK (0) or a negative LD_E_* code.
  *     No call aborts the process or lets a C++ exception escape.
@@ -106,7 +112,8 @@ int ld_weights_size(const ld_config* cfg, const ld_options* opt, size_t* bytes_o
 int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights, size_t bytes,
               void* hip_stream, ld_model** out);
 
-/* Zero both KV caches (the calloc'd state of the pages).  Asynchronous. */
+/* Zero the KV caches of every sequence (the calloc'd state of the pages).
+ * Asynchronous. */
 int ld_reset(ld_model* m);
 
 /* One decode step at (token, pos): writes KV-cache row pos of every layer,
