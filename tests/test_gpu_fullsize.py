@@ -12,7 +12,9 @@ Same bar as everywhere: max |d logit| <= 1e-4 * max |logit|.
 Prompt prefill is checked at these sizes too: three tokens at once after an
 installed prefix against the oracle, and a long prompt (512 / 1024 tokens)
 against the same prompt decoded one token at a time on the GPU, whose steps
-the checks above tie to the oracle.
+the checks above tie to the oracle.  So are a batched step of sequences at
+different positions and the sampling generation loop (a forced token, then
+top-p draws) after an installed prefix.
 """
 import numpy as np
 import pytest
@@ -167,3 +169,29 @@ def test_batch_step_at_full_size(big):
         print(f"[{cfg.name}] batch row {b} at {lengths[b]}: max |d logit| {err:.3g} (tolerance {tol:.3g})",
               flush=True)
         assert ok
+
+
+def test_sampled_steps_at_full_size(big):
+    # the generation loop with a forced token and two top-p draws after an installed prefix
+    cfg, blob, w = big
+    import torch
+    p0 = {"llama7b": 900, "llama70b_8l": 3000}[cfg.name]
+    cache = _prefix(cfg, p0, 1300)
+    prompt = [int(t) for t in synth.prefill_tokens(cfg, p0 + 2)[p0:]]
+    coins = synth.coins(3, cfg.seed, 31)
+    with pkg.Model(cfg, w) as m:
+        m.write_kv_cache(torch.from_numpy(cache.k).cuda(), torch.from_numpy(cache.v).cuda())
+        got = m.generate_sampled(prompt, p0, 3, 0.9, 0.9, -1, coins)
+    assert got.size == 3 and got[0] == prompt[1]
+    tok = prompt[0]
+    for i in range(3):
+        logits = oracle.forward(cfg, blob, cache, tok, p0 + i)
+        if i >= 1:
+            want = oracle.sample(logits, 0.9, 0.9, float(coins[i]))
+            if got[i] != want:  # a coin within the generation bar of a step: both draws are right
+                bar = 1e-4 * float(np.max(np.abs(logits)))
+                d = 2 * bar / 0.9 + 1e-5
+                assert any(got[i] == oracle.sample(logits, 0.9, 0.9 + dp, min(max(float(coins[i]) + dc, 0.0), 0.99999994))
+                           for dc in np.linspace(-d, d, 21) for dp in (-d, 0.0, d))
+                break
+        tok = int(got[i])
