@@ -142,7 +142,9 @@ struct GemmParams {
     const StepState* row_state;  // G_QKV of a decode batch: row m is sequence m at row_state[m].pos
     size_t seq_stride;           //   floats between two sequences' caches
     float* part;                 // workspace for split-K partials (NULL: no split)
-    size_t part_floats;
+    size_t part_floats;          //   at least gemm_part_floats(m, n, k)
+    const float* gain;           // non-NULL: C = RMSNorm(A) B^T, the norm with this gain
+    float eps;                   //   (over the K columns of each row of A) and eps
     int splits;                  // set by the launcher
     int kchunk;
 };
@@ -169,7 +171,8 @@ hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* 
                               int tokens_stride, hipStream_t s);
 hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s);
 hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s);
-int gemm_splits(int m, int n, int k);  // K splits the launcher uses for m rows (workspace: splits * m * n floats)
+int gemm_splits(int m, int n, int k);  // K splits the launcher uses for m rows
+size_t gemm_part_floats(int m, int n, int k);  // split workspace: splits * m * (n + 1) floats
 bool attn_prefill_supported(int head_size);
 hipError_t attn_prefill_launch(int head_size, const AttnPrefillParams& p, hipStream_t s);
 

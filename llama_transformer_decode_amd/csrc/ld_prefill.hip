@@ -5,7 +5,8 @@
 // used T times, so the projections are dense fp32 contractions
 // (2 flops per weight per token) and run on the matrix cores:
 //
-//   gemm_kernel     C(T x N) = A(T x K) * B(N x K)^T with v_mfma_f32_32x32x2f32,
+//   gemm_kernel     C(T x N) = A(T x K) * B(N x K)^T with v_mfma_f32_32x32x2f32
+//                   (or 16x16x4f32 for batches of up to 16 decode steps),
 //                   epilogues: plain store, residual add, RoPE + cache append,
 //                   SwiGLU (the same epilogues as the decode GEMVs)
 //   attn_prefill    causal grouped-query attention of T queries over the
@@ -70,29 +71,39 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // C = A * B^T on the matrix cores.
 //
-// A block of 256 threads computes a BM x 128 tile of C with
-// v_mfma_f32_32x32x2f32 (4 waves; BM = 128 for prompts, 32 for a batch of
-// decode steps, see gemm_kernel).  K is walked in slabs of BK (16 or 32):
-// both operand slabs go global -> registers -> LDS (row-major, K contiguous,
-// rows padded by 4 floats), double-buffered with one barrier per slab; the
-// next slab's global loads are in flight while the current one is
-// multiplied.  Within a slab, the MFMA's two k positions of step s are taken
-// as k = (BK/2) h + s (lane half h), so each lane reads BK/2 consecutive
-// floats of its row with 16-byte LDS loads; every k is still used exactly
-// once.  Rows of A past M and of B past N are clamped (their results are not
-// stored); k past the end reads as zero.
+// A block of 256 threads (4 waves) computes a BM x 128 tile of C on the
+// matrix cores (BM and the MFMA shape per product, see gemm_kernel).  K is
+// walked in slabs of BK (16 or 32): both operand slabs go global -> registers
+// -> LDS (row-major, K contiguous, rows padded by 4 floats), double-buffered
+// with one barrier per slab, while the next slabs' global loads are in
+// flight.  Within a slab, lane group g of an MFMA step supplies k position
+// HK g + s at step s (HK = BK / lane groups), so each lane reads HK
+// consecutive floats of its row with 16-byte LDS loads; every k is still used
+// exactly once.  Rows of A past M and of B past N are clamped (their results
+// are not stored); k past the end reads as zero.
 
 constexpr int kBN = 128, kGemmThreads = 256;
 
-// K slab depth per row tile (16 or 32): prompts gain about 2% from 32 (fewer
-// barriers per flop); decode batches, bound by the weight stream, run faster
-// with 16 (measured on the 7B shape: 242 vs 247 ms for a 2048-token prompt,
-// 7.6 vs 8.1 ms per batch-of-one step).
+// K slab depth and slabs in flight per row tile.  Prompts (BM = 128) gain
+// about 2% from BK = 32 (fewer barriers per flop).  Decode batches, bound by
+// the weight stream, run faster with 2 slabs in flight, and with BK = 32 for
+// the 16- and 32-row tiles (a whole 128-byte line of each weight row per
+// slab) but 16 for the 64-row tile (measured on the 7B shape: 6.8 vs 7.2 ms
+// per step at 16 rows, 8.0 vs 8.1 at 32, 11.5 vs 12.3 at 64).
 #ifndef LD_GEMM_BK128
 #define LD_GEMM_BK128 32
 #endif
-#ifndef LD_GEMM_BK32
-#define LD_GEMM_BK32 16
+#ifndef LD_GEMM_BK_M16
+#define LD_GEMM_BK_M16 32
+#endif
+#ifndef LD_GEMM_BK_M32
+#define LD_GEMM_BK_M32 32
+#endif
+#ifndef LD_GEMM_BK_M64
+#define LD_GEMM_BK_M64 16
+#endif
+#ifndef LD_GEMM_R_BATCH
+#define LD_GEMM_R_BATCH 2
 #endif
 
 template <int KIND>
@@ -106,10 +117,30 @@ __device__ __forceinline__ const float* b_row(const GemmParams& p, int r) {
     return p.w0 + (size_t)r * p.k;
 }
 
-// 4 floats of a row at k (zero from kend on; the address stays inside the row)
-__device__ __forceinline__ float4 load_k4(const float* row, int k, int kend, int K) {
-    const float4 v = *reinterpret_cast<const float4*>(row + min(k, K - 4));
-    return k < kend ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}  // namespace
+
+// Zeros read in place of k past the end of a product's K, and ones in place of
+// an RMSNorm gain where there is none.  Never written; their external linkage
+// keeps the compiler from folding their values.
+__device__ __attribute__((aligned(16))) float gemm_zero4[4];
+__device__ __attribute__((aligned(16))) float gemm_one4[4] = {1.f, 1.f, 1.f, 1.f};
+
+namespace {
+
+// 4 floats of a row at k, zero from kend on.  Past the end the load takes the
+// address of gemm_zero4 instead of selecting on the loaded value: with a
+// select the compiler turns the load into a branch, and a load that may not
+// have been issued makes every later wait one for all loads in flight.
+__device__ __forceinline__ float4 load_k4(const float* row, int k, int kend) {
+    const float* a = k < kend ? row + k : gemm_zero4;
+    return *reinterpret_cast<const float4*>(a);
+}
+
+// 4 gains at k (clamped to the last 4 of K: past the end the A values they
+// scale are zero); ones without a gain
+__device__ __forceinline__ float4 load_gain4(const float* gain, int k, int K) {
+    const float* a = gain ? gain + min(k, K - 4) : gemm_one4;
+    return *reinterpret_cast<const float4*>(a);
 }
 
 // Blocks are dealt to the 8 XCDs round-robin; renumber them so that each XCD
@@ -158,20 +189,65 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int gm, int gn, fl
     }
 }
 
-// BM = 128 rows (prompt prefill): 2 x 2 waves of 64 x 64.  BM = 32 rows
-// (a batch of decode steps, where the weight stream is the cost): 1 x 4
-// waves of 32 x 32, a quarter of the matrix-core work per weight byte.
-template <int KIND, int BM, int BK>
+// Matrix-core shapes: MT = 32 is v_mfma_f32_32x32x2f32 (k advances 2 per
+// step), MT = 16 is v_mfma_f32_16x16x4f32 (k advances 4).  Lane l supplies
+// row l % MT of A and of B; the G = 64 / MT lane groups supply the step's k
+// positions.
+template <int MT>
+struct Mfma;
+template <>
+struct Mfma<32> {
+    typedef v16f acc;
+    static __device__ __forceinline__ acc step(float a, float b, acc c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    // row of register r in lane group g (the column is l % 32)
+    static __device__ __forceinline__ int row(int r, int g) { return (r >> 2) * 8 + g * 4 + (r & 3); }
+};
+template <>
+struct Mfma<16> {
+    typedef v4f acc;
+    static __device__ __forceinline__ acc step(float a, float b, acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ int row(int r, int g) { return g * 4 + r; }
+};
+
+// Tiles: BM = 128 rows (prompt prefill), 2 x 2 waves of 64 x 64 with MT = 32.
+// A decode batch, where the weight stream is the cost, takes the smallest
+// tile that holds its rows: BM = 16 (1 x 4 waves of 16 x 32, MT = 16), 32
+// (1 x 4 waves of 32 x 32) or 64 (2 x 2 waves of 32 x 64).  The matrix-core
+// work per weight byte grows with BM: at BM = 32 streaming the weights at
+// 8 TB/s would keep the fp32 matrix cores 80% busy, at BM = 16 40%.
+//
+// Pipeline: R register sets hold the next R slabs' global loads, so R slabs
+// per block are in flight while slab kt is multiplied out of LDS; at the end
+// of iteration kt the set holding slab kt+1 goes to the other LDS buffer and
+// is refilled with slab kt+1+R.
+//
+// NORM: C = RMSNorm(A) B^T with the gain p.gain ("run.c 逐行解讀" §4, the
+// rmsnorm before the q/k/v and w1/w3 products and the classifier).  The norm's
+// row scale is a common factor of a row of C, so A is multiplied by the gain
+// on its way to LDS, the blocks accumulate each row's sum of squares from the
+// same A values, and the scale 1/sqrt(mean(a^2) + eps) multiplies the row's
+// products before the epilogue: here when the block holds all of K, in
+// gemm_reduce_kernel (which sums the squares' split partials too) otherwise.
+template <int KIND, int BM, int BK, int MT, int R, bool NORM>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
-    constexpr int WAVES_M = BM == 128 ? 2 : 1, WAVES_N = 4 / WAVES_M;
-    constexpr int TM = BM / (32 * WAVES_M), TN = kBN / (32 * WAVES_N);  // 32 x 32 tiles per wave
+    constexpr int WAVES_M = BM / MT >= 2 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+    constexpr int TM = BM / (MT * WAVES_M), TN = kBN / (MT * WAVES_N);  // MT x MT tiles per wave
+    constexpr int G = 64 / MT;                                           // lane groups (k per step)
+    constexpr int HK = BK / G;                                           // k per lane and slab
+    constexpr int NR = MT * MT / 64;                                     // accumulator registers per tile
     constexpr int ROW = BK + 4;                                          // padded LDS row
     constexpr int Q4 = BK / 4;                                           // float4 per row and slab
     constexpr int A_PER = (BM * Q4 + kGemmThreads - 1) / kGemmThreads;  // A float4 loads per thread and slab
     constexpr int B_PER = kBN * Q4 / kGemmThreads;
-    constexpr int HK = BK / 2;                                           // k per lane half and slab
+    static_assert(HK % 4 == 0 && TM >= 1 && TN >= 1, "tile shape");
+    typedef typename Mfma<MT>::acc acc_t;
     __shared__ __attribute__((aligned(16))) float As[2][BM][ROW];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBN][ROW];
+    __shared__ float row_scale[NORM ? BM : 1];
 
     const int mtiles = (p.m + BM - 1) / BM;
     const int lb = xcd_local_block(blockIdx.x, gridDim.x);
@@ -179,8 +255,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
     const int m0 = (tile % mtiles) * BM, n0 = (tile / mtiles) * kBN;
     const int kbeg = ks * p.kchunk, kend = min(p.k, kbeg + p.kchunk);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 31, lh = lane >> 5;
-    const int wm = (wave % WAVES_M) * (TM * 32), wn = (wave / WAVES_M) * (TN * 32);
+    const int li = lane % MT, lg = lane / MT;
+    const int wm = (wave % WAVES_M) * (TM * MT), wn = (wave / WAVES_M) * (TN * MT);
 
     // this thread's rows and k quads of every slab: float4 number q of a slab is
     // row q / Q4, k 4 (q % Q4)
@@ -205,73 +281,114 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
         brow[i] = b_row<KIND>(p, min(n0 + blrow[i], p.n - 1));
     }
 
-    v16f acc[TM][TN];
+    acc_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = (kend - kbeg + BK - 1) / BK;
-    float4 ra[A_PER], rb[B_PER];
+    // register sets: A, its gains (NORM), B
+    constexpr int GS = NORM ? R : 1, GP = NORM ? A_PER : 1;
+    float4 ra[R][A_PER], rg[GS][GP], rb[R][B_PER];
+    float sq[A_PER];  // NORM: this thread's part of its A rows' sums of squares
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) ra[i] = load_k4(arow[i], kbeg + alk[i], kend, p.k);
+    for (int i = 0; i < A_PER; ++i) sq[i] = 0.f;
+    auto load_slab = [&](float4(&xa)[A_PER], float4(&xg)[GP], float4(&xb)[B_PER], int k) {
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) rb[i] = load_k4(brow[i], kbeg + blk[i], kend, p.k);
+        for (int i = 0; i < A_PER; ++i) xa[i] = load_k4(arow[i], k + alk[i], kend);
+        if constexpr (NORM) {
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-        if (aon[i]) *reinterpret_cast<float4*>(&As[0][alrow[i]][alk[i]]) = ra[i];
+            for (int i = 0; i < A_PER; ++i) xg[i] = load_gain4(p.gain, k + alk[i], p.k);
+        }
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) *reinterpret_cast<float4*>(&Bs[0][blrow[i]][blk[i]]) = rb[i];
+        for (int i = 0; i < B_PER; ++i) xb[i] = load_k4(brow[i], k + blk[i], kend);
+    };
+    auto store_slab = [&](const float4(&xa)[A_PER], const float4(&xg)[GP], const float4(&xb)[B_PER], int buf) {
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            float4 v = xa[i];
+            if constexpr (NORM) {
+                sq[i] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+                const float4 g = xg[i];
+                v = make_float4(g.x * v.x, g.y * v.y, g.z * v.z, g.w * v.w);
+            }
+            if (aon[i]) *reinterpret_cast<float4*>(&As[buf][alrow[i]][alk[i]]) = v;
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) *reinterpret_cast<float4*>(&Bs[buf][blrow[i]][blk[i]]) = xb[i];
+    };
+
+    // slabs of this split, rounded up to a whole number of register-set turns
+    // (the extra slabs read zeros and add nothing), so that no load or store
+    // of the loop sits behind a branch
+    const int nk = ((kend - kbeg + BK - 1) / BK + R - 1) / R * R;
+#pragma unroll
+    for (int s = 0; s < R; ++s) load_slab(ra[s], rg[s % GS], rb[s], kbeg + s * BK);
+    store_slab(ra[0], rg[0], rb[0], 0);
+    load_slab(ra[0], rg[0], rb[0], kbeg + R * BK);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int k = kbeg + (kt + 1) * BK;
+    for (int kt0 = 0; kt0 < nk; kt0 += R) {
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i) ra[i] = load_k4(arow[i], k + alk[i], kend, p.k);
-#pragma unroll
-            for (int i = 0; i < B_PER; ++i) rb[i] = load_k4(brow[i], k + blk[i], kend, p.k);
-        }
-        // the MFMA's two k positions of step s are k = HK h + s (lane half h):
-        // each lane reads HK consecutive floats of its row
-        float av[TM][HK], bv[TN][HK];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int q = 0; q < HK; q += 4) {
-                const float4 x = *reinterpret_cast<const float4*>(&As[buf][wm + i * 32 + li][lh * HK + q]);
-                av[i][q] = x.x; av[i][q + 1] = x.y; av[i][q + 2] = x.z; av[i][q + 3] = x.w;
-            }
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < HK; q += 4) {
-                const float4 y = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * 32 + li][lh * HK + q]);
-                bv[j][q] = y.x; bv[j][q + 1] = y.y; bv[j][q + 2] = y.z; bv[j][q + 3] = y.w;
-            }
-#pragma unroll
-        for (int st = 0; st < HK; ++st)
+        for (int u = 0; u < R; ++u) {
+            const int kt = kt0 + u;
+            const int buf = kt & 1;
+            // the MFMA's k positions of step s are k = HK g + s (lane group
+            // g): each lane reads HK consecutive floats of its row
+            float av[TM][HK], bv[TN][HK];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[i][st], bv[j][st], acc[i][j], 0, 0, 0);
-        if (more) {
+                for (int q = 0; q < HK; q += 4) {
+                    const float4 x = *reinterpret_cast<const float4*>(&As[buf][wm + i * MT + li][lg * HK + q]);
+                    av[i][q] = x.x; av[i][q + 1] = x.y; av[i][q + 2] = x.z; av[i][q + 3] = x.w;
+                }
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i)
-                if (aon[i]) *reinterpret_cast<float4*>(&As[buf ^ 1][alrow[i]][alk[i]]) = ra[i];
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) *reinterpret_cast<float4*>(&Bs[buf ^ 1][blrow[i]][blk[i]]) = rb[i];
+                for (int q = 0; q < HK; q += 4) {
+                    const float4 y = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * MT + li][lg * HK + q]);
+                    bv[j][q] = y.x; bv[j][q + 1] = y.y; bv[j][q + 2] = y.z; bv[j][q + 3] = y.w;
+                }
+#pragma unroll
+            for (int st = 0; st < HK; ++st)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<MT>::step(av[i][st], bv[j][st], acc[i][j]);
+            // slab kt+1 to the other buffer (read in the previous iteration,
+            // before the barrier), then its register set takes slab kt+1+R;
+            // in the last iteration both only touch zeros
+            store_slab(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], buf ^ 1);
+            load_slab(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], kbeg + (kt + 1 + R) * BK);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
-    // Epilogue.  Register r of tile (i, j) holds C(row, col) with
-    // row = wm + 32i + 8(r/4) + 4h + r%4 and col = wn + 32j + (lane % 32):
+    if constexpr (NORM) {
+        // the Q4 consecutive lanes of an A row hold its sum of squares over
+        // this split's k in parts; the first column tile publishes them
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) {
+            float v = sq[i];
+#pragma unroll
+            for (int o = 1; o < Q4; o <<= 1) v += __shfl_xor(v, o);
+            const int q = tid + kGemmThreads * i, gm = m0 + alrow[i];
+            if (aon[i] && q % Q4 == 0) {
+                if (p.splits > 1) {
+                    if (n0 == 0 && gm < p.m) p.part[(size_t)p.splits * p.m * p.n + (size_t)ks * p.m + gm] = v;
+                } else {
+                    row_scale[alrow[i]] = 1.0f / sqrtf(v / (float)p.k + p.eps);
+                }
+            }
+        }
+        if (p.splits == 1) __syncthreads();
+    }
+
+    // Epilogue.  Register r of tile (i, j) in lane group g holds C(row, col)
+    // with row = wm + MT i + Mfma<MT>::row(r, g) and col = wn + MT j + l % MT:
     // lanes 2c and 2c+1 hold the adjacent columns (2c, 2c+1) of one row, the
     // pair RoPE rotates and the (w1, w3) pair SwiGLU combines.  With split K
     // the block stores its partial tile instead; gemm_reduce_kernel sums the
@@ -281,10 +398,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = m0 + wm + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-                const int gn = n0 + wn + j * 32 + li;
-                const float v = acc[i][j][r];
+            for (int r = 0; r < NR; ++r) {
+                const int gm = m0 + wm + i * MT + Mfma<MT>::row(r, lg);
+                const int gn = n0 + wn + j * MT + li;
+                float v = acc[i][j][r];
+                if constexpr (NORM) {
+                    if (p.splits == 1) v *= row_scale[gm - m0];
+                }
                 if (p.splits > 1) {
                     if (gm < p.m && gn < p.n) p.part[((size_t)ks * p.m + gm) * p.n + gn] = v;
                     continue;
@@ -295,7 +415,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
 }
 
 // Sum of the split partials of C, in split order, then the epilogue: one
-// thread per (row, column pair).
+// thread per (row, column pair).  The loads of 8 splits are issued before
+// their sums.  With a norm gain the row's sum of squares is summed the same
+// way and its scale multiplies the two sums.
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
     const int pairs = (p.n + 1) / 2;
@@ -303,12 +425,38 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
     if (e >= (long long)p.m * pairs) return;
     const int gm = (int)(e / pairs), c = (int)(e % pairs), gn = 2 * c;
     const bool two = gn + 1 < p.n;
-    float v0 = 0.f, v1 = 0.f;
     const size_t stride = (size_t)p.m * p.n;
     const float* src = p.part + (size_t)gm * p.n + gn;
-    for (int ks = 0; ks < p.splits; ++ks) {
+    const int d1 = two ? 1 : 0;  // without a second column v1 is never used
+    const float* sqs = p.gain ? p.part + (size_t)p.splits * stride + gm : src;
+    const size_t sq_stride = p.gain ? (size_t)p.m : stride;
+    float v0 = 0.f, v1 = 0.f, ss = 0.f;
+    constexpr int U = 8;
+    int ks = 0;
+    for (; ks + U <= p.splits; ks += U) {
+        float a[U], b[U], q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = src[(ks + u) * stride];
+            b[u] = src[(ks + u) * stride + d1];
+            q[u] = sqs[(ks + u) * sq_stride];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            v0 += a[u];
+            v1 += b[u];
+            ss += q[u];
+        }
+    }
+    for (; ks < p.splits; ++ks) {
         v0 += src[ks * stride];
-        if (two) v1 += src[ks * stride + 1];
+        v1 += src[ks * stride + d1];
+        ss += sqs[ks * sq_stride];
+    }
+    if (p.gain) {
+        const float r = 1.0f / sqrtf(ss / (float)p.k + p.eps);
+        v0 *= r;
+        v1 *= r;
     }
     epilogue<KIND>(p, gm, gn, v0, v1);
     if (two) epilogue<KIND>(p, gm, gn + 1, v1, v0);
@@ -461,18 +609,26 @@ hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t,
 
 namespace {
 
-template <int BM, int BK>
+template <int BM, int BK, int MT, int R, bool NORM>
+void gemm_launch_kind(int kind, const GemmParams& p, dim3 grid, dim3 block, hipStream_t s) {
+    switch (kind) {
+        case G_PLAIN: hipLaunchKernelGGL((gemm_kernel<G_PLAIN, BM, BK, MT, R, NORM>), grid, block, 0, s, p); break;
+        case G_RESID: hipLaunchKernelGGL((gemm_kernel<G_RESID, BM, BK, MT, R, NORM>), grid, block, 0, s, p); break;
+        case G_QKV: hipLaunchKernelGGL((gemm_kernel<G_QKV, BM, BK, MT, R, NORM>), grid, block, 0, s, p); break;
+        case G_SWIGLU: hipLaunchKernelGGL((gemm_kernel<G_SWIGLU, BM, BK, MT, R, NORM>), grid, block, 0, s, p); break;
+    }
+}
+
+template <int BM, int BK, int MT, int R>
 hipError_t gemm_launch_bm(int kind, const GemmParams& p, hipStream_t s) {
     const long long blocks = (long long)((p.m + BM - 1) / BM) * ((p.n + kBN - 1) / kBN) * p.splits;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
+    if (kind != G_PLAIN && kind != G_RESID && kind != G_QKV && kind != G_SWIGLU) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks), block(kGemmThreads);
-    switch (kind) {
-        case G_PLAIN: hipLaunchKernelGGL((gemm_kernel<G_PLAIN, BM, BK>), grid, block, 0, s, p); break;
-        case G_RESID: hipLaunchKernelGGL((gemm_kernel<G_RESID, BM, BK>), grid, block, 0, s, p); break;
-        case G_QKV: hipLaunchKernelGGL((gemm_kernel<G_QKV, BM, BK>), grid, block, 0, s, p); break;
-        case G_SWIGLU: hipLaunchKernelGGL((gemm_kernel<G_SWIGLU, BM, BK>), grid, block, 0, s, p); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (p.gain)
+        gemm_launch_kind<BM, BK, MT, R, true>(kind, p, grid, block, s);
+    else
+        gemm_launch_kind<BM, BK, MT, R, false>(kind, p, grid, block, s);
     if (p.splits > 1) {
         const long long threads = (long long)p.m * ((p.n + 1) / 2);
         const dim3 rgrid((unsigned)((threads + 255) / 256));
@@ -488,16 +644,16 @@ hipError_t gemm_launch_bm(int kind, const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Row tile of a product of m rows: the smallest of 16, 32, 64 that holds a
+// decode batch (m <= 64, where the weight stream is the cost and the
+// matrix-core work per weight byte grows with the tile), 128 above.
+int gemm_tile_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
+
 // Splits of K for a product with few row tiles (a decode batch): with whole K
 // each block would stream its weight rows alone, and a few hundred blocks
 // leave most of the chip idle; splitting K gives about 1024 blocks (at least
 // 256 of K each), so every CU has several weight streams in flight.  Used
 // only where the caller provides the partials' workspace.
-// Row tile of a product of m rows: 32 for a decode batch (m <= 64, where the
-// weight stream is the cost and a 128-row tile would be matrix-core bound)
-// and for short prompts, 128 above.
-int gemm_tile_rows(int m) { return m <= 64 ? 32 : 128; }
-
 #ifndef LD_GEMM_SPLIT_BLOCKS
 #define LD_GEMM_SPLIT_BLOCKS 1024
 #endif
@@ -513,7 +669,14 @@ int gemm_splits(int m, int n, int k) {
     return max(1, min(sp, k / LD_GEMM_SPLIT_MINK));
 }
 
-// 32- or 128-row tiles (gemm_tile_rows); split K when a workspace is given
+// the product partials (splits x m x n) and the row sums of squares of a
+// normed product (splits x m)
+size_t gemm_part_floats(int m, int n, int k) {
+    const int sp = gemm_splits(m, n, k);
+    return sp > 1 ? (size_t)sp * m * (n + 1) : 0;
+}
+
+// Tiles of gemm_tile_rows rows; split K when a workspace is given
 hipError_t gemm_launch(int kind, const GemmParams& p0, hipStream_t s) {
     GemmParams p = p0;
     if (p.m <= 0 || p.n <= 0 || p.k < 4 || (p.k % 4)) return hipErrorInvalidValue;
@@ -521,9 +684,13 @@ hipError_t gemm_launch(int kind, const GemmParams& p0, hipStream_t s) {
     const int chunk = (p.k + p.splits - 1) / p.splits;
     p.kchunk = (chunk + 31) / 32 * 32;  // a whole number of slabs of either depth
     p.splits = (p.k + p.kchunk - 1) / p.kchunk;
-    if (p.splits > 1 && (size_t)p.splits * p.m * p.n > p.part_floats) return hipErrorInvalidValue;
-    return gemm_tile_rows(p.m) == 32 ? gemm_launch_bm<32, LD_GEMM_BK32>(kind, p, s)
-                                     : gemm_launch_bm<128, LD_GEMM_BK128>(kind, p, s);
+    if (p.splits > 1 && (size_t)p.splits * p.m * (p.n + 1) > p.part_floats) return hipErrorInvalidValue;
+    switch (gemm_tile_rows(p.m)) {
+        case 16: return gemm_launch_bm<16, LD_GEMM_BK_M16, 16, LD_GEMM_R_BATCH>(kind, p, s);
+        case 32: return gemm_launch_bm<32, LD_GEMM_BK_M32, 32, LD_GEMM_R_BATCH>(kind, p, s);
+        case 64: return gemm_launch_bm<64, LD_GEMM_BK_M64, 32, LD_GEMM_R_BATCH>(kind, p, s);
+    }
+    return gemm_launch_bm<128, LD_GEMM_BK128, 32, 1>(kind, p, s);
 }
 
 bool attn_prefill_supported(int hs) {

@@ -130,7 +130,7 @@ struct ld_model {
     // (max_batch, L, S, kv_dim)), their activations, states and tokens, and
     // one captured graph per batch size
     int max_batch = 1;
-    float *bx = nullptr, *bxn = nullptr, *bq = nullptr, *batt = nullptr, *bhb = nullptr, *blogits = nullptr;
+    float *bx = nullptr, *bq = nullptr, *batt = nullptr, *bhb = nullptr, *blogits = nullptr;
     float2* bpart_ml = nullptr;
     float* bpart_acc = nullptr;
     float* bsplit = nullptr;         // split-K partials of the batch products
@@ -498,8 +498,8 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
 
 // One decode step of sequences 0..n-1 of the batch, each reading (token, pos)
 // from m->bstate[b]: the single step's sequence of operations with the weight
-// matrices as 32-row matrix-core products, so every weight is read once for
-// the whole batch.
+// matrices as matrix-core products of n rows (each RMSNorm fused into the
+// product it feeds), so every weight is read once for the whole batch.
 int launch_batch_step(ld_model* m, int n) {
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
@@ -507,10 +507,11 @@ int launch_batch_step(ld_model* m, int n) {
     hipStream_t s = m->stream;
     HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s));
     for (int l = 0; l < c.n_layers; ++l) {
-        HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_att + (size_t)l * d, m->opt.norm_eps, n, c.dim, m->bxn, s));
         {
             GemmParams g{};
-            g.a = m->bxn;
+            g.a = m->bx;
+            g.gain = m->rms_att + (size_t)l * d;
+            g.eps = m->opt.norm_eps;
             g.lda = c.dim;
             g.m = n;
             g.part = m->bsplit;
@@ -565,10 +566,11 @@ int launch_batch_step(ld_model* m, int n) {
             g.ldo = c.dim;
             HIP_TRY(gemm_launch(G_RESID, g, s));
         }
-        HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_ffn + (size_t)l * d, m->opt.norm_eps, n, c.dim, m->bxn, s));
         {
             GemmParams g{};
-            g.a = m->bxn;
+            g.a = m->bx;
+            g.gain = m->rms_ffn + (size_t)l * d;
+            g.eps = m->opt.norm_eps;
             g.lda = c.dim;
             g.m = n;
             g.part = m->bsplit;
@@ -596,10 +598,11 @@ int launch_batch_step(ld_model* m, int n) {
             HIP_TRY(gemm_launch(G_RESID, g, s));
         }
     }
-    HIP_TRY(rmsnorm_rows_launch(m->bx, m->rms_final, m->opt.norm_eps, n, c.dim, m->bxn, s));
     {
         GemmParams g{};
-        g.a = m->bxn;
+        g.a = m->bx;
+        g.gain = m->rms_final;
+        g.eps = m->opt.norm_eps;
         g.lda = c.dim;
         g.m = n;
         g.part = m->bsplit;
@@ -773,7 +776,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (rc) break;
         {  // batch buffers (also for max_batch 1, so a batch of one runs)
             const size_t B = m->max_batch;
-            if ((rc = dalloc(m, &m->bx, B * d)) || (rc = dalloc(m, &m->bxn, B * d)) || (rc = dalloc(m, &m->bq, B * d)) ||
+            if ((rc = dalloc(m, &m->bx, B * d)) || (rc = dalloc(m, &m->bq, B * d)) ||
                 (rc = dalloc(m, &m->batt, B * d)) || (rc = dalloc(m, &m->bhb, B * h)) ||
                 (rc = dalloc(m, &m->blogits, B * V)) ||
                 (rc = dalloc(m, &m->bpart_ml, B * cfg->n_heads * m->nsplit)) ||
@@ -787,7 +790,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             size_t ws = 0;
             for (int nb = 1; nb <= m->max_batch; ++nb)
                 for (const auto& sh : shapes) {
-                    const size_t need = (size_t)gemm_splits(nb, sh[0], sh[1]) * nb * sh[0];
+                    const size_t need = gemm_part_floats(nb, sh[0], sh[1]);
                     if (need > ws) ws = need;
                 }
             m->bsplit_floats = ws;
@@ -1334,11 +1337,8 @@ int ld_op_gemm(const float* d_a, const float* d_w, int32_t m, int32_t n, int32_t
     g.ldo = n;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     Temps tmp;
-    const int splits = gemm_splits(m, n, k);
-    if (splits > 1) {  // split K, as a decode batch runs it
-        g.part_floats = (size_t)splits * m * n;
-        HIP_TRY(tmp.get(&g.part, g.part_floats));
-    }
+    g.part_floats = gemm_part_floats(m, n, k);
+    if (g.part_floats) HIP_TRY(tmp.get(&g.part, g.part_floats));  // split K, as a decode batch runs it
     HIP_TRY(gemm_launch(G_PLAIN, g, s));
     HIP_TRY(hipStreamSynchronize(s));
     return LD_OK;

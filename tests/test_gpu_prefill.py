@@ -43,7 +43,9 @@ def gemm(a, w):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 4), (3, 5, 8), (128, 128, 16), (129, 130, 20), (200, 300, 100),
-                                   (17, 1000, 36), (64, 1536, 288), (256, 1024, 4096), (5, 64, 176)])
+                                   (17, 1000, 36), (64, 1536, 288), (256, 1024, 4096), (5, 64, 176),
+                                   # each row tile (16, 32, 64) with K split, ragged slabs and tails
+                                   (16, 1000, 1028), (32, 520, 2052), (33, 300, 1000), (63, 260, 772)])
 def test_gemm_exact_on_small_integers(m, n, k):
     rng = np.random.default_rng(m * 1000 + n + k)
     a = rng.integers(-4, 5, (m, k)).astype(np.float32)
