@@ -124,6 +124,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain streaming read that measures the practical HBM read ceiling")
     ap.add_argument("--cpu-steps", type=int, default=4,
                     help="oracle decode steps timed for the CPU baseline (about 13 s on the 7B shape)")
     ap.add_argument("--prefill-tokens", type=int, default=None,
@@ -329,24 +331,65 @@ def main() -> int:
     del weights
     torch.cuda.empty_cache()
 
+    # ---- the practical read ceiling: a plain streaming read, same run, same stream timing ----
+    ceiling = None
+    if not args.no_read_ceiling:
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        sums = torch.empty(pkg.ld.LD_STREAM_READ_BLOCKS, dtype=torch.float32, device="cuda:0")
+        st = torch.cuda.current_stream()
+        for _ in range(3):
+            pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+        reps, dts = 10, []
+        for _ in range(3):  # the best of 3 rounds of 10 reads: the ceiling is what the read can reach
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+            e1.record(st)
+            torch.cuda.synchronize()
+            dts.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        dt = min(dts)
+        c_gbps = nbytes / dt / 1e9
+        ceiling = {"kernel": "stream_read_kernel", "bytes_per_launch": nbytes, "avg_us": round(dt * 1e6, 1),
+                   "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4),
+                   "decode_frac_of_ceiling": round(gbps / c_gbps, 4)}
+        if roofline:
+            ceiling["dominant_kernel_frac_of_ceiling"] = round(roofline["achieved"] / c_gbps, 4)
+        del buf, sums
+        torch.cuda.empty_cache()
+        print(f"# read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         cache = oracle.KVCache(cfg)
         n_cpu = max(1, min(args.cpu_steps, S - start))
-        # a step's cost does not depend on the cache contents: late positions run on a zero cache
+        # one thread, pinned to one core; a step's cost does not depend on the
+        # cache contents: late positions run on a zero cache
+        allowed = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(allowed)})
         t0 = time.perf_counter()
         tok = 1
         for p in range(start, start + n_cpu):
             logits = oracle.forward(cfg, blob, cache, tok, p)
             tok = oracle.argmax(logits)
         dt = time.perf_counter() - t0
+        os.sched_setaffinity(0, allowed)
+        cpu_model = ""
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(n_cpu / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": f"{n_cpu} greedy decode steps (positions {start}-{start + n_cpu - 1}) of the {cfg.name} "
                          f"workload, single-threaded C oracle with double accumulation, {dt:.1f} s",
                "GBps": round(sum(bytes_per_token(cfg, p) for p in range(start, start + n_cpu)) / dt / 1e9, 2),
-               "host_cores_available": os.cpu_count()}
+               "host_cores_available": os.cpu_count(), "pinned_core": min(allowed), "cpu_model": cpu_model}
 
     line = {
         "metric": "batch-1 decode tokens/sec + achieved HBM GB/s as % of MI355X peak",
@@ -377,6 +420,7 @@ def main() -> int:
         "generation_loop": sampled,
         "prefill": prefill,
         "batch_decode": batch,
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -299,6 +299,21 @@ int ld_op_argmax(const float* d_v, int32_t n, int32_t* h_index_out, void* hip_st
 int ld_op_sample(const float* d_logits, int32_t n, float temperature, float topp, float coin,
                  int32_t* h_token_out, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement.  A plain streaming read of d_src[0..bytes): the practical HBM
+ * read ceiling that the decode step's weight streams are reported against
+ * (the step reads every weight once per token, so its bound is the read
+ * bandwidth).  The buffer is split into LD_STREAM_READ_BLOCKS contiguous
+ * shares of bytes / 16 float4 (share b starts at float4 b * ceil(n / blocks));
+ * d_sums[b] receives the fp32 sum of share b's floats in an unspecified
+ * order, which keeps every load live.  bytes > 0 and a multiple of 16 (else
+ * LD_E_SIZE); d_src 16-byte aligned (else LD_E_ALIGN); d_sums holds
+ * LD_STREAM_READ_BLOCKS floats.  Asynchronous on hip_stream (NULL = null
+ * stream), so that HIP events around it time the kernel alone.
+ */
+#define LD_STREAM_READ_BLOCKS 2048
+int ld_op_stream_read(const void* d_src, size_t bytes, float* d_sums, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

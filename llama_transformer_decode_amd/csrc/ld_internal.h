@@ -189,6 +189,9 @@ hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
 hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s);
 // per-block bests of v (the classifier kernel writes its own)
 hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblocks, hipStream_t s);
+// block b of kStreamReadBlocks sums its contiguous share of bytes / 16 float4 into sums[b]
+constexpr int kStreamReadBlocks = 2048;
+hipError_t stream_read_launch(const void* src, size_t bytes, float* sums, hipStream_t s);
 int argmax_blocks(int n);
 // the next token from the per-block bests and the logits: st->next,
 // tokens_out[pos], advance (token, pos), set `stopped` at the stop token

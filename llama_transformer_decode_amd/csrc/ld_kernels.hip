@@ -775,6 +775,41 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     if constexpr (KIND == K_CLS) publish_best<NT>(bv, bi, p.best);
 }
 
+// A plain streaming read: the practical HBM read ceiling the weight streams
+// are measured against.  Block b sums its contiguous range of the buffer
+// (non-temporal 16-byte loads, 16 per thread in flight, like the weight
+// loads of the GEMVs) into sums[b]; the sums keep the loads live.
+constexpr int kStreamThreads = 256, kStreamU = 16;
+
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const float4* __restrict__ src, long long n4,
+                                                                     long long per, float* __restrict__ sums) {
+    __shared__ float part[kStreamThreads / 64];
+    const long long b0 = (long long)blockIdx.x * per;
+    const long long b1 = min(n4, b0 + per);
+    float acc = 0.f;
+    long long i = b0 + threadIdx.x;
+    for (; i + (long long)(kStreamU - 1) * kStreamThreads < b1; i += (long long)kStreamThreads * kStreamU) {
+        float4 v[kStreamU];
+#pragma unroll
+        for (int u = 0; u < kStreamU; ++u) v[u] = load_w(src + i + u * kStreamThreads);
+#pragma unroll
+        for (int u = 0; u < kStreamU; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    for (; i < b1; i += kStreamThreads) {
+        const float4 v = load_w(src + i);
+        acc += (v.x + v.y) + (v.z + v.w);
+    }
+    acc = wave_sum(acc);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStreamThreads / 64; ++w) t += part[w];
+        sums[blockIdx.x] = t;
+    }
+}
+
 // Argmax of a vector: per-block bests (the reduction the classifier uses),
 // then next_token_kernel.
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_partial_kernel(const float* v, int n, float2* best) {
@@ -1495,6 +1530,14 @@ hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblock
 hipError_t next_token_launch(const NextTokenParams& p, hipStream_t s) {
     static_assert(kMaxSampleVocab == 1024 * 32, "sampler register layout");
     hipLaunchKernelGGL((next_token_kernel<1024, 32>), dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t stream_read_launch(const void* src, size_t bytes, float* sums, hipStream_t s) {
+    const long long n4 = (long long)(bytes / 16);
+    const long long per = (n4 + kStreamReadBlocks - 1) / kStreamReadBlocks;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamReadBlocks), dim3(kStreamThreads), 0, s,
+                       static_cast<const float4*>(src), n4, per, sums);
     return hipGetLastError();
 }
 

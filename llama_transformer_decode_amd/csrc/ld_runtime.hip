@@ -1389,4 +1389,13 @@ int ld_op_sample(const float* d_logits, int32_t n, float temperature, float topp
     return op_next_token(d_logits, n, c, coin, h_token_out, static_cast<hipStream_t>(hip_stream));
 }
 
+int ld_op_stream_read(const void* d_src, size_t bytes, float* d_sums, void* hip_stream) {
+    static_assert(LD_STREAM_READ_BLOCKS == kStreamReadBlocks, "stream-read block count");
+    if (!d_src || !d_sums) return LD_E_NULL;
+    if (bytes == 0 || bytes % 16) return LD_E_SIZE;
+    if (!aligned16(d_src)) return LD_E_ALIGN;
+    HIP_TRY(stream_read_launch(d_src, bytes, d_sums, static_cast<hipStream_t>(hip_stream)));
+    return LD_OK;
+}
+
 }  // extern "C"

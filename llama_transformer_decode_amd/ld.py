@@ -30,6 +30,7 @@ EXPORTS = (
     "ld_generate", "ld_prefill", "ld_prefill_seq", "ld_forward_batch", "ld_generate_greedy_batch", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
     "ld_profile_steps", "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope",
     "ld_op_attention", "ld_op_gemm", "ld_op_attention_prefill", "ld_op_argmax", "ld_op_sample",
+    "ld_op_stream_read",
 )
 
 
@@ -108,6 +109,7 @@ def library():
             "ld_op_attention_prefill": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_argmax": ([_P, _I, ctypes.POINTER(_I), _P], ctypes.c_int),
             "ld_op_sample": ([_P, _I, _F, _F, _F, ctypes.POINTER(_I), _P], ctypes.c_int),
+            "ld_op_stream_read": ([_P, ctypes.c_size_t, _P, _P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -285,6 +287,15 @@ def ld_op_sample(d_logits, n, temperature, topp, coin, stream=0) -> int:
     _check(library().ld_op_sample(d_logits, n, temperature, topp, coin, ctypes.byref(out), stream or None),
            "ld_op_sample")
     return out.value
+
+
+LD_STREAM_READ_BLOCKS = 2048
+
+
+def ld_op_stream_read(d_src, nbytes, d_sums, stream=0):
+    """Enqueue the plain streaming read of nbytes at d_src (asynchronous);
+    d_sums (LD_STREAM_READ_BLOCKS floats) receives the per-share sums."""
+    _check(library().ld_op_stream_read(d_src, nbytes, d_sums, stream or None), "ld_op_stream_read")
 
 
 def ld_op_gemm(d_a, d_w, m, n, k, d_out, stream=0):

@@ -145,3 +145,13 @@ def test_prefill_and_gemm_argument_checks_come_first():
     assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 8, 16, 0, 2, fake, None) == ld.LD_E_CONFIG
     assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 4, 16, 0, 0, fake, None) == ld.LD_E_RANGE
     assert lib.ld_op_attention_prefill(fake, fake, fake, 4, 4, 16, -1, 2, fake, None) == ld.LD_E_RANGE
+
+
+def test_stream_read_argument_checks_come_first():
+    lib = pkg.library()
+    fake = 0x10000  # never dereferenced
+    assert lib.ld_op_stream_read(None, 16, fake, None) == ld.LD_E_NULL
+    assert lib.ld_op_stream_read(fake, 16, None, None) == ld.LD_E_NULL
+    assert lib.ld_op_stream_read(fake, 0, fake, None) == ld.LD_E_SIZE
+    assert lib.ld_op_stream_read(fake, 20, fake, None) == ld.LD_E_SIZE
+    assert lib.ld_op_stream_read(fake + 4, 16, fake, None) == ld.LD_E_ALIGN

@@ -211,3 +211,22 @@ def test_op_argument_errors():
     with pytest.raises(ld.LdError) as e:
         ld.ld_op_attention(x.data_ptr(), x.data_ptr(), x.data_ptr(), 1, 1, 24, 0, x.data_ptr())
     assert e.value.status == ld.LD_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n4", [1, 7, 2048, 2049, 100_003, 2_000_000])
+def test_stream_read_sums_every_share(n4):
+    # small integers: every partial sum is exact in fp32, in any order
+    import torch
+    rng = np.random.default_rng(n4)
+    v = rng.integers(-2, 3, 4 * n4).astype(np.float32)
+    dv = dev(v)
+    sums = torch.full((ld.LD_STREAM_READ_BLOCKS,), float("nan"), dtype=torch.float32, device="cuda")
+    ld.ld_op_stream_read(dv.data_ptr(), 16 * n4, sums.data_ptr())
+    torch.cuda.synchronize()
+    got = host(sums).astype(np.float64)
+    per = -(-n4 // ld.LD_STREAM_READ_BLOCKS)
+    want = np.zeros(ld.LD_STREAM_READ_BLOCKS)
+    for b in range(ld.LD_STREAM_READ_BLOCKS):
+        lo, hi = min(n4, b * per), min(n4, (b + 1) * per)
+        want[b] = v[4 * lo:4 * hi].astype(np.float64).sum()
+    assert np.array_equal(got, want)
