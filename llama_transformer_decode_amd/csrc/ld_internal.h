@@ -65,6 +65,7 @@ struct GemvPlan {
     int rpi;
     int units;
     int grid;
+    int nb;                // 0: one vector; else the batch kernel for up to nb vectors
 };
 
 struct GemvParams {
@@ -89,6 +90,13 @@ struct GemvParams {
     const float2* rope;    // K_QKV: (position, head_size/2) -> (cos, sin)
     StepState* state;
     float2* best;          // K_CLS: per-block (value, index bits)
+    // the batch kernel (GemvPlan.nb > 0): vectors 0..nb-1, vector b at x + b ldx
+    // (out + b ldo, x_resid + b ldr); K_QKV: vector b is sequence b at
+    // row_state[b].pos, its caches seq_stride floats after sequence b-1's
+    int nb;
+    int ldx, ldo, ldr;
+    const StepState* row_state;
+    size_t seq_stride;
 };
 
 struct AttnParams {
@@ -179,6 +187,10 @@ hipError_t attn_prefill_launch(int head_size, const AttnPrefillParams& p, hipStr
 // Plans and launchers.  Return hipSuccess, or hipErrorInvalidValue for a
 // shape outside the compiled kernels.
 hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan);
+// the batch kernel for up to kGemvBatch vectors (hipErrorInvalidValue when n
+// is beyond its shapes); K_PLAIN, K_RESID, K_QKV, K_SWIGLU
+constexpr int kGemvBatch = 4;
+hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan);
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s);
 
 int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)

@@ -775,6 +775,141 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     if constexpr (KIND == K_CLS) publish_best<NT>(bv, bi, p.best);
 }
 
+// The same product for a few vectors at once (a decode batch of up to NB
+// sequences): every weight row is streamed once and multiplied into the NB
+// vectors held in registers, so for small batches the step keeps the GEMV's
+// weight stream, its fused RMSNorm and epilogues, and no split of K.  Vectors
+// past p.nb repeat the last one; their results are not stored.
+template <int NT, int NX, int RPI, int KIND, int NB>
+__global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
+    constexpr int NW = NT / 64, V = NB * RPI;
+    static_assert(V <= 64, "the epilogue lanes sit in wave 0");
+    __shared__ float red[2][NW][V];
+    __shared__ float ss_part[NW][NB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n4 = p.n >> 2;
+
+    const int u0 = (int)(((long long)blockIdx.x * p.units) / gridDim.x);
+    const int u1 = (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    float4 w[RPI][NX];
+    if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
+
+    float4 xr[NB][NX];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float4* x4 = reinterpret_cast<const float4*>(p.x + (size_t)min(b, p.nb - 1) * p.ldx);
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+            const int idx = tid + k * NT;
+            xr[b][k] = zero_unless(idx < n4, x4[min(idx, n4 - 1)]);
+        }
+    }
+    // RMSNorm of every vector: x' = g * (x * 1/sqrt(mean(x^2) + eps))
+    if (p.gain) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < NX; ++k) ss = dot4(xr[b][k], xr[b][k], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) ss_part[wave][b] = ss;
+        }
+        __syncthreads();
+        const float4* g4 = reinterpret_cast<const float4*>(p.gain);
+        float4 g[NX];
+#pragma unroll
+        for (int k = 0; k < NX; ++k) {
+            const int idx = tid + k * NT;
+            g[k] = zero_unless(idx < n4, g4[min(idx, n4 - 1)]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) tot += ss_part[w2][b];
+            const float r = 1.0f / sqrtf(tot / (float)p.n + p.eps);
+#pragma unroll
+            for (int k = 0; k < NX; ++k)
+                xr[b][k] = make_float4(g[k].x * (r * xr[b][k].x), g[k].y * (r * xr[b][k].y),
+                                       g[k].z * (r * xr[b][k].z), g[k].w * (r * xr[b][k].w));
+        }
+    }
+
+    // lane tid < V of wave 0 finishes (vector tid / RPI, row tid % RPI) of a group
+    const int vb = tid / RPI, vr = tid % RPI;
+    const bool mine = tid < V && vb < p.nb;
+    int buf = 0;
+    for (int u = u0; u < u1; ++u) {
+        float acc[NB][RPI];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) {
+                acc[b][r] = 0.f;
+#pragma unroll
+                for (int k = 0; k < NX; ++k) acc[b][r] = dot4(w[r][k], xr[b][k], acc[b][r]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < u1) load_group<NT, NX, RPI, KIND>(p, u + 1, n4, w);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < RPI; ++r) {
+                const float t = wave_sum(acc[b][r]);
+                if (lane == 0) red[buf][wave][b * RPI + r] = t;
+            }
+        __syncthreads();
+        float total = 0.f;
+        if (tid < V) {
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) total += red[buf][w2][tid];
+        }
+        buf ^= 1;
+
+        if constexpr (KIND == K_PLAIN) {
+            const int row = u * RPI + vr;
+            if (mine && row < p.rows) p.out[(size_t)vb * p.ldo + row] = total;
+        } else if constexpr (KIND == K_RESID) {
+            const int row = u * RPI + vr;
+            if (mine && row < p.rows) p.x_resid[(size_t)vb * p.ldr + row] += total;
+        } else if constexpr (KIND == K_QKV) {
+            // RoPE and the cache append as in gemv_kernel, at sequence vb's
+            // own position and in its own caches
+            const float other = __shfl_xor(total, 1);
+            const int row = u * RPI + vr;
+            if (mine && row < p.rows) {
+                const bool odd = vr & 1;
+                const int pos = p.row_state[vb].pos;
+                const size_t seq = (size_t)vb * p.seq_stride;
+                if (row < p.seg2) {
+                    const bool is_q = row < p.seg1;
+                    const int local = is_q ? row : row - p.seg1;
+                    const int hs = p.head_size;
+                    const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + ((local % hs) >> 1)];
+                    const float a = odd ? other : total;  // element 2j
+                    const float b = odd ? total : other;  // element 2j+1
+                    const float v = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
+                    if (is_q)
+                        p.out[(size_t)vb * p.ldo + row] = v;
+                    else
+                        p.kc[seq + (size_t)pos * p.kv_stride + local] = v;
+                } else {
+                    p.vc[seq + (size_t)pos * p.kv_stride + (row - p.seg2)] = total;
+                }
+            }
+        } else if constexpr (KIND == K_SWIGLU) {
+            const float other = __shfl_xor(total, 1);
+            const int e = u * (RPI / 2) + (vr >> 1);
+            if (mine && !(vr & 1) && e < p.rows) {
+                float a = total;
+                a *= 1.0f / (1.0f + expf(-a));
+                a *= other;
+                p.out[(size_t)vb * p.ldo + e] = a;
+            }
+        }
+    }
+}
+
 // A plain streaming read: the practical HBM read ceiling the weight streams
 // are measured against.  Block b sums its contiguous range of the buffer
 // (non-temporal 16-byte loads, 16 per thread in flight, like the weight
@@ -1359,7 +1494,64 @@ GemvFn gemv_fn_kind(int kind, int t) {
     return nullptr;
 }
 
+// Batch kernel shapes: NB vectors of NX float4 per thread stay in registers,
+// so NB * NX stays at 24 or below (and blocks at 512 threads, which leave a
+// wave 256 registers).  Two rows per group: four cost more registers than
+// the pipelined loads gain (measured on the 7B shape, 4 sequences: 4.83 ms
+// per step with 2 rows per group at n <= 4096, 5.35 with 4; 512 x 2 x 2:
+// 5.11; one row per group for the residual products: 4.86-4.89).
+#ifndef LD_GEMVB_4096
+#define LD_GEMVB_4096 {256, 4, 2}
+#endif
+#ifndef LD_GEMVB_12288
+#define LD_GEMVB_12288 {512, 6, 2}
+#endif
+constexpr Tpl kTplB[] = {
+    {64, 1, 4},       // n <= 256
+    {256, 1, 4},      // n <= 1024
+    LD_GEMVB_4096,    // n <= 4096
+    {512, 4, 2},      // n <= 8192
+    LD_GEMVB_12288,   // n <= 12288
+};
+constexpr int kNumTplB = sizeof(kTplB) / sizeof(kTplB[0]);
+
+constexpr int rows_per_group_b(int t, int kind) {
+    return (kind == K_QKV || kind == K_SWIGLU) && kTplB[t].rpi < 2 ? 2 : kTplB[t].rpi;
+}
+
+template <int KIND, int T>
+GemvFn gemv_batch_fn_t() {
+    return gemv_batch_kernel<kTplB[T].nt, kTplB[T].nx, rows_per_group_b(T, KIND), KIND, kGemvBatch>;
+}
+
+template <int KIND>
+GemvFn gemv_batch_fn(int t) {
+    switch (t) {
+        case 0: return gemv_batch_fn_t<KIND, 0>();
+        case 1: return gemv_batch_fn_t<KIND, 1>();
+        case 2: return gemv_batch_fn_t<KIND, 2>();
+        case 3: return gemv_batch_fn_t<KIND, 3>();
+        case 4: return gemv_batch_fn_t<KIND, 4>();
+    }
+    return nullptr;
+}
+
+GemvFn gemv_batch_fn_kind(int kind, int t) {
+    switch (kind) {
+        case K_PLAIN: return gemv_batch_fn<K_PLAIN>(t);
+        case K_RESID: return gemv_batch_fn<K_RESID>(t);
+        case K_QKV: return gemv_batch_fn<K_QKV>(t);
+        case K_SWIGLU: return gemv_batch_fn<K_SWIGLU>(t);
+    }
+    return nullptr;
+}
+
 int template_for(const GemvPlan& pl) {
+    if (pl.nb) {
+        for (int t = 0; t < kNumTplB; ++t)
+            if (kTplB[t].nt == pl.nt && kTplB[t].nx == pl.nx && rows_per_group_b(t, pl.kind) == pl.rpi) return t;
+        return -1;
+    }
     for (int t = 0; t < kNumTpl; ++t)
         if (kTpl[t].nt == pl.nt && kTpl[t].nx == pl.nx && rows_per_group(t, pl.kind) == pl.rpi) return t;
     return -1;
@@ -1387,6 +1579,7 @@ hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan) {
     plan->nt = tp.nt;
     plan->nx = tp.nx;
     plan->rpi = rpi;
+    plan->nb = 0;
     plan->units = (rows + per_iter - 1) / per_iter;
 
     int dev = 0, cus = 0, occ = 0;
@@ -1410,12 +1603,51 @@ hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan) {
     return hipSuccess;
 }
 
+hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan) {
+    if (n <= 0 || rows <= 0 || (n & 3)) return hipErrorInvalidValue;
+    if (kind != K_PLAIN && kind != K_RESID && kind != K_QKV && kind != K_SWIGLU) return hipErrorInvalidValue;
+    const int n4 = n / 4;
+    int t = 0;
+    while (t < kNumTplB && kTplB[t].nt * kTplB[t].nx < n4) ++t;
+    if (t == kNumTplB) return hipErrorInvalidValue;
+    const Tpl tp = kTplB[t];
+    const int rpi = rows_per_group_b(t, kind);
+    const int per_iter = kind == K_SWIGLU ? rpi / 2 : rpi;
+    plan->kind = kind;
+    plan->nt = tp.nt;
+    plan->nx = tp.nx;
+    plan->rpi = rpi;
+    plan->nb = kGemvBatch;
+    plan->units = (rows + per_iter - 1) / per_iter;
+    int dev = 0, cus = 0, occ = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_batch_fn_kind(kind, t), tp.nt, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    const int slots = cus * occ;
+    if (plan->units <= slots) {
+        plan->grid = plan->units;
+    } else {
+        const int even = divisor_in(plan->units, (slots + 1) / 2, slots);
+        plan->grid = even ? even : slots;
+    }
+    return hipSuccess;
+}
+
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s) {
     const int t = template_for(plan);
     if (t < 0) return hipErrorInvalidValue;
     GemvParams p = p0;
     p.units = plan.units;
-    hipLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    if (plan.nb) {
+        if (p.nb < 1 || p.nb > plan.nb) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(gemv_batch_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    }
     return hipGetLastError();
 }
 

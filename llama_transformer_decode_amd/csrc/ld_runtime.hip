@@ -143,6 +143,8 @@ struct ld_model {
     bool bstate_pending = false;
     std::map<int, std::pair<hipGraph_t, hipGraphExec_t>> batch_graphs;
     GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
+    GemvPlan bpq{}, bpwo{}, bpffn{}, bpw2{}, bpcls{};  // batches of up to kGemvBatch
+    bool bgemv = false;                                  //   (when every shape has a batch plan)
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
     hipGraph_t graph = nullptr;
@@ -496,11 +498,118 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
     return LD_OK;
 }
 
+// Attention of layer l for sequences 0..n-1 of the batch (q rows in bq, each
+// sequence's own caches and position).
+hipError_t launch_batch_attention(ld_model* m, int n, int l) {
+    const ld_config& c = m->cfg;
+    const size_t cache_layer = (size_t)c.seq_len * m->kv_dim;
+    AttnParams a{};
+    a.q = m->bq;
+    a.kc = m->kc + (size_t)l * cache_layer;
+    a.vc = m->vc + (size_t)l * cache_layer;
+    a.out = m->batt;
+    a.part_ml = m->bpart_ml;
+    a.part_acc = m->bpart_acc;
+    a.state = m->bstate;
+    a.n_heads = c.n_heads;
+    a.n_kv_heads = c.n_kv_heads;
+    a.kv_dim = m->kv_dim;
+    a.nsplit = m->nsplit;
+    a.batch = n;
+    a.q_stride = c.dim;
+    a.seq_stride = (size_t)c.n_layers * cache_layer;
+    return attn_launch(m->hs, a, m->stream);
+}
+
+// A decode step of up to kGemvBatch sequences with the batch GEMV kernels:
+// the single step's launches (each weight streamed once, the RMSNorms fused)
+// with the vectors of all sequences in registers.
+int launch_batch_step_gemv(ld_model* m, int n) {
+    const ld_config& c = m->cfg;
+    const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
+    const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
+    hipStream_t s = m->stream;
+    auto bparams = [&](const float* x, int ldx) {
+        GemvParams p{};
+        p.eps = m->opt.norm_eps;
+        p.nb = n;
+        p.x = x;
+        p.ldx = ldx;
+        p.ldr = c.dim;
+        return p;
+    };
+    HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        {
+            GemvParams p = bparams(m->bx, c.dim);
+            p.gain = m->rms_att + (size_t)l * d;
+            p.n = c.dim;
+            p.rows = c.dim + 2 * m->kv_dim;
+            p.w0 = m->wq + (size_t)l * d * d;
+            p.w1 = m->wk + (size_t)l * kv * d;
+            p.w2 = m->wv + (size_t)l * kv * d;
+            p.seg1 = c.dim;
+            p.seg2 = c.dim + m->kv_dim;
+            p.out = m->bq;
+            p.ldo = c.dim;
+            p.kc = m->kc + (size_t)l * cache_layer;
+            p.vc = m->vc + (size_t)l * cache_layer;
+            p.kv_stride = m->kv_dim;
+            p.head_size = m->hs;
+            p.rope = m->rope;
+            p.row_state = m->bstate;
+            p.seq_stride = seq_stride;
+            HIP_TRY(gemv_launch(m->bpq, p, s));
+        }
+        HIP_TRY(launch_batch_attention(m, n, l));
+        {
+            GemvParams p = bparams(m->batt, c.dim);
+            p.x_resid = m->bx;
+            p.n = c.dim;
+            p.rows = c.dim;
+            p.w0 = m->wo + (size_t)l * d * d;
+            HIP_TRY(gemv_launch(m->bpwo, p, s));
+        }
+        {
+            GemvParams p = bparams(m->bx, c.dim);
+            p.gain = m->rms_ffn + (size_t)l * d;
+            p.n = c.dim;
+            p.rows = c.hidden_dim;
+            p.w0 = m->w1 + (size_t)l * h * d;
+            p.w1 = m->w3 + (size_t)l * h * d;
+            p.out = m->bhb;
+            p.ldo = c.hidden_dim;
+            HIP_TRY(gemv_launch(m->bpffn, p, s));
+        }
+        {
+            GemvParams p = bparams(m->bhb, c.hidden_dim);
+            p.x_resid = m->bx;
+            p.n = c.hidden_dim;
+            p.rows = c.dim;
+            p.w0 = m->w2 + (size_t)l * d * h;
+            HIP_TRY(gemv_launch(m->bpw2, p, s));
+        }
+    }
+    {
+        GemvParams p = bparams(m->bx, c.dim);
+        p.gain = m->rms_final;
+        p.n = c.dim;
+        p.rows = c.vocab_size;
+        p.w0 = m->wcls;
+        p.out = m->blogits;
+        p.ldo = c.vocab_size;
+        HIP_TRY(gemv_launch(m->bpcls, p, s));
+    }
+    HIP_TRY(argmax_rows_launch(m->blogits, n, c.vocab_size, m->bstate, m->btokens, c.seq_len, s));
+    return LD_OK;
+}
+
 // One decode step of sequences 0..n-1 of the batch, each reading (token, pos)
 // from m->bstate[b]: the single step's sequence of operations with the weight
 // matrices as matrix-core products of n rows (each RMSNorm fused into the
 // product it feeds), so every weight is read once for the whole batch.
 int launch_batch_step(ld_model* m, int n) {
+    if (n <= kGemvBatch && m->bgemv) return launch_batch_step_gemv(m, n);
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
     const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
@@ -534,24 +643,7 @@ int launch_batch_step(ld_model* m, int n) {
             g.seq_stride = seq_stride;
             HIP_TRY(gemm_launch(G_QKV, g, s));
         }
-        {
-            AttnParams a{};
-            a.q = m->bq;
-            a.kc = m->kc + (size_t)l * cache_layer;
-            a.vc = m->vc + (size_t)l * cache_layer;
-            a.out = m->batt;
-            a.part_ml = m->bpart_ml;
-            a.part_acc = m->bpart_acc;
-            a.state = m->bstate;
-            a.n_heads = c.n_heads;
-            a.n_kv_heads = c.n_kv_heads;
-            a.kv_dim = m->kv_dim;
-            a.nsplit = m->nsplit;
-            a.batch = n;
-            a.q_stride = c.dim;
-            a.seq_stride = seq_stride;
-            HIP_TRY(attn_launch(m->hs, a, s));
-        }
+        HIP_TRY(launch_batch_attention(m, n, l));
         {
             GemmParams g{};
             g.a = m->batt;
@@ -795,6 +887,11 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
                 }
             m->bsplit_floats = ws;
             if ((rc = dalloc(m, &m->bsplit, ws))) break;
+            m->bgemv = gemv_plan_batch(K_QKV, cfg->dim + 2 * m->kv_dim, cfg->dim, &m->bpq) == hipSuccess &&
+                       gemv_plan_batch(K_RESID, cfg->dim, cfg->dim, &m->bpwo) == hipSuccess &&
+                       gemv_plan_batch(K_SWIGLU, cfg->hidden_dim, cfg->dim, &m->bpffn) == hipSuccess &&
+                       gemv_plan_batch(K_RESID, cfg->dim, cfg->hidden_dim, &m->bpw2) == hipSuccess &&
+                       gemv_plan_batch(K_PLAIN, cfg->vocab_size, cfg->dim, &m->bpcls) == hipSuccess;
             e = hipHostMalloc((void**)&m->h_bstate, sizeof(StepState) * B, hipHostMallocDefault);
             if (e == hipSuccess)
                 e = hipHostMalloc((void**)&m->h_btokens, sizeof(int32_t) * B * cfg->seq_len, hipHostMallocDefault);
