@@ -197,6 +197,32 @@ def main() -> int:
     torch.cuda.synchronize()
     first_tok = tok
 
+    # ---- the practical read ceiling: a plain streaming read, timed just before the decode ----
+    ceiling = None
+    if not args.no_read_ceiling:
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        sums = torch.empty(pkg.ld.LD_STREAM_READ_BLOCKS, dtype=torch.float32, device="cuda:0")
+        st = torch.cuda.current_stream()
+        for _ in range(3):
+            pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+        reps, dts = 10, []
+        for _ in range(3):  # the best of 3 rounds of 10 reads: the ceiling is what the read can reach
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+            e1.record(st)
+            torch.cuda.synchronize()
+            dts.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        dt = min(dts)
+        c_gbps = nbytes / dt / 1e9
+        ceiling = {"kernel": "stream_read_kernel", "bytes_per_launch": nbytes, "avg_us": round(dt * 1e6, 1),
+                   "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4)}
+        del buf, sums
+        torch.cuda.empty_cache()
+        print(f"# read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
+
     # ---- timed region: greedy decode of `steps` tokens from (tok, start) ----
     chunks = []
     done, t_total = 0, 0.0
@@ -331,35 +357,6 @@ def main() -> int:
     del weights
     torch.cuda.empty_cache()
 
-    # ---- the practical read ceiling: a plain streaming read, same run, same stream timing ----
-    ceiling = None
-    if not args.no_read_ceiling:
-        nbytes = 4 << 30
-        buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
-        sums = torch.empty(pkg.ld.LD_STREAM_READ_BLOCKS, dtype=torch.float32, device="cuda:0")
-        st = torch.cuda.current_stream()
-        for _ in range(3):
-            pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
-        reps, dts = 10, []
-        for _ in range(3):  # the best of 3 rounds of 10 reads: the ceiling is what the read can reach
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(reps):
-                pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
-            e1.record(st)
-            torch.cuda.synchronize()
-            dts.append(e0.elapsed_time(e1) * 1e-3 / reps)
-        dt = min(dts)
-        c_gbps = nbytes / dt / 1e9
-        ceiling = {"kernel": "stream_read_kernel", "bytes_per_launch": nbytes, "avg_us": round(dt * 1e6, 1),
-                   "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4),
-                   "decode_frac_of_ceiling": round(gbps / c_gbps, 4)}
-        if roofline:
-            ceiling["dominant_kernel_frac_of_ceiling"] = round(roofline["achieved"] / c_gbps, 4)
-        del buf, sums
-        torch.cuda.empty_cache()
-        print(f"# read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
-
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -390,6 +387,11 @@ def main() -> int:
                          f"workload, single-threaded C oracle with double accumulation, {dt:.1f} s",
                "GBps": round(sum(bytes_per_token(cfg, p) for p in range(start, start + n_cpu)) / dt / 1e9, 2),
                "host_cores_available": os.cpu_count(), "pinned_core": min(allowed), "cpu_model": cpu_model}
+
+    if ceiling:
+        ceiling["decode_frac_of_ceiling"] = round(gbps / ceiling["GBps"], 4)
+        if roofline:
+            ceiling["dominant_kernel_frac_of_ceiling"] = round(roofline["achieved"] / ceiling["GBps"], 4)
 
     line = {
         "metric": "batch-1 decode tokens/sec + achieved HBM GB/s as % of MI355X peak",

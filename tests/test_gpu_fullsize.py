@@ -152,12 +152,10 @@ def test_long_prefill_equals_token_by_token_decode(big):
 def test_batch_step_at_full_size(big, case):
     # one batched step of several sequences at different installed prefixes, each row against the oracle;
     # 7B-shaped: 4 sequences (the batch GEMV kernels) and 6 (the split-K matrix-core products);
-    # 70B-layer: 2 sequences (its 28672-wide input has no batch GEMV shape: matrix-core products)
+    # 70B-layer: 2 and 3 sequences (its 28672-wide input has no batch GEMV shape: matrix-core products)
     cfg, blob, w = big
     lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300]],
-               "llama70b_8l": [[4000, 1500], None]}[cfg.name][case]
-    if lengths is None:
-        pytest.skip("one case for this workload")
+               "llama70b_8l": [[4000, 1500], [100, 4095, 2048]]}[cfg.name][case]
     B = len(lengths)
     caches = [(_prefix(cfg, p, 900 + 50 * b) if p else oracle.KVCache(cfg)) for b, p in enumerate(lengths)]
     toks = synth.prefill_tokens(cfg, B)
