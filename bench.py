@@ -10,7 +10,10 @@ once.  The weights are resident in HBM before the timed region starts.
 Output: one JSON line with decode tokens/s, achieved HBM GB/s (algorithmic
 bytes read per token / time), the roofline of the dominant kernel (its average
 launch duration measured with HIP events on the library's stream over a pass
-of the same workload) and the CPU oracle timed on a bounded sample.
+of the same workload; for the GEMV kernels the events are recorded by the
+kernel's own dispatch), the practical read ceiling (a plain streaming read
+timed just before the decode), the next rows' legs and the CPU oracle timed on
+a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 """
@@ -259,7 +262,7 @@ def main() -> int:
     print(f"# timed {steps} steps in {t_total:.3f} s: {tok_s:.1f} tok/s, {gbps:.0f} GB/s", file=sys.stderr,
           flush=True)
 
-    # ---- kernel durations: the same workload, every launch bracketed by HIP events ----
+    # ---- kernel durations: the same workload, every launch timed with HIP events ----
     roofline = None
     kernels = None
     if not args.no_kernel_timing:

@@ -191,7 +191,10 @@ hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan);
 // is beyond its shapes); K_PLAIN, K_RESID, K_QKV, K_SWIGLU
 constexpr int kGemvBatch = 4;
 hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan);
-hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s);
+// start / stop (optional): events recorded by the kernel's own dispatch, so that
+// their interval is the kernel's execution alone
+hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)
 int attn_splits(int head_size, int seq_len, int n_kv_heads);  // grid.y of the attention kernel

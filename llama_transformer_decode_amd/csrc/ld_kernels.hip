@@ -15,6 +15,7 @@
 // dense contraction.
 #include "ld_internal.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -1637,7 +1638,7 @@ hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan) {
     return hipSuccess;
 }
 
-hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s) {
+hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int t = template_for(plan);
     if (t < 0) return hipErrorInvalidValue;
     GemvParams p = p0;
@@ -1645,6 +1646,9 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s
     if (plan.nb) {
         if (p.nb < 1 || p.nb > plan.nb) return hipErrorInvalidValue;
         hipLaunchKernelGGL(gemv_batch_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    } else if (start || stop) {
+        // events taken by the dispatch itself: they bracket the kernel's execution
+        hipExtLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, start, stop, 0, p);
     } else {
         hipLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
     }

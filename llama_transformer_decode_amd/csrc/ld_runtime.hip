@@ -21,6 +21,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <map>
+#include <utility>
 #include <new>
 #include <vector>
 
@@ -249,6 +250,16 @@ void mark(Timer* t, hipStream_t s, int kind, bool before) {
     (void)hipEventRecord(t->ev[t->used++], s);
 }
 
+// the next event pair of the timer for a kernel that records them itself
+// (gemv_launch), or none without a timer
+std::pair<hipEvent_t, hipEvent_t> pair_for(Timer* t, int kind) {
+    if (!t) return {nullptr, nullptr};
+    t->kind[t->used / 2] = kind;
+    const size_t i = t->used;
+    t->used += 2;
+    return {t->ev[i], t->ev[i + 1]};
+}
+
 // One decode step, reading (token, pos) from m->state.
 int launch_step(ld_model* m, Timer* timer) {
     const ld_config& c = m->cfg;
@@ -275,9 +286,8 @@ int launch_step(ld_model* m, Timer* timer) {
             p.kv_stride = m->kv_dim;
             p.head_size = m->hs;
             p.rope = m->rope;
-            mark(timer, s, KQKV, true);
-            HIP_TRY(gemv_launch(m->pq, p, s));
-            mark(timer, s, KQKV, false);
+            const auto ev = pair_for(timer, KQKV);
+            HIP_TRY(gemv_launch(m->pq, p, s, ev.first, ev.second));
         }
         {
             AttnParams a{};
@@ -303,9 +313,8 @@ int launch_step(ld_model* m, Timer* timer) {
             p.n = c.dim;
             p.rows = c.dim;
             p.w0 = m->wo + (size_t)l * d * d;
-            mark(timer, s, KWO, true);
-            HIP_TRY(gemv_launch(m->pwo, p, s));
-            mark(timer, s, KWO, false);
+            const auto ev = pair_for(timer, KWO);
+            HIP_TRY(gemv_launch(m->pwo, p, s, ev.first, ev.second));
         }
         {
             GemvParams p = base_params(m);
@@ -316,9 +325,8 @@ int launch_step(ld_model* m, Timer* timer) {
             p.w0 = m->w1 + (size_t)l * h * d;
             p.w1 = m->w3 + (size_t)l * h * d;
             p.out = m->hb;
-            mark(timer, s, KFFN, true);
-            HIP_TRY(gemv_launch(m->pffn, p, s));
-            mark(timer, s, KFFN, false);
+            const auto ev = pair_for(timer, KFFN);
+            HIP_TRY(gemv_launch(m->pffn, p, s, ev.first, ev.second));
         }
         {
             GemvParams p = base_params(m);
@@ -327,9 +335,8 @@ int launch_step(ld_model* m, Timer* timer) {
             p.n = c.hidden_dim;
             p.rows = c.dim;
             p.w0 = m->w2 + (size_t)l * d * h;
-            mark(timer, s, KW2, true);
-            HIP_TRY(gemv_launch(m->pw2, p, s));
-            mark(timer, s, KW2, false);
+            const auto ev = pair_for(timer, KW2);
+            HIP_TRY(gemv_launch(m->pw2, p, s, ev.first, ev.second));
         }
     }
     GemvParams p = base_params(m);
