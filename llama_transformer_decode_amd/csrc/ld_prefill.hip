@@ -295,20 +295,43 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
     float sq[A_PER];  // NORM: this thread's part of its A rows' sums of squares
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) sq[i] = 0.f;
-    auto load_slab = [&](float4(&xa)[A_PER], float4(&xg)[GP], float4(&xb)[B_PER], int k) {
+
+    // Whole slabs (K chunk / BK of them) go through plain pointer offsets.
+    // The loop runs a whole number of register-set turns; slabs past the last
+    // whole one reload that one (always in bounds) with A scaled by zero, so
+    // they add nothing and no load of the loop sits behind a branch (a load
+    // that may not have been issued makes every later wait one for all loads
+    // in flight).  A ragged end of K is one masked slab after the loop.
+    const int nfull = (kend - kbeg) / BK;
+    const int nmain = (nfull + R - 1) / R * R;
+    const float* pa[A_PER];
+    const float* pg[GP];
+    const float* pb[B_PER];
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) xa[i] = load_k4(arow[i], k + alk[i], kend);
+    for (int i = 0; i < A_PER; ++i) pa[i] = arow[i] + kbeg + alk[i];
+#pragma unroll
+    for (int i = 0; i < GP; ++i) pg[i] = NORM ? (p.gain ? p.gain + kbeg + alk[i] : gemm_one4) : nullptr;
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) pb[i] = brow[i] + kbeg + blk[i];
+    const size_t gstep = NORM && p.gain ? BK : 0;  // the ones vector does not advance
+    auto load_whole = [&](float4(&xa)[A_PER], float4(&xg)[GP], float4(&xb)[B_PER], int slab) {
+        const size_t off = (size_t)min(slab, nfull - 1) * BK;
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) xa[i] = *reinterpret_cast<const float4*>(pa[i] + off);
         if constexpr (NORM) {
+            const size_t goff = (size_t)min(slab, nfull - 1) * gstep;
 #pragma unroll
-            for (int i = 0; i < A_PER; ++i) xg[i] = load_gain4(p.gain, k + alk[i], p.k);
+            for (int i = 0; i < A_PER; ++i) xg[i] = *reinterpret_cast<const float4*>(pg[i] + goff);
         }
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) xb[i] = load_k4(brow[i], k + blk[i], kend);
+        for (int i = 0; i < B_PER; ++i) xb[i] = *reinterpret_cast<const float4*>(pb[i] + off);
     };
-    auto store_slab = [&](const float4(&xa)[A_PER], const float4(&xg)[GP], const float4(&xb)[B_PER], int buf) {
+    // keep: 1 for a slab of this split, 0 for a padding slab
+    auto store_slab = [&](const float4(&xa)[A_PER], const float4(&xg)[GP], const float4(&xb)[B_PER], int buf,
+                          float keep) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
-            float4 v = xa[i];
+            float4 v = make_float4(keep * xa[i].x, keep * xa[i].y, keep * xa[i].z, keep * xa[i].w);
             if constexpr (NORM) {
                 sq[i] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
                 const float4 g = xg[i];
@@ -319,52 +342,67 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) *reinterpret_cast<float4*>(&Bs[buf][blrow[i]][blk[i]]) = xb[i];
     };
-
-    // slabs of this split, rounded up to a whole number of register-set turns
-    // (the extra slabs read zeros and add nothing), so that no load or store
-    // of the loop sits behind a branch
-    const int nk = ((kend - kbeg + BK - 1) / BK + R - 1) / R * R;
+    auto multiply = [&](int buf) {
+        // the MFMA's k positions of step s are k = HK g + s (lane group g):
+        // each lane reads HK consecutive floats of its row
+        float av[TM][HK], bv[TN][HK];
 #pragma unroll
-    for (int s = 0; s < R; ++s) load_slab(ra[s], rg[s % GS], rb[s], kbeg + s * BK);
-    store_slab(ra[0], rg[0], rb[0], 0);
-    load_slab(ra[0], rg[0], rb[0], kbeg + R * BK);
-    __syncthreads();
-
-    for (int kt0 = 0; kt0 < nk; kt0 += R) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int kt = kt0 + u;
-            const int buf = kt & 1;
-            // the MFMA's k positions of step s are k = HK g + s (lane group
-            // g): each lane reads HK consecutive floats of its row
-            float av[TM][HK], bv[TN][HK];
+            for (int q = 0; q < HK; q += 4) {
+                const float4 x = *reinterpret_cast<const float4*>(&As[buf][wm + i * MT + li][lg * HK + q]);
+                av[i][q] = x.x; av[i][q + 1] = x.y; av[i][q + 2] = x.z; av[i][q + 3] = x.w;
+            }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < HK; q += 4) {
+                const float4 y = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * MT + li][lg * HK + q]);
+                bv[j][q] = y.x; bv[j][q + 1] = y.y; bv[j][q + 2] = y.z; bv[j][q + 3] = y.w;
+            }
+#pragma unroll
+        for (int st = 0; st < HK; ++st)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int q = 0; q < HK; q += 4) {
-                    const float4 x = *reinterpret_cast<const float4*>(&As[buf][wm + i * MT + li][lg * HK + q]);
-                    av[i][q] = x.x; av[i][q + 1] = x.y; av[i][q + 2] = x.z; av[i][q + 3] = x.w;
-                }
+                for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<MT>::step(av[i][st], bv[j][st], acc[i][j]);
+    };
+
+    if (nfull > 0) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+        for (int s = 0; s < R; ++s) load_whole(ra[s], rg[s % GS], rb[s], s);
+        store_slab(ra[0], rg[0], rb[0], 0, 1.f);
+        load_whole(ra[0], rg[0], rb[0], R);
+        __syncthreads();
+        for (int kt0 = 0; kt0 < nmain; kt0 += R) {
 #pragma unroll
-                for (int q = 0; q < HK; q += 4) {
-                    const float4 y = *reinterpret_cast<const float4*>(&Bs[buf][wn + j * MT + li][lg * HK + q]);
-                    bv[j][q] = y.x; bv[j][q + 1] = y.y; bv[j][q + 2] = y.z; bv[j][q + 3] = y.w;
-                }
-#pragma unroll
-            for (int st = 0; st < HK; ++st)
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<MT>::step(av[i][st], bv[j][st], acc[i][j]);
-            // slab kt+1 to the other buffer (read in the previous iteration,
-            // before the barrier), then its register set takes slab kt+1+R;
-            // in the last iteration both only touch zeros
-            store_slab(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], buf ^ 1);
-            load_slab(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], kbeg + (kt + 1 + R) * BK);
-            __syncthreads();
+            for (int u = 0; u < R; ++u) {
+                const int kt = kt0 + u;
+                const int buf = kt & 1;
+                multiply(buf);
+                // slab kt+1 to the other buffer (read in the previous
+                // iteration, before the barrier), then its register set
+                // takes slab kt+1+R
+                store_slab(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], buf ^ 1, kt + 1 < nfull ? 1.f : 0.f);
+                load_whole(ra[(u + 1) % R], rg[(u + 1) % R % GS], rb[(u + 1) % R], kt + 1 + R);
+                __syncthreads();
+            }
         }
+    }
+    if (kbeg + nfull * BK < kend) {  // the ragged end of K: one slab, zero past kend
+        const int k = kbeg + nfull * BK;
+        const int buf = nmain & 1;  // not read since the last barrier
+#pragma unroll
+        for (int i = 0; i < A_PER; ++i) ra[0][i] = load_k4(arow[i], k + alk[i], kend);
+        if constexpr (NORM) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) rg[0][i] = load_gain4(p.gain, k + alk[i], p.k);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) rb[0][i] = load_k4(brow[i], k + blk[i], kend);
+        store_slab(ra[0], rg[0], rb[0], buf, 1.f);
+        __syncthreads();
+        multiply(buf);
     }
 
     if constexpr (NORM) {
