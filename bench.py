@@ -129,8 +129,9 @@ def main() -> int:
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the plain streaming read that measures the practical HBM read ceiling")
-    ap.add_argument("--cpu-steps", type=int, default=4,
-                    help="oracle decode steps timed for the CPU baseline (about 13 s on the 7B shape)")
+    ap.add_argument("--cpu-positions", default=None,
+                    help="comma-separated positions of the oracle decode steps timed for the CPU baseline "
+                         "(default: the first timed position, 511 and the last one; about 10 s on the 7B shape)")
     ap.add_argument("--prefill-tokens", type=int, default=None,
                     help="prompt length of the timed batched prefill (default: the workload's prompt, else 2048; "
                          "0: skip)")
@@ -365,17 +366,24 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         cache = oracle.KVCache(cfg)
-        n_cpu = max(1, min(args.cpu_steps, S - start))
+        if args.cpu_positions:
+            cpu_pos = sorted({int(x) for x in args.cpu_positions.split(",") if x.strip()})
+        else:
+            cpu_pos = sorted({start, S - 1} | ({511} if start <= 511 < S else set()))
+        if not cpu_pos or cpu_pos[0] < 0 or cpu_pos[-1] >= S:
+            print(f"CPU baseline positions must lie in [0, {S})", file=sys.stderr)
+            return 2
         # one thread, pinned to one core; a step's cost does not depend on the
-        # cache contents: late positions run on a zero cache
+        # cache contents, so each position runs on the zero cache
         allowed = os.sched_getaffinity(0)
         os.sched_setaffinity(0, {min(allowed)})
-        t0 = time.perf_counter()
-        tok = 1
-        for p in range(start, start + n_cpu):
-            logits = oracle.forward(cfg, blob, cache, tok, p)
-            tok = oracle.argmax(logits)
-        dt = time.perf_counter() - t0
+        per_step = {}
+        for p in cpu_pos:
+            t0 = time.perf_counter()
+            oracle.forward(cfg, blob, cache, 1, p)
+            per_step[str(p)] = round(time.perf_counter() - t0, 3)
+        dt = sum(per_step.values())
+        n_cpu = len(cpu_pos)
         os.sched_setaffinity(0, allowed)
         cpu_model = ""
         try:
@@ -386,9 +394,11 @@ def main() -> int:
         except OSError:
             pass
         cpu = {"value": round(n_cpu / dt, 5), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n_cpu} greedy decode steps (positions {start}-{start + n_cpu - 1}) of the {cfg.name} "
-                         f"workload, single-threaded C oracle with double accumulation, {dt:.1f} s",
-               "GBps": round(sum(bytes_per_token(cfg, p) for p in range(start, start + n_cpu)) / dt / 1e9, 2),
+               "sample": f"{n_cpu} decode steps of the {cfg.name} workload at positions "
+                         f"{', '.join(map(str, cpu_pos))} (zero cache), single-threaded C oracle with double "
+                         f"accumulation, {dt:.1f} s",
+               "seconds_per_step": per_step,
+               "GBps": round(sum(bytes_per_token(cfg, p) for p in cpu_pos) / dt / 1e9, 2),
                "host_cores_available": os.cpu_count(), "pinned_core": min(allowed), "cpu_model": cpu_model}
 
     if ceiling:
