@@ -381,8 +381,9 @@ def main() -> int:
         for p in cpu_pos:
             t0 = time.perf_counter()
             oracle.forward(cfg, blob, cache, 1, p)
-            per_step[str(p)] = round(time.perf_counter() - t0, 3)
+            per_step[str(p)] = time.perf_counter() - t0
         dt = sum(per_step.values())
+        per_step = {k: float(f"{v:.4g}") for k, v in per_step.items()}
         n_cpu = len(cpu_pos)
         os.sched_setaffinity(0, allowed)
         cpu_model = ""
