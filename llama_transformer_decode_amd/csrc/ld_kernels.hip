@@ -1673,9 +1673,16 @@ int attn_chunk(int hs) {
 #define LD_ATTN_BLOCKS 512
 #endif
 
+#ifndef LD_ATTN_ONE_BLOCK_BYTES
+#define LD_ATTN_ONE_BLOCK_BYTES (128 << 10)
+#endif
+
 int attn_splits(int hs, int seq_len, int n_kv_heads) {
     const int ch = attn_chunk(hs);
     if (!ch) return 0;
+    // a kv head's whole cache is small enough for one block: no split, so no
+    // merge launch (a launch costs ~4 us even with nothing to do)
+    if ((long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES) return 1;
     const int tiles = (seq_len + ch - 1) / ch;
     // about LD_ATTN_BLOCKS blocks at the longest context (two per compute
     // unit), and no split shorter than LD_ATTN_MIN_TILES tiles
@@ -1706,14 +1713,14 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
             hipLaunchKernelGGL((attn128_kernel<4, 2>), grid, block, 0, s, p);
         else
             hipLaunchKernelGGL((attn128_kernel<8, 2>), grid, block, 0, s, p);
-        hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
+        if (p.nsplit > 1) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
         return hipGetLastError();
     }
     switch (hs) {
 #define LD_ATTN_CASE(HS, CH)                                                               \
     case HS:                                                                               \
         hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);                   \
-        hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p);                \
+        if (p.nsplit > 1) hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p); \
         break;
         LD_ATTN_CASE(16, 64)
         LD_ATTN_CASE(32, 64)
