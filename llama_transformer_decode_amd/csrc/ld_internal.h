@@ -177,7 +177,6 @@ hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim,
 hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s);
 hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* st, int32_t* tokens_out,
                               int tokens_stride, hipStream_t s);
-hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s);
 hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s);
 int gemm_splits(int m, int n, int k);  // K splits the launcher uses for m rows
 size_t gemm_part_floats(int m, int n, int k);  // split workspace: splits * m * (n + 1) floats

@@ -12,7 +12,8 @@
 //   attn_prefill    causal grouped-query attention of T queries over the
 //                   cache rows with v_mfma_f32_16x16x4f32 (flash-attention
 //                   style: online softmax, scores never leave registers)
-//   embed / rmsnorm_rows   the per-token gather and RMSNorm
+//   embed           the per-token gather (the RMSNorms are fused into the
+//                   products that follow them)
 //
 // All arithmetic is fp32 (products and sums), as in the decode kernels.
 #include "ld_internal.h"
@@ -29,7 +30,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Embedding gather and per-token RMSNorm.
+// Embedding gather.
 
 __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ emb, const int32_t* __restrict__ tokens,
                                                     int dim, float* __restrict__ x) {
@@ -39,34 +40,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ em
     for (int i = threadIdx.x; i < dim / 4; i += 256) dst[i] = src[i];
 }
 
-// out[t] = g * (x[t] * 1/sqrt(mean(x[t]^2) + eps)), one block per token, the
-// decode kernels' formula and order of operations.
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ g,
-                                                           float eps, int dim, float* __restrict__ out) {
-    __shared__ float part[4];
-    const int t = blockIdx.x;
-    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * dim);
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < dim / 4; i += 256) {
-        const float4 v = x4[i];
-        ss = fmaf(v.x, v.x, ss);
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = part[0] + part[1] + part[2] + part[3];
-    const float r = 1.0f / sqrtf(tot / (float)dim + eps);
-    const float4* g4 = reinterpret_cast<const float4*>(g);
-    float4* o4 = reinterpret_cast<float4*>(out + (size_t)t * dim);
-    for (int i = threadIdx.x; i < dim / 4; i += 256) {
-        const float4 v = x4[i], w = g4[i];
-        o4[i] = make_float4(w.x * (r * v.x), w.y * (r * v.y), w.z * (r * v.z), w.w * (r * v.w));
-    }
-}
 
 // ---------------------------------------------------------------------------
 // C = A * B^T on the matrix cores.
@@ -651,11 +624,6 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
 
 hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s) {
     hipLaunchKernelGGL(embed_kernel, dim3(t), dim3(256), 0, s, emb, tokens, dim, x);
-    return hipGetLastError();
-}
-
-hipError_t rmsnorm_rows_launch(const float* x, const float* g, float eps, int t, int dim, float* out, hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(t), dim3(256), 0, s, x, g, eps, dim, out);
     return hipGetLastError();
 }
 

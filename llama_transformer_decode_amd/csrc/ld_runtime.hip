@@ -126,7 +126,7 @@ struct ld_model {
     hipEvent_t ev_ptok = nullptr;
     bool ptok_pending = false;
     int pf_cap = 0;
-    float *pf_x = nullptr, *pf_xn = nullptr, *pf_q = nullptr, *pf_att = nullptr, *pf_hb = nullptr;
+    float *pf_x = nullptr, *pf_q = nullptr, *pf_att = nullptr, *pf_hb = nullptr;
     // decode batch: max_batch sequences, each with its own cache (caches are
     // (max_batch, L, S, kv_dim)), their activations, states and tokens, and
     // one captured graph per batch size
@@ -180,7 +180,7 @@ void release(ld_model* m) {
     if (m->h_btokens) (void)hipHostFree(m->h_btokens);
     if (m->ev_bstate) (void)hipEventDestroy(m->ev_bstate);
     for (void* p : m->dev_allocs) (void)hipFree(p);
-    for (float* p : {m->pf_x, m->pf_xn, m->pf_q, m->pf_att, m->pf_hb})
+    for (float* p : {m->pf_x, m->pf_q, m->pf_att, m->pf_hb})
         if (p) (void)hipFree(p);
     if (m->h_ptok) (void)hipHostFree(m->h_ptok);
     if (m->ev_ptok) (void)hipEventDestroy(m->ev_ptok);
@@ -397,14 +397,13 @@ constexpr int kPrefillChunk = 2048;
 int prefill_workspace(ld_model* m, int tokens) {
     if (tokens <= m->pf_cap) return LD_OK;
     HIP_TRY(hipStreamSynchronize(m->stream));
-    for (float** p : {&m->pf_x, &m->pf_xn, &m->pf_q, &m->pf_att, &m->pf_hb}) {
+    for (float** p : {&m->pf_x, &m->pf_q, &m->pf_att, &m->pf_hb}) {
         if (*p) (void)hipFree(*p);
         *p = nullptr;
     }
     m->pf_cap = 0;
     const size_t d = (size_t)m->cfg.dim * tokens, h = (size_t)m->cfg.hidden_dim * tokens;
     hipError_t e = hipMalloc((void**)&m->pf_x, d * sizeof(float));
-    if (e == hipSuccess) e = hipMalloc((void**)&m->pf_xn, d * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&m->pf_q, d * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&m->pf_att, d * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&m->pf_hb, h * sizeof(float));
@@ -425,10 +424,11 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
     hipStream_t s = m->stream;
     HIP_TRY(embed_launch(m->emb, m->ptok + p0, T, c.dim, m->pf_x, s));
     for (int l = 0; l < c.n_layers; ++l) {
-        HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_att + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_xn, s));
         {
             GemmParams g{};
-            g.a = m->pf_xn;
+            g.a = m->pf_x;
+            g.gain = m->rms_att + (size_t)l * d;
+            g.eps = m->opt.norm_eps;
             g.lda = c.dim;
             g.m = T;
             g.n = c.dim + 2 * m->kv_dim;
@@ -475,10 +475,11 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
             g.ldo = c.dim;
             HIP_TRY(gemm_launch(G_RESID, g, s));
         }
-        HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_ffn + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_xn, s));
         {
             GemmParams g{};
-            g.a = m->pf_xn;
+            g.a = m->pf_x;
+            g.gain = m->rms_ffn + (size_t)l * d;
+            g.eps = m->opt.norm_eps;
             g.lda = c.dim;
             g.m = T;
             g.n = 2 * c.hidden_dim;
