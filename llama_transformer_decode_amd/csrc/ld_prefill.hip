@@ -671,11 +671,14 @@ int gemm_tile_rows(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 
 
 // Splits of K for a product with few row tiles (a decode batch): with whole K
 // each block would stream its weight rows alone, and a few hundred blocks
-// leave most of the chip idle; splitting K gives about 1024 blocks (at least
-// 256 of K each), so every CU has several weight streams in flight.  Used
-// only where the caller provides the partials' workspace.
+// leave most of the chip idle; splitting K gives about 768 blocks (at least
+// 256 of K each): three per CU, as many as the 16- and 32-row tiles' LDS lets
+// a CU hold, so every block streams from the start and none runs in a second
+// round (7B shape: 6.5 against 6.9 ms per step at 16 sequences with 1024
+// blocks, 7.3 against 8.0 at 32, 10.7 against 11.4 at 64).  Used only where
+// the caller provides the partials' workspace.
 #ifndef LD_GEMM_SPLIT_BLOCKS
-#define LD_GEMM_SPLIT_BLOCKS 1024
+#define LD_GEMM_SPLIT_BLOCKS 768
 #endif
 #ifndef LD_GEMM_SPLIT_MINK
 #define LD_GEMM_SPLIT_MINK 256
