@@ -106,16 +106,19 @@ struct AttnParams {
     float* out;            // n_heads * head_size
     float2* part_ml;       // (n_heads, nsplit) running max and sum
     float* part_acc;       // (n_heads, nsplit, head_size) unnormalised outputs
+    unsigned* arrive;      // (batch, n_kv_heads) split arrival counts: zero before and after every launch
     const StepState* state;
     int n_heads;
     int n_kv_heads;
     int kv_dim;
     int nsplit;            // grid.y
     int chunk;             // keys per split (set by the launcher)
+    int fuse;              // 1: the last split block of a kv group merges it (set by the launcher)
     // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
     // out and state are b * q_stride floats / b states further, its caches
     // b * seq_stride floats, its split partials b * (n_heads * nsplit) pairs
-    // and b * (n_heads * nsplit * head_size) floats
+    // and b * (n_heads * nsplit * head_size) floats, its arrival counts
+    // b * n_kv_heads further
     int batch;
     int q_stride;
     size_t seq_stride;
@@ -197,7 +200,7 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s,
 
 int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)
 int attn_splits(int head_size, int seq_len, int n_kv_heads);  // grid.y of the attention kernel
-hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention + merge
+hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention (+ merge)
 
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
 hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s);

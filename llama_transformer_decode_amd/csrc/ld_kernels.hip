@@ -1023,8 +1023,11 @@ __global__ void set_state_kernel(StepState* st, int token, int pos) {
 // grows, l and the sum are rescaled by e^{m_old - m_new}).  The next tile's
 // loads are issued before the current tile is computed, so the block keeps
 // HBM requests in flight throughout.  Each block leaves (m, l, sum) as a
-// partial; attn_merge_kernel combines them exactly:
-// out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, M = max_s m_s.
+// partial, and they are combined exactly,
+// out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, M = max_s m_s:
+// by the last block of the kv group to finish (merge_group) when each thread
+// of that block folds a few splits, else by attn_merge_kernel, one block per
+// query head.
 //
 // All 256 threads work in every phase: a (head, key) score is split over up to
 // 16 threads when the group is small, and the value sum over key groups whose
@@ -1059,8 +1062,123 @@ __device__ __forceinline__ AttnParams seq_view(const AttnParams& p) {
     v.vc += (size_t)b * p.seq_stride;
     v.part_ml += (size_t)b * p.n_heads * p.nsplit;
     v.part_acc += (size_t)b * p.n_heads * p.nsplit * HS;
+    v.arrive += (size_t)b * p.n_kv_heads;
     v.state += b;
     return v;
+}
+
+// Split partials pass between blocks of one launch, which may run on
+// different XCDs with separate L2 caches.  They are stored and loaded with
+// agent-scope relaxed atomics (64 bits at a time), which the compiler issues
+// with the coherence bit set: stores write through the L2 and loads read past
+// stale lines, so no cache-wide write-back or invalidate is needed.
+__device__ __forceinline__ unsigned long long pack2(float a, float b) {
+    return ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
+}
+__device__ __forceinline__ float2 unpack2(unsigned long long v) {
+    return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), pack2(v.x, v.y), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float4* p, float4 v) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    __hip_atomic_store(q, pack2(v.x, v.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, pack2(v.z, v.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+    return unpack2(
+        __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float4 load_coherent(const float4* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const float2 a = unpack2(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float2 b = unpack2(__hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
+__device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
+    return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
+}
+
+// Exact merge of the split partials of query heads h_lo .. h_lo + G - 1 into
+// the output: with M = max_s m_s, out = sum_s e^{m_s - M} acc_s /
+// sum_s e^{m_s - M} l_s.  Thread (kg, o) folds splits kg, kg + KG, ... of
+// float4 output slot o into its own running (m, l, acc) (the online-softmax
+// rescaling, so every split's loads are independent of the others and all go
+// out at once); the KG key groups are then combined through LDS the same way.
+template <int HS>
+__device__ void merge_group(const AttnParams& p, int h_lo, int G, int nact) {
+    constexpr int H4 = HS / 4;
+    __shared__ float4 acc_s[kAttnThreads];
+    __shared__ float m_s[kAttnThreads], l_s[kAttnThreads];
+    const int tid = threadIdx.x;
+    const int slots = G * H4;  // float4 outputs of the group
+    const int KG = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    for (int o0 = 0; o0 < slots; o0 += kAttnThreads) {
+        const int o = o0 + (slots < kAttnThreads ? tid % slots : tid), kg = slots < kAttnThreads ? tid / slots : 0;
+        const int h = h_lo + o / H4, c = o % H4;
+        float m = -INFINITY, l = 0.f;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (o < slots && kg < KG) {
+            const float2* ml = p.part_ml + (size_t)h * p.nsplit;
+            const float4* ah = reinterpret_cast<const float4*>(p.part_acc) + (size_t)h * p.nsplit * H4 + c;
+#pragma unroll 8
+            for (int sp = kg; sp < nact; sp += KG) {
+                const float2 e = load_coherent(ml + sp);
+                const float4 v = load_coherent(ah + (size_t)sp * H4);
+                const float mn = fmaxf(m, e.x);
+                const float r = __expf(m - mn), w = __expf(e.x - mn);  // r = 0 for the first split
+                l = fmaf(l, r, e.y * w);
+                a = fma4(w, v, make_float4(a.x * r, a.y * r, a.z * r, a.w * r));
+                m = mn;
+            }
+        }
+        if (KG > 1) {
+            acc_s[tid] = a;
+            m_s[tid] = m;
+            l_s[tid] = l;
+            __syncthreads();
+            if (tid < slots) {
+                float M = m;
+                for (int k = 1; k < KG; ++k) M = fmaxf(M, m_s[k * slots + tid]);
+                l = 0.f;
+                a = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int k = 0; k < KG; ++k) {
+                    const float e = __expf(m_s[k * slots + tid] - M);  // 0 for a group without splits
+                    l = fmaf(l_s[k * slots + tid], e, l);
+                    a = fma4(e, acc_s[k * slots + tid], a);
+                }
+            }
+        }
+        if (o < slots && (KG == 1 || tid < slots)) {
+            const float il = 1.0f / l;
+            reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + c] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+        }
+    }
+}
+
+// Called by every thread of a split block after it has stored its partial
+// (coherent stores).  Each thread waits for its stores to complete before
+// thread 0 counts the block's arrival; the block that brings the count to nact
+// resets the counter for the next launch and merges the group, whose partials
+// it then reads with coherent loads.  No block waits for another, so the grid
+// always drains.
+template <int HS>
+__device__ void arrive_and_merge(const AttnParams& p, int g, int h_lo, int G, int nact) {
+    __shared__ int last_s;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned before = atomicAdd(p.arrive + g, 1u);
+        const int last = before + 1 == (unsigned)nact;
+        if (last) atomicExch(p.arrive + g, 0u);
+        last_s = last;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    merge_group<HS>(p, h_lo, G, nact);
 }
 
 template <int HS, int CH>
@@ -1195,7 +1313,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
 #pragma unroll
         for (int j = 0; j < NACC; ++j) {
             const int o = tid + j * kAttnThreads;
-            if (o < slots) part4[((size_t)(h_lo + o / H4) * p.nsplit + s) * H4 + o % H4] = acc[j];
+            if (o < slots) store_coherent(part4 + ((size_t)(h_lo + o / H4) * p.nsplit + s) * H4 + o % H4, acc[j]);
         }
     } else {
         red_s[tid] = acc[0];
@@ -1211,7 +1329,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
                 reinterpret_cast<float4*>(p.out)[(size_t)(h_lo + tid / H4) * H4 + tid % H4] =
                     make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
             } else {
-                part4[((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4] = a;
+                store_coherent(part4 + ((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4, a);
             }
         }
         if (nact == 1) return;
@@ -1231,7 +1349,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
         }
         return;
     }
-    if (tid < G) p.part_ml[(size_t)(h_lo + tid) * p.nsplit + s] = make_float2(m_s[tid], l_s[tid]);
+    if (tid < G) store_coherent(p.part_ml + (size_t)(h_lo + tid) * p.nsplit + s, make_float2(m_s[tid], l_s[tid]));
+    if (p.fuse) arrive_and_merge<HS>(p, g, h_lo, G, nact);
 }
 
 // Head size 128: a register-only variant.  Each wave is an independent
@@ -1248,10 +1367,6 @@ __device__ __forceinline__ float half_sum(float v) {  // lanes 16-31: sum of 0-3
     v += dpp<kRowMirror>(0.f, v);
     v += dpp<kRowBcast15, 0xa>(0.f, v);
     return v;
-}
-
-__device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
-    return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
 }
 
 template <int GMAX, int U>
@@ -1371,17 +1486,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams pb) {
             const float il = 1.0f / L;
             reinterpret_cast<float4*>(p.out)[(size_t)h * 32 + cc] = make_float4(A.x * il, A.y * il, A.z * il, A.w * il);
         } else {
-            reinterpret_cast<float4*>(p.part_acc)[((size_t)h * p.nsplit + s) * 32 + cc] = A;
-            if (cc == 0) p.part_ml[(size_t)h * p.nsplit + s] = make_float2(M, L);
+            store_coherent(reinterpret_cast<float4*>(p.part_acc) + ((size_t)h * p.nsplit + s) * 32 + cc, A);
+            if (cc == 0) store_coherent(p.part_ml + (size_t)h * p.nsplit + s, make_float2(M, L));
         }
     }
+    if (nact > 1 && p.fuse) arrive_and_merge<HS>(p, g, h_lo, G, nact);
 }
 
-// Exact merge of the split partials of query head blockIdx.x (one block per
-// query head, so a group of 8 heads spreads over 8 blocks).  Wave 0 finds
-// M = max_s m_s and L = sum_s e^{m_s - M} l_s over the splits (lane-strided
-// loads); then every column's float4 is summed over split groups, 8 loads in
-// flight per thread, and the groups are added through LDS.
+// Exact merge of the split partials of query head blockIdx.x, one block per
+// query head, for groups whose partials are too many for one block to fold.
+// Wave 0 finds M = max_s m_s and L = sum_s e^{m_s - M} l_s over the splits
+// (lane-strided loads); then every column's float4 is summed over split
+// groups, 8 loads in flight per thread, and the groups are added through LDS.
 template <int HS>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb) {
     const AttnParams p = seq_view<HS>(pb);
@@ -1692,6 +1808,10 @@ int attn_splits(int hs, int seq_len, int n_kv_heads) {
     return want < 1 ? 1 : want;
 }
 
+#ifndef LD_ATTN_FUSE_FOLDS
+#define LD_ATTN_FUSE_FOLDS 4  // most splits a thread of the merging block folds
+#endif
+
 #ifndef LD_ATTN_REG128
 #define LD_ATTN_REG128 1  // head size 128 takes the register-only kernel
 #endif
@@ -1702,6 +1822,13 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
     const dim3 grid(p.n_kv_heads, p.nsplit, nb), block(kAttnThreads), mgrid(p.n_heads, 1, nb);
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
+    // the last split block of a kv group merges it when each of its threads
+    // folds at most LD_ATTN_FUSE_FOLDS splits (the merge launch costs more than
+    // such a tail); larger groups of partials go to the merge kernel
+    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    p.fuse = p.nsplit > 1 && (p.nsplit + kg - 1) / kg <= LD_ATTN_FUSE_FOLDS;
+    if (p.fuse && !p.arrive) return hipErrorInvalidValue;  // split blocks count their arrivals there
+    const bool merge = p.nsplit > 1 && !p.fuse;
     if (hs == 128 && LD_ATTN_REG128) {
         // 4 key pairs per wave batch for one or two heads per kv head, 2 for
         // larger groups (whose per-batch register and ALU load is larger)
@@ -1713,14 +1840,14 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
             hipLaunchKernelGGL((attn128_kernel<4, 2>), grid, block, 0, s, p);
         else
             hipLaunchKernelGGL((attn128_kernel<8, 2>), grid, block, 0, s, p);
-        if (p.nsplit > 1) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
+        if (merge) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
         return hipGetLastError();
     }
     switch (hs) {
-#define LD_ATTN_CASE(HS, CH)                                                               \
-    case HS:                                                                               \
-        hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);                   \
-        if (p.nsplit > 1) hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p); \
+#define LD_ATTN_CASE(HS, CH)                                                       \
+    case HS:                                                                       \
+        hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);           \
+        if (merge) hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p); \
         break;
         LD_ATTN_CASE(16, 64)
         LD_ATTN_CASE(32, 64)

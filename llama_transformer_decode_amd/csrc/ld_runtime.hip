@@ -132,6 +132,7 @@ struct ld_model {
     // one captured graph per batch size
     int max_batch = 1;
     float *bx = nullptr, *bq = nullptr, *batt = nullptr, *bhb = nullptr, *blogits = nullptr;
+    unsigned* arrive = nullptr;  // (max_batch, n_kv_heads) attention split arrival counts, kept at zero
     float2* bpart_ml = nullptr;
     float* bpart_acc = nullptr;
     float* bsplit = nullptr;         // split-K partials of the batch products
@@ -297,6 +298,7 @@ int launch_step(ld_model* m, Timer* timer) {
             a.out = m->xb;
             a.part_ml = m->part_ml;
             a.part_acc = m->part_acc;
+            a.arrive = m->arrive;
             a.state = m->state;
             a.n_heads = c.n_heads;
             a.n_kv_heads = c.n_kv_heads;
@@ -518,6 +520,7 @@ hipError_t launch_batch_attention(ld_model* m, int n, int l) {
     a.out = m->batt;
     a.part_ml = m->bpart_ml;
     a.part_acc = m->bpart_acc;
+    a.arrive = m->arrive;
     a.state = m->bstate;
     a.n_heads = c.n_heads;
     a.n_kv_heads = c.n_kv_heads;
@@ -881,8 +884,11 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
                 (rc = dalloc(m, &m->blogits, B * V)) ||
                 (rc = dalloc(m, &m->bpart_ml, B * cfg->n_heads * m->nsplit)) ||
                 (rc = dalloc(m, &m->bpart_acc, B * cfg->n_heads * m->nsplit * m->hs)) ||
+                (rc = dalloc(m, &m->arrive, B * cfg->n_kv_heads)) ||
                 (rc = dalloc(m, &m->bstate, B)) || (rc = dalloc(m, &m->btokens, B * cfg->seq_len)))
                 break;
+            e = hipMemset(m->arrive, 0, sizeof(unsigned) * B * cfg->n_kv_heads);
+            if (e != hipSuccess) { rc = fail_hip(e, "hipMemset"); break; }
             // the largest split-K workspace any batch size up to B needs
             const int shapes[5][2] = {{cfg->dim + 2 * m->kv_dim, cfg->dim}, {cfg->dim, cfg->dim},
                                       {2 * cfg->hidden_dim, cfg->dim}, {cfg->dim, cfg->hidden_dim},
@@ -1406,6 +1412,9 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
     StepState* st = nullptr;
     HIP_TRY(tmp.get(&ml, (size_t)n_heads * nsplit));
     HIP_TRY(tmp.get(&acc, (size_t)n_heads * nsplit * head_size));
+    unsigned* arrive = nullptr;
+    HIP_TRY(tmp.get(&arrive, (size_t)n_kv_heads));
+    HIP_TRY(hipMemsetAsync(arrive, 0, sizeof(unsigned) * n_kv_heads, s));
     HIP_TRY(tmp.get(&st, 1));
     StepState hs_state{0, pos, -1, 0};
     HIP_TRY(hipMemcpy(st, &hs_state, sizeof(hs_state), hipMemcpyHostToDevice));
@@ -1416,6 +1425,7 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
     a.out = d_out;
     a.part_ml = ml;
     a.part_acc = acc;
+    a.arrive = arrive;
     a.state = st;
     a.n_heads = n_heads;
     a.n_kv_heads = n_kv_heads;

@@ -141,6 +141,9 @@ ATTN_CASES = [  # (n_heads, n_kv_heads, head_size, pos)
     (6, 4, 48, 511), (32, 32, 128, 0), (32, 32, 128, 31), (32, 32, 128, 32), (32, 32, 128, 33),
     (32, 32, 128, 511), (32, 32, 128, 2047), (64, 8, 128, 0), (64, 8, 128, 3583), (64, 8, 128, 4095),
     (8, 1, 64, 700), (3, 2, 32, 5), (4, 2, 256, 100), (2, 2, 80, 70), (4, 2, 96, 129),
+    # split partials merged by the last block of each kv group: 256 and 512
+    # float4 outputs per group (one and two passes of the block), four splits
+    (8, 2, 256, 90), (16, 2, 256, 70), (64, 8, 128, 200),
 ]
 
 
