@@ -1558,17 +1558,28 @@ struct Tpl {
 
 
 // Ordered by capacity nt*nx float4 (= input floats / 4).  Two groups of
-// weights are live at once (the pipelined loads), so rpi*nx stays near 16.
-// The q/k/v and w1/w3 kernels pair rows and use at least 2 rows per group.
-// (The 1024-thread shape for 8192 < n <= 12288 was the fastest of the shapes
-// timed for the 11008-wide down projection.)
+// weights are live at once (the pipelined loads), so rpi*nx stays at 16 or
+// below.  The q/k/v and w1/w3 kernels pair rows and use at least 2 rows per
+// group.  For 1024 < n <= 4096 and 8192 < n <= 12288 (the 7B shape's
+// products and its 11008-wide down projection) the shapes are the fastest of
+// those timed on a whole greedy decode: 512 x 2 x 2 and 1024 x 3 x 2 (about
+// 1.2% more tokens/s than 256 x 4 x 4 and 1024 x 3 x 4; 256 x 4 x 2 gave
+// 0.8%, 512 x 2 x 1 and 1024 x 3 x 1 less, 1024 x 1 x 2/4 and 512 x 2 x 4
+// 5-6% less).  Smaller groups and more blocks start every weight stream
+// sooner.
+#ifndef LD_GEMV_4096
+#define LD_GEMV_4096 {512, 2, 2}
+#endif
+#ifndef LD_GEMV_12288
+#define LD_GEMV_12288 {1024, 3, 2}
+#endif
 constexpr Tpl kTpl[] = {
-    {64, 1, 4},    // n <= 256
-    {64, 2, 4},    // n <= 512
-    {64, 4, 4},    // n <= 1024
-    {256, 4, 4},   // n <= 4096
-    {256, 8, 2},   // n <= 8192
-    {1024, 3, 4},  // n <= 12288
+    {64, 1, 4},        // n <= 256
+    {64, 2, 4},        // n <= 512
+    {64, 4, 4},        // n <= 1024
+    LD_GEMV_4096,      // n <= 4096
+    {256, 8, 2},       // n <= 8192
+    LD_GEMV_12288,     // n <= 12288
     {512, 14, 1},  // n <= 28672
     {512, 16, 1},  // n <= 32768
 };
