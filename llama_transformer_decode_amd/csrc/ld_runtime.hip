@@ -146,7 +146,8 @@ struct ld_model {
     std::map<int, std::pair<hipGraph_t, hipGraphExec_t>> batch_graphs;
     GemvPlan pq{}, pwo{}, pffn{}, pw2{}, pcls{};
     GemvPlan bpq{}, bpwo{}, bpffn{}, bpw2{}, bpcls{};  // batches of up to kGemvBatch
-    bool bgemv = false;                                  //   (when every shape has a batch plan)
+    bool bgemv = false;                                  //   (when every shape but the down projection has one)
+    bool bgemv_w2 = false;                               //   the down projection has one too
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
     hipGraph_t graph = nullptr;
@@ -534,7 +535,8 @@ hipError_t launch_batch_attention(ld_model* m, int n, int l) {
 
 // A decode step of up to kGemvBatch sequences with the batch GEMV kernels:
 // the single step's launches (each weight streamed once, the RMSNorms fused)
-// with the vectors of all sequences in registers.
+// with the vectors of all sequences in registers.  A down projection wider
+// than the batch kernel's shapes is the split-K matrix-core product instead.
 int launch_batch_step_gemv(ld_model* m, int n) {
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
@@ -592,13 +594,26 @@ int launch_batch_step_gemv(ld_model* m, int n) {
             p.ldo = c.hidden_dim;
             HIP_TRY(gemv_launch(m->bpffn, p, s));
         }
-        {
+        if (m->bgemv_w2) {
             GemvParams p = bparams(m->bhb, c.hidden_dim);
             p.x_resid = m->bx;
             p.n = c.hidden_dim;
             p.rows = c.dim;
             p.w0 = m->w2 + (size_t)l * d * h;
             HIP_TRY(gemv_launch(m->bpw2, p, s));
+        } else {
+            GemmParams g{};
+            g.a = m->bhb;
+            g.lda = c.hidden_dim;
+            g.m = n;
+            g.part = m->bsplit;
+            g.part_floats = m->bsplit_floats;
+            g.n = c.dim;
+            g.k = c.hidden_dim;
+            g.w0 = m->w2 + (size_t)l * d * h;
+            g.out = m->bx;
+            g.ldo = c.dim;
+            HIP_TRY(gemm_launch(G_RESID, g, s));
         }
     }
     {
@@ -904,8 +919,10 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             m->bgemv = gemv_plan_batch(K_QKV, cfg->dim + 2 * m->kv_dim, cfg->dim, &m->bpq) == hipSuccess &&
                        gemv_plan_batch(K_RESID, cfg->dim, cfg->dim, &m->bpwo) == hipSuccess &&
                        gemv_plan_batch(K_SWIGLU, cfg->hidden_dim, cfg->dim, &m->bpffn) == hipSuccess &&
-                       gemv_plan_batch(K_RESID, cfg->dim, cfg->hidden_dim, &m->bpw2) == hipSuccess &&
                        gemv_plan_batch(K_PLAIN, cfg->vocab_size, cfg->dim, &m->bpcls) == hipSuccess;
+            // a hidden width beyond the batch kernel's shapes (the 70B layer's
+            // 28672) takes the split-K product for the down projection alone
+            m->bgemv_w2 = gemv_plan_batch(K_RESID, cfg->dim, cfg->hidden_dim, &m->bpw2) == hipSuccess;
             e = hipHostMalloc((void**)&m->h_bstate, sizeof(StepState) * B, hipHostMallocDefault);
             if (e == hipSuccess)
                 e = hipHostMalloc((void**)&m->h_btokens, sizeof(int32_t) * B * cfg->seq_len, hipHostMallocDefault);

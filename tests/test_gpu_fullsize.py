@@ -152,7 +152,8 @@ def test_long_prefill_equals_token_by_token_decode(big):
 def test_batch_step_at_full_size(big, case):
     # one batched step of several sequences at different installed prefixes, each row against the oracle;
     # 7B-shaped: 4 sequences (the batch GEMV kernels) and 6 (the split-K matrix-core products);
-    # 70B-layer: 2 and 3 sequences (its 28672-wide input has no batch GEMV shape: matrix-core products)
+    # 70B-layer: 2 and 3 sequences (the batch GEMV kernels, with the split-K product for the
+    # 28672-wide down projection, which has no batch GEMV shape)
     cfg, blob, w = big
     lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300]],
                "llama70b_8l": [[4000, 1500], [100, 4095, 2048]]}[cfg.name][case]
