@@ -1921,11 +1921,19 @@ hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblock
     return hipGetLastError();
 }
 
-// 1024 threads of 32 tokens each hold a vocabulary of up to kMaxSampleVocab;
-// a larger one is only ever chosen from greedily (the kernel checks)
+// The smallest block whose NT threads of E tokens hold the vocabulary: every
+// pass of a draw is a block-wide sum, whose cost grows with the waves, and the
+// index-order walk takes log2(E) of them.  1024 threads of 32 tokens hold up
+// to kMaxSampleVocab; a larger vocabulary is only ever chosen from greedily
+// (the kernel checks).
 hipError_t next_token_launch(const NextTokenParams& p, hipStream_t s) {
     static_assert(kMaxSampleVocab == 1024 * 32, "sampler register layout");
-    hipLaunchKernelGGL((next_token_kernel<1024, 32>), dim3(1), dim3(1024), 0, s, p);
+    if (p.n <= 256)
+        hipLaunchKernelGGL((next_token_kernel<256, 1>), dim3(1), dim3(256), 0, s, p);
+    else if (p.n <= 1024 * 8)
+        hipLaunchKernelGGL((next_token_kernel<1024, 8>), dim3(1), dim3(1024), 0, s, p);
+    else
+        hipLaunchKernelGGL((next_token_kernel<1024, 32>), dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

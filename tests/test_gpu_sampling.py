@@ -81,7 +81,7 @@ def test_temperature_and_greedy():
         assert op_sample(t, -1.0, 0.0, coin) == 1
 
 
-@pytest.mark.parametrize("n", [1, 3, 1000, 1023, 1025, 4097, 32000, 32768])
+@pytest.mark.parametrize("n", [1, 3, 256, 257, 1000, 1023, 1025, 4097, 8192, 8193, 32000, 32768])
 @pytest.mark.parametrize("T,topp", [(1.0, 0.0), (0.6, 0.0), (1.0, 0.9), (0.8, 0.5), (1.5, 0.95)])
 def test_random_logits_many_coins(n, T, topp):
     rng = np.random.default_rng(n * 7 + int(T * 10) + int(topp * 100))
