@@ -1038,15 +1038,24 @@ __device__ __forceinline__ void group_of(int g, int H, int KV, int& h_lo, int& G
     G = ((g + 1) * H + KV - 1) / KV - h_lo;    // query heads with floor(h KV / H) = g
 }
 
-#ifndef LD_ATTN_MIN_TILES
-#define LD_ATTN_MIN_TILES 2  // fewest key tiles a split takes (below that one split serves all keys)
+// Fewest keys a split takes (below that one split serves all keys).  64 keys
+// measured best for both kernels: one-tile (32-key) splits of the head-size
+// 128 kernel cost 0.4% at positions below 512 (7B shape), and one-tile
+// (64-key) splits of the generic kernel gained 7% over two-tile ones on the
+// GQA-small workload.
+#ifndef LD_ATTN_MIN_KEYS
+#define LD_ATTN_MIN_KEYS 64
 #endif
 
-// Tiles of a position: `per` consecutive tiles per split (at least min_tiles),
-// `nact` splits in use.
+__host__ __device__ constexpr int attn_min_tiles(int ch) {
+    return (LD_ATTN_MIN_KEYS + ch - 1) / ch;
+}
+
+// Tiles of a position: `per` consecutive tiles per split (at least
+// attn_min_tiles), `nact` splits in use.
 __device__ __forceinline__ void split_of(int n, int ch, int nsplit, int& tiles, int& per, int& nact) {
     tiles = (n + ch - 1) / ch;
-    per = max((tiles + nsplit - 1) / nsplit, LD_ATTN_MIN_TILES);
+    per = max((tiles + nsplit - 1) / nsplit, attn_min_tiles(ch));
     nact = (tiles + per - 1) / per;
 }
 
@@ -1827,9 +1836,9 @@ int attn_splits(int hs, int seq_len, int n_kv_heads) {
     if ((long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES) return 1;
     const int tiles = (seq_len + ch - 1) / ch;
     // about LD_ATTN_BLOCKS blocks at the longest context (two per compute
-    // unit), and no split shorter than LD_ATTN_MIN_TILES tiles
+    // unit), and no split shorter than attn_min_tiles(ch) tiles
     int want = (LD_ATTN_BLOCKS + n_kv_heads - 1) / n_kv_heads;
-    const int most = (tiles + LD_ATTN_MIN_TILES - 1) / LD_ATTN_MIN_TILES;
+    const int most = (tiles + attn_min_tiles(ch) - 1) / attn_min_tiles(ch);
     if (want > most) want = most;
     return want < 1 ? 1 : want;
 }
