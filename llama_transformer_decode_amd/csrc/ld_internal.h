@@ -199,7 +199,7 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s,
                        hipEvent_t stop = nullptr);
 
 int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)
-int attn_splits(int head_size, int seq_len, int n_kv_heads);  // grid.y of the attention kernel
+int attn_splits(int head_size, int seq_len, int n_heads, int n_kv_heads);  // grid.y of the attention kernel
 hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention (+ merge)
 
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);

@@ -1828,24 +1828,39 @@ int attn_chunk(int hs) {
 #define LD_ATTN_ONE_BLOCK_BYTES (128 << 10)
 #endif
 
-int attn_splits(int hs, int seq_len, int n_kv_heads) {
+#ifndef LD_ATTN_FUSE_FOLDS
+#define LD_ATTN_FUSE_FOLDS 4  // most splits a thread of the merging block folds
+#endif
+
+// Whether the last split block of a kv group merges the group's partials:
+// when each thread of that block folds at most LD_ATTN_FUSE_FOLDS splits (the
+// merge launch costs more than such a tail).  Larger groups of partials go to
+// the merge kernel.
+bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit) {
+    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
+    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    return nsplit > 1 && (nsplit + kg - 1) / kg <= LD_ATTN_FUSE_FOLDS;
+}
+
+int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
     const int ch = attn_chunk(hs);
     if (!ch) return 0;
-    // a kv head's whole cache is small enough for one block: no split, so no
-    // merge launch (a launch costs ~4 us even with nothing to do)
-    if ((long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES) return 1;
     const int tiles = (seq_len + ch - 1) / ch;
     // about LD_ATTN_BLOCKS blocks at the longest context (two per compute
     // unit), and no split shorter than attn_min_tiles(ch) tiles
     int want = (LD_ATTN_BLOCKS + n_kv_heads - 1) / n_kv_heads;
     const int most = (tiles + attn_min_tiles(ch) - 1) / attn_min_tiles(ch);
     if (want > most) want = most;
-    return want < 1 ? 1 : want;
+    if (want < 1) want = 1;
+    // where the partials would need the merge launch (~4 us even with nothing
+    // to do) and a kv head's whole cache fits one block, one block per kv head
+    // serves it.  A split merged by its last block beats one block per kv head
+    // (stories15M-shaped workload: 6% more tokens/s).
+    if (want > 1 && !attn_fused(hs, n_heads, n_kv_heads, want) &&
+        (long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES)
+        return 1;
+    return want;
 }
-
-#ifndef LD_ATTN_FUSE_FOLDS
-#define LD_ATTN_FUSE_FOLDS 4  // most splits a thread of the merging block folds
-#endif
 
 #ifndef LD_ATTN_REG128
 #define LD_ATTN_REG128 1  // head size 128 takes the register-only kernel
@@ -1857,11 +1872,7 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
     const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
     const dim3 grid(p.n_kv_heads, p.nsplit, nb), block(kAttnThreads), mgrid(p.n_heads, 1, nb);
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
-    // the last split block of a kv group merges it when each of its threads
-    // folds at most LD_ATTN_FUSE_FOLDS splits (the merge launch costs more than
-    // such a tail); larger groups of partials go to the merge kernel
-    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
-    p.fuse = p.nsplit > 1 && (p.nsplit + kg - 1) / kg <= LD_ATTN_FUSE_FOLDS;
+    p.fuse = attn_fused(hs, p.n_heads, p.n_kv_heads, p.nsplit);
     if (p.fuse && !p.arrive) return hipErrorInvalidValue;  // split blocks count their arrivals there
     const bool merge = p.nsplit > 1 && !p.fuse;
     if (hs == 128 && LD_ATTN_REG128) {

@@ -832,7 +832,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         if (e != hipSuccess) { rc = fail_hip(e, "hipGetDevice"); break; }
         m->hs = cfg->dim / cfg->n_heads;
         m->kv_dim = cfg->dim * cfg->n_kv_heads / cfg->n_heads;
-        m->nsplit = attn_splits(m->hs, cfg->seq_len, cfg->n_kv_heads);
+        m->nsplit = attn_splits(m->hs, cfg->seq_len, cfg->n_heads, cfg->n_kv_heads);
 
         // weight pointers: 64-bit offsets into the blob
         const float* w = static_cast<const float*>(d_weights);
@@ -1422,7 +1422,7 @@ int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int3
     if (pos < 0) return LD_E_RANGE;
     if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc)) return LD_E_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const int nsplit = attn_splits(head_size, pos + 1, n_kv_heads);
+    const int nsplit = attn_splits(head_size, pos + 1, n_heads, n_kv_heads);
     Temps tmp;
     float2* ml = nullptr;
     float* acc = nullptr;
