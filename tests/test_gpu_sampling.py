@@ -259,6 +259,46 @@ def test_generation_is_deterministic_and_graph_equals_direct():
     assert np.array_equal(a, a2) and np.array_equal(a, c)
 
 
+@pytest.mark.parametrize("graph", [True, False])
+@pytest.mark.parametrize("name", ["tiny", "gqa_small"])
+def test_greedy_prompt_and_stop_token_match_the_oracle(name, graph):
+    # at temperature 0: prompt forcing, the greedy steps after it and a stop
+    # token must equal the oracle's loop, with and without graph replay
+    cfg, b, w = blob_of(name)
+    prompt = [int(t) for t in synth.prefill_tokens(cfg, 6)]
+    n = 24
+    with pkg.Model(cfg, w, graph=graph) as m:
+        got = m.generate_sampled(prompt, 0, n, 0.0, 0.0, -1, None)
+        assert got.size == n and np.array_equal(got[:len(prompt) - 1], prompt[1:])
+        matched, _ = compare_generation(cfg, b, got, prompt, 0, 0.0, 0.0, np.zeros(n, np.float32))
+        assert matched == n
+        # stop at the first greedy token that is new to the run
+        j = next((i for i in range(len(prompt), n) if got[i] not in got[:i]), None)
+        if j is not None:
+            m.reset()
+            stopped = m.generate_sampled(prompt, 0, n, 0.0, 0.0, int(got[j]), None)
+            assert np.array_equal(stopped, got[:j + 1])
+
+
+def test_greedy_and_sampled_calls_alternate_on_one_model():
+    # the control block changes call by call under one captured step:
+    # switching between greedy and sampled calls changes no result
+    cfg, b, w = blob_of("stories15m")
+    coins = synth.coins(16, 5, 5)
+    with pkg.Model(cfg, w) as m:
+        g1 = m.generate(1, 0, 16)
+        s1 = m.generate_sampled([int(g1[-1])], 16, 16, 0.9, 0.9, -1, coins)
+        g2 = m.generate(int(s1[-1]), 32, 16)
+    with pkg.Model(cfg, w) as a, pkg.Model(cfg, w) as c:
+        assert np.array_equal(a.generate(1, 0, 16), g1)
+        assert np.array_equal(a.generate_sampled([int(g1[-1])], 16, 16, 0.9, 0.9, -1, coins), s1)
+        c.generate(1, 0, 16)
+        c.generate_sampled([int(g1[-1])], 16, 16, 0.9, 0.9, -1, coins)
+        assert np.array_equal(c.generate(int(s1[-1]), 32, 16), g2)
+    matched, _ = compare_generation(cfg, b, g1, [1], 0, 0.0, 0.0, np.zeros(16, np.float32))
+    assert matched == 16
+
+
 def test_generate_range_errors():
     cfg, b, w = blob_of("tiny")
     with pkg.Model(cfg, w) as m:
