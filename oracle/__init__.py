@@ -25,7 +25,7 @@ if os.environ.get("ORACLE_LIB"):
     _SOS[False] = os.environ["ORACLE_LIB"]
 _libs: dict = {}
 
-_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared"]
+_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared", "-pthread"]
 
 
 def build(force: bool = True) -> None:
@@ -63,6 +63,7 @@ def _load(page: bool = False):
             "oracle_blob_floats": ([_P, _P], ctypes.c_int64),
             "oracle_rmsnorm": ([_P, _P, _P, _I, ctypes.c_double], None),
             "oracle_matvec": ([_P, _P, _P, _I, _I], None),
+            "oracle_set_threads": ([_I], None),
             "oracle_rope": ([_P, _I, _I, _I, ctypes.c_double], None),
             "oracle_kv_head": ([_I, _I, _I], _I),
             "oracle_attention": ([_P, _P, _P, _P, _I, _I, _I, _I], None),
@@ -106,6 +107,12 @@ def _opt(cfg, shared=None, eps=None, theta=None):
 
 def page_literal(page: bool = False) -> bool:
     return bool(_load(page).oracle_page_literal())
+
+
+def set_threads(n: int, page: bool = False) -> None:
+    """Threads over which matrix rows and attention heads are shared out (default 1).
+    Results are bit-identical for every count; only the wall time changes."""
+    _load(page).oracle_set_threads(int(n))
 
 
 def blob_floats(cfg, page: bool = False) -> int:

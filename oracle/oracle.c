@@ -14,11 +14,12 @@
  *     q is rotated in every head, k in its n_kv_heads heads.
  *   - query head h reads key/value head floor(h*n_kv/n_heads), i.e. the page's
  *     h / kv_mul with kv_mul = n_heads/n_kv_heads taken as a real ratio.
- *   - argmax returns the lowest index among equal maxima (strict '>' scan).
+ *   - argmax returns the lowest index among equal maxima.
  */
 #include "oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -91,21 +92,34 @@ int64_t oracle_blob_floats(const oracle_config* c, const oracle_options* o) {
     return map_weights(c, o, NULL, NULL);
 }
 
-/* RMSNorm: "run.c 逐行解讀" §4 RMSNorm, weight * x / sqrt(mean(x^2) + eps);
- * same as rmsnorm() of the "run.c" page. */
+/* RMSNorm ("run.c 逐行解讀" §4 RMSNorm; rmsnorm() of the "run.c" page): the
+ * root mean square of x, with eps added to the mean square under the root,
+ * divides every element, and the gain then scales it element-wise. */
 void oracle_rmsnorm(float* out, const float* x, const float* g, int n, double eps) {
-    acc_t ss = 0;
-    for (int j = 0; j < n; ++j) ss += (acc_t)x[j] * (acc_t)x[j];
-    ss /= (acc_t)n;
-    ss += (acc_t)eps;
-    acc_t r = (acc_t)1 / ACC_SQRT(ss);
-    for (int j = 0; j < n; ++j) out[j] = (float)((acc_t)g[j] * (r * (acc_t)x[j]));
+    acc_t sum_sq = 0;
+    for (int j = 0; j < n; ++j) sum_sq += (acc_t)x[j] * (acc_t)x[j];
+    const acc_t rms = ACC_SQRT(sum_sq / (acc_t)n + (acc_t)eps);
+    for (int j = 0; j < n; ++j) {
+        const acc_t unit = (acc_t)x[j] / rms;
+        out[j] = (float)((acc_t)g[j] * unit);
+    }
 }
 
 /* Matrix-vector product: "run.c 逐行解讀" §4 Matmul, W(d,n) @ x(n) -> out(d),
- * element (i, j) of W at w[i*n + j]. */
-void oracle_matvec(float* out, const float* w, const float* x, int d, int n) {
-    for (int i = 0; i < d; ++i) {
+ * element (i, j) of W at w[i*n + j].  Output i is the dot product of row i
+ * with x, summed in index order.
+ *
+ * The rows are independent, so oracle_set_threads(t) lets t threads share
+ * them out in contiguous ranges.  Each output is still the same sequential
+ * sum, so the result is bit-identical for every thread count (default 1). */
+static int g_threads = 1;
+
+void oracle_set_threads(int t) { g_threads = t < 1 ? 1 : (t > ORACLE_MAX_THREADS ? ORACLE_MAX_THREADS : t); }
+
+/* rows i0..i1-1 of out(d) = W(d, n) x(n) */
+static void matvec_rows(float* out, const float* w, const float* x, int d, int n, int i0, int i1) {
+    (void)d;
+    for (int i = i0; i < i1; ++i) {
         const float* row = w + (int64_t)i * n;
         acc_t s = 0;
         for (int j = 0; j < n; ++j) s += (acc_t)row[j] * (acc_t)x[j];
@@ -113,25 +127,59 @@ void oracle_matvec(float* out, const float* w, const float* x, int d, int n) {
     }
 }
 
-/* RoPE: "run.c 逐行解讀" §4 step 2d.  Within each head the element at offset
- * 2j pairs with 2j+1; the pair turns by pos * freq with
- * freq = 1 / theta^(2j / head_size), as the complex product (v0 + i v1) e^{i pos freq}. */
+typedef struct {
+    float* out;
+    const float* w;
+    const float* x;
+    int d, n, i0, i1;
+} rows_job;
+
+static void* rows_thread(void* p) {
+    const rows_job* j = (const rows_job*)p;
+    matvec_rows(j->out, j->w, j->x, j->d, j->n, j->i0, j->i1);
+    return NULL;
+}
+
+void oracle_matvec(float* out, const float* w, const float* x, int d, int n) {
+    int t = g_threads;
+    if ((int64_t)d * n < ((int64_t)1 << 20) || d < 2 * t) t = 1;
+    if (t == 1) {
+        matvec_rows(out, w, x, d, n, 0, d);
+        return;
+    }
+    rows_job jobs[ORACLE_MAX_THREADS];
+    pthread_t tid[ORACLE_MAX_THREADS];
+    int started[ORACLE_MAX_THREADS];
+    for (int k = 0; k < t; ++k) {
+        jobs[k] = (rows_job){out, w, x, d, n, (int)((int64_t)d * k / t), (int)((int64_t)d * (k + 1) / t)};
+        started[k] = k > 0 && pthread_create(&tid[k], NULL, rows_thread, &jobs[k]) == 0;
+        if (k > 0 && !started[k]) rows_thread(&jobs[k]);
+    }
+    rows_thread(&jobs[0]);
+    for (int k = 1; k < t; ++k)
+        if (started[k]) pthread_join(tid[k], NULL);
+}
+
+/* RoPE ("run.c 逐行解讀" §4 step 2d; the rotary embedding of the R/Keras
+ * page): in every head, pair j = (v[2j], v[2j+1]) is multiplied by the 2x2
+ * rotation matrix of the angle a_j = pos * theta^(-2j / head_size),
+ *     [ cos a_j   -sin a_j ]
+ *     [ sin a_j    cos a_j ].
+ * The double build takes the angle, cos and sin in double; the page-literal
+ * build takes them in fp32 (powf, cosf, sinf), as the pages do. */
 void oracle_rope(float* v, int n_heads, int head_size, int pos, double theta) {
-    for (int h = 0; h < n_heads; ++h) {
-        float* vh = v + (int64_t)h * head_size;
-        for (int i = 0; i < head_size; i += 2) {
+    for (int j = 0; 2 * j < head_size; ++j) {
 #ifdef ORACLE_PAGE_LITERAL
-            float freq = 1.0f / powf((float)theta, (float)i / (float)head_size);
-            float ang = (float)pos * freq;
-            float fcr = cosf(ang), fci = sinf(ang);
+        const float a = (float)pos * (1.0f / powf((float)theta, (float)(2 * j) / (float)head_size));
+        const acc_t R[2][2] = {{cosf(a), -sinf(a)}, {sinf(a), cosf(a)}};
 #else
-            double freq = 1.0 / pow(theta, (double)i / (double)head_size);
-            double ang = (double)pos * freq;
-            double fcr = cos(ang), fci = sin(ang);
+        const double a = (double)pos * pow(theta, -(double)(2 * j) / (double)head_size);
+        const acc_t R[2][2] = {{cos(a), -sin(a)}, {sin(a), cos(a)}};
 #endif
-            acc_t v0 = vh[i], v1 = vh[i + 1];
-            vh[i] = (float)(v0 * fcr - v1 * fci);
-            vh[i + 1] = (float)(v0 * fci + v1 * fcr);
+        for (int h = 0; h < n_heads; ++h) {
+            float* pair = v + (int64_t)h * head_size + 2 * j;
+            const acc_t in[2] = {pair[0], pair[1]};
+            for (int r = 0; r < 2; ++r) pair[r] = (float)(R[r][0] * in[0] + R[r][1] * in[1]);
         }
     }
 }
@@ -141,16 +189,25 @@ int oracle_kv_head(int h, int n_heads, int n_kv_heads) { return (int)(((int64_t)
 /* Causal multi-head attention with grouped KV heads: "run.c 逐行解讀" §4
  * step 2e.  For every query head: scores q.k_t / sqrt(head_size) for t = 0..pos,
  * softmax with the maximum subtracted (§4 Softmax), then the weighted sum of
- * the value rows. */
-void oracle_attention(float* out, const float* q, const float* kc, const float* vc, int n_heads,
-                      int n_kv_heads, int head_size, int pos) {
-    const int64_t kv_dim = (int64_t)head_size * n_kv_heads;
+ * the value rows.  Heads are independent; like the matrix rows above they may
+ * be shared out among the oracle_set_threads() threads, with results that do
+ * not depend on the thread count. */
+typedef struct {
+    float* out;
+    const float *q, *kc, *vc;
+    int n_heads, n_kv_heads, head_size, pos, h0, h1;
+} heads_job;
+
+static void* attend_heads(void* p) {
+    const heads_job* J = (const heads_job*)p;
+    const int head_size = J->head_size, pos = J->pos;
+    const int64_t kv_dim = (int64_t)head_size * J->n_kv_heads;
     acc_t* att = (acc_t*)malloc(sizeof(acc_t) * (size_t)(pos + 1));
-    for (int h = 0; h < n_heads; ++h) {
-        const int g = oracle_kv_head(h, n_heads, n_kv_heads);
-        const float* qh = q + (int64_t)h * head_size;
+    for (int h = J->h0; h < J->h1; ++h) {
+        const int g = oracle_kv_head(h, J->n_heads, J->n_kv_heads);
+        const float* qh = J->q + (int64_t)h * head_size;
         for (int t = 0; t <= pos; ++t) {
-            const float* k = kc + (int64_t)t * kv_dim + (int64_t)g * head_size;
+            const float* k = J->kc + (int64_t)t * kv_dim + (int64_t)g * head_size;
             acc_t s = 0;
             for (int i = 0; i < head_size; ++i) s += (acc_t)qh[i] * (acc_t)k[i];
             att[t] = s / ACC_SQRT((acc_t)head_size);
@@ -167,34 +224,55 @@ void oracle_attention(float* out, const float* q, const float* kc, const float* 
         for (int i = 0; i < head_size; ++i) {
             acc_t acc = 0;
             for (int t = 0; t <= pos; ++t)
-                acc += att[t] * (acc_t)vc[(int64_t)t * kv_dim + (int64_t)g * head_size + i];
-            out[(int64_t)h * head_size + i] = (float)acc;
+                acc += att[t] * (acc_t)J->vc[(int64_t)t * kv_dim + (int64_t)g * head_size + i];
+            J->out[(int64_t)h * head_size + i] = (float)acc;
         }
     }
     free(att);
+    return NULL;
 }
 
-/* SwiGLU gate: "run.c 逐行解讀" §4 step 2h, silu(u) = u * (1 / (1 + e^-u)),
- * multiplied element-wise by the w3 branch. */
+void oracle_attention(float* out, const float* q, const float* kc, const float* vc, int n_heads,
+                      int n_kv_heads, int head_size, int pos) {
+    int t = g_threads;
+    if ((int64_t)n_heads * head_size * (pos + 1) < ((int64_t)1 << 18) || n_heads < 2 * t) t = 1;
+    heads_job jobs[ORACLE_MAX_THREADS];
+    pthread_t tid[ORACLE_MAX_THREADS];
+    int started[ORACLE_MAX_THREADS];
+    for (int k = 0; k < t; ++k) {
+        jobs[k] = (heads_job){out, q, kc, vc, n_heads, n_kv_heads, head_size, pos, n_heads * k / t,
+                              n_heads * (k + 1) / t};
+        started[k] = k > 0 && pthread_create(&tid[k], NULL, attend_heads, &jobs[k]) == 0;
+        if (k > 0 && !started[k]) attend_heads(&jobs[k]);
+    }
+    attend_heads(&jobs[0]);
+    for (int k = 1; k < t; ++k)
+        if (started[k]) pthread_join(tid[k], NULL);
+}
+
+/* The logistic function sigma(u) = 1 / (1 + e^-u).  For u far below zero
+ * e^-u overflows to infinity and sigma(u) is 0, never NaN. */
+static acc_t logistic(acc_t u) { return (acc_t)1 / ((acc_t)1 + ACC_EXP(-u)); }
+
+/* SwiGLU ("run.c 逐行解讀" §4 step 2h; the FeedForward layer of the R/Keras
+ * page): the SiLU of the w1 branch, silu(u) = u * sigma(u), times the w3
+ * branch, element by element. */
 void oracle_swiglu(float* hb, const float* h1, const float* h3, int n) {
     for (int i = 0; i < n; ++i) {
-        acc_t u = h1[i];
-        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));
-        u *= (acc_t)h3[i];
-        hb[i] = (float)u;
+        const acc_t gate = (acc_t)h1[i] * logistic((acc_t)h1[i]);
+        hb[i] = (float)(gate * (acc_t)h3[i]);
     }
 }
 
-/* Greedy choice: argmax() of the "run.c" page, a strict '>' scan. */
+/* Greedy choice (argmax() of the "run.c" page): the largest logit, and of the
+ * indices holding it the lowest one. */
 int oracle_argmax(const float* v, int n) {
-    int best = 0;
-    float bv = v[0];
+    float top = v[0];
     for (int i = 1; i < n; ++i)
-        if (v[i] > bv) {
-            bv = v[i];
-            best = i;
-        }
-    return best;
+        if (v[i] > top) top = v[i];
+    for (int i = 0; i < n; ++i)
+        if (v[i] == top) return i;
+    return 0;
 }
 
 typedef struct {

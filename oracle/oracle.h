@@ -51,6 +51,13 @@ void oracle_rmsnorm(float* out, const float* x, const float* g, int n, double ep
 /* out(d) = W(d, n) x(n). */
 void oracle_matvec(float* out, const float* w, const float* x, int d, int n);
 
+/* Threads over which matrix rows and attention heads are shared out (1 by
+ * default, at most ORACLE_MAX_THREADS).  Every output is computed the same way
+ * whatever the count, so results are bit-identical; only the wall time changes.
+ * Process-wide; not to be changed while another thread is inside the oracle. */
+#define ORACLE_MAX_THREADS 64
+void oracle_set_threads(int t);
+
 /* Rotate adjacent pairs (2j, 2j+1) of the first n_heads heads of v (head_size
  * each) by the angle pos * theta^(-2j/head_size).  In place. */
 void oracle_rope(float* v, int n_heads, int head_size, int pos, double theta);

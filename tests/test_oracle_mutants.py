@@ -17,13 +17,14 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 MUTANTS = {
     "causal_range_off_by_one": ("for (int t = 0; t <= pos; ++t) {\n            const float* k", "for (int t = 0; t < pos; ++t) {\n            const float* k"),
     "attention_scale_dropped": ("att[t] = s / ACC_SQRT((acc_t)head_size);", "att[t] = s;"),
-    "rmsnorm_eps_dropped": ("ss += (acc_t)eps;", ""),
-    "rmsnorm_sum_not_mean": ("ss /= (acc_t)n;", ""),
-    "rope_sign_flipped": ("vh[i] = (float)(v0 * fcr - v1 * fci);", "vh[i] = (float)(v0 * fcr + v1 * fci);"),
-    "rope_frequency_index": ("double freq = 1.0 / pow(theta, (double)i / (double)head_size);",
-                             "double freq = 1.0 / pow(theta, (double)(i / 2) / (double)head_size);"),
-    "swiglu_branches_swapped": ("acc_t u = h1[i];\n        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));\n        u *= (acc_t)h3[i];",
-                                "acc_t u = h3[i];\n        u *= (acc_t)1 / ((acc_t)1 + ACC_EXP(-u));\n        u *= (acc_t)h1[i];"),
+    "rmsnorm_eps_dropped": ("sum_sq / (acc_t)n + (acc_t)eps", "sum_sq / (acc_t)n"),
+    "rmsnorm_sum_not_mean": ("sum_sq / (acc_t)n + (acc_t)eps", "sum_sq + (acc_t)eps"),
+    "rope_sign_flipped": ("const acc_t R[2][2] = {{cos(a), -sin(a)}, {sin(a), cos(a)}};",
+                          "const acc_t R[2][2] = {{cos(a), sin(a)}, {sin(a), cos(a)}};"),
+    "rope_frequency_index": ("pow(theta, -(double)(2 * j) / (double)head_size)",
+                             "pow(theta, -(double)j / (double)head_size)"),
+    "swiglu_branches_swapped": ("const acc_t gate = (acc_t)h1[i] * logistic((acc_t)h1[i]);\n        hb[i] = (float)(gate * (acc_t)h3[i]);",
+                                "const acc_t gate = (acc_t)h3[i] * logistic((acc_t)h3[i]);\n        hb[i] = (float)(gate * (acc_t)h1[i]);"),
     "attention_residual_overwrites": ("add_into(x, xb2, dim);", "memcpy(x, xb2, sizeof(float) * (size_t)dim);"),
     "ffn_residual_dropped": ("oracle_matvec(xb, w.w2 + lw * dim * hidden, hb, dim, hidden);\n        add_into(x, xb, dim);",
                              "oracle_matvec(xb, w.w2 + lw * dim * hidden, hb, dim, hidden);"),
@@ -31,7 +32,8 @@ MUTANTS = {
                                "return h / (n_heads / n_kv_heads) < n_kv_heads ? h / (n_heads / n_kv_heads) : n_kv_heads - 1;"),
     "matvec_transposed": ("for (int j = 0; j < n; ++j) s += (acc_t)row[j] * (acc_t)x[j];",
                           "for (int j = 0; j < n; ++j) s += (acc_t)w[(int64_t)j * d + i] * (acc_t)x[j];"),
-    "argmax_last_maximum": ("if (v[i] > bv) {", "if (v[i] >= bv) {"),
+    "argmax_last_maximum": ("for (int i = 0; i < n; ++i)\n        if (v[i] == top) return i;",
+                            "for (int i = n - 1; i >= 0; --i)\n        if (v[i] == top) return i;"),
     "key_rope_skipped": ("oracle_rope(krow, KV, hs, pos, o->rope_theta);", ""),
     "ffn_norm_uses_attention_gain": ("oracle_rmsnorm(xb, x, w.rms_ffn + lw * dim, dim, o->norm_eps);",
                                      "oracle_rmsnorm(xb, x, w.rms_att + lw * dim, dim, o->norm_eps);"),
@@ -59,7 +61,7 @@ def test_pins_reject_mutant(name, tmp_path):
     mut = tmp_path / "oracle_mut.c"
     mut.write_text(src.replace(old, new))
     so = tmp_path / "liboracle_mut.so"
-    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared",
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fPIC", "-shared", "-pthread",
                     "-I", os.path.join(ROOT, "oracle"), str(mut), "-o", str(so), "-lm"], check=True)
     env = dict(os.environ, ORACLE_LIB=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +

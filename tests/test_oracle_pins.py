@@ -400,3 +400,22 @@ def test_forward_rejects_out_of_range_arguments():
     for tok, pos in ((-1, 0), (c.vocab_size, 0), (0, -1), (0, c.seq_len)):
         with pytest.raises(ValueError):
             oracle.forward(c, blob, kv, tok, pos)
+
+
+# ----------------------------------------------------------------------------- thread count
+
+def test_thread_count_does_not_change_a_bit():
+    # rows and heads shared out among threads: every output is the same sequential sum,
+    # so a generation must be bit-identical for any thread count (the stored full-size
+    # runs were made with several threads)
+    cfg = synth.CONFIGS["gqa_small"].replace(seq_len=48)
+    blob = synth.make_blob(cfg)
+    runs = []
+    try:
+        for t in (1, 2, 5, 7):
+            oracle.set_threads(t)
+            runs.append(oracle.generate(cfg, blob, oracle.KVCache(cfg), 1, 0, 48, keep_logits=True))
+    finally:
+        oracle.set_threads(1)
+    for toks, logits in runs[1:]:
+        assert np.array_equal(toks, runs[0][0]) and np.array_equal(logits, runs[0][1])
