@@ -104,18 +104,159 @@ def load_traffic(kernel: str, workload: str):
 START = {"llama70b_8l": 3584}
 
 
-def windows_for(seq_len: int, steps: int, width: int = 16, start: int = 0):
-    """Chunk boundaries (absolute positions) of the timed generation: 16-step
-    windows at the start, around position 511 (when inside the range) and at
-    the end, so per-position rates come from the same timed pass."""
-    end = start + steps
-    marks = {start, min(start + width, end), end}
-    if start < 504 and end > 520:
-        marks |= {504, 520}
-    if steps > 2 * width:
-        marks.add(end - width)
-    b = sorted(m for m in marks if start <= m <= end)
-    return list(zip(b[:-1], b[1:]))
+def windows_for(seq_len: int, start: int = 0, width: int = 16):
+    """16-step windows whose rates are reported on their own, whatever the
+    timed step count: the first positions of the decode, positions 504-519
+    (around the 512th token) where the context reaches them, and the last 16
+    positions of the context."""
+    marks = {start, seq_len - width}
+    if start <= 504 and 520 <= seq_len:
+        marks.add(504)
+    return [(a, min(a + width, seq_len)) for a in sorted(m for m in marks if start <= m < seq_len)]
+
+
+def median(xs):
+    ys = sorted(xs)
+    k = len(ys)
+    return ys[k // 2] if k % 2 else 0.5 * (ys[k // 2 - 1] + ys[k // 2])
+
+
+def fill_cache(model, cfg, start: int) -> int:
+    """Reset the cache and fill rows 0..start-1 (the 70B-layer workload's seeded
+    prompt, through forward calls); returns the first token to decode."""
+    import synth
+    model.reset()
+    if not start:
+        return 1
+    prompt = synth.prefill_tokens(cfg, start)
+    for p in range(start):
+        model.forward_async(int(prompt[p]), p)
+    return model.argmax_last()
+
+
+def timed_generations(model, tok: int, pos: int, n: int, reps: int, torch):
+    """reps timed greedy generations of n steps from (tok, pos).  Generation is
+    deterministic, so every repeat rewrites the same cache rows with the same
+    values and takes the same tokens.  Returns (tokens, seconds per repeat)."""
+    times, toks = [], None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks = model.generate(tok, pos, n)
+        times.append(time.perf_counter() - t0)
+    return toks, times
+
+
+def kernel_table(cfg, stats, pos_list):
+    out = {}
+    for s in stats:
+        if s["launches"]:
+            avg_ms = s["total_ms"] / s["launches"]
+            byt = kernel_bytes(cfg, s["name"], pos_list)
+            out[s["name"]] = {"launches": s["launches"], "avg_us": round(avg_ms * 1e3, 2),
+                              "bytes_per_launch": int(byt), "GBps": round(byt / (avg_ms * 1e-3) / 1e9, 1),
+                              "share_of_time": round(s["total_ms"], 3)}
+    tot = sum(k["share_of_time"] for k in out.values()) or 1.0
+    for k in out.values():
+        k["share_of_time"] = round(k["share_of_time"] / tot, 4)
+    return out
+
+
+def decode_legs(model, cfg, start: int, steps: int, reps: int, torch, kernel_timing: bool = True):
+    """The timed decode of one workload on a model whose weights are resident:
+    `steps` greedy steps from `start` (the first token after the cache fill),
+    timed `reps` times (the median is the value); the per-position windows,
+    each timed `reps` times after decoding up to it untimed; and the kernel
+    durations of the timed positions and of each window.  Returns a dict."""
+    S = cfg.seq_len
+    first_tok = fill_cache(model, cfg, start)
+    torch.cuda.synchronize()
+    span = S - start
+    passes = [span] * (steps // span) + ([steps % span] if steps % span else [])
+    rep_times = []
+    for _ in range(reps):
+        t_rep = 0.0
+        for i, n_pass in enumerate(passes):
+            if i:  # more steps than positions: a fresh pass over the context (untimed refill)
+                fill_cache(model, cfg, start)
+            _, dts = timed_generations(model, first_tok, start, n_pass, 1, torch)
+            t_rep += dts[0]
+        rep_times.append(t_rep)
+    if len(passes) > 1:
+        fill_cache(model, cfg, start)
+    t_med = median(rep_times)
+    pos_all = [start + (i % span) for i in range(steps)]
+    total_bytes = sum(bytes_per_token(cfg, p) for p in pos_all)
+    out = {"steps": steps, "positions": [start, start + min(steps, span) - 1], "repeats": reps,
+           "seconds": [round(t, 6) for t in rep_times], "tok_s": round(steps / t_med, 2),
+           "tok_s_min": round(steps / max(rep_times), 2), "tok_s_max": round(steps / min(rep_times), 2),
+           "ms_per_step": round(1e3 * t_med / steps, 4), "hbm_GBps": round(total_bytes / t_med / 1e9, 1)}
+    out["hbm_frac_of_peak"] = round(out["hbm_GBps"] / HBM_PEAK_GBPS, 4)
+
+    # per-position windows, decoding through the gaps untimed
+    per_pos, win_kernels = {}, {}
+    tok, pos = first_tok, start
+    for a, b in windows_for(S, start):
+        if pos < a:
+            tok = int(model.generate(tok, pos, a - pos)[-1])
+            pos = a
+        toks, dts = timed_generations(model, tok, a, b - a, reps, torch)
+        dt = median(dts)
+        byt = sum(bytes_per_token(cfg, p) for p in range(a, b))
+        key = f"pos_{a}_{b - 1}"
+        per_pos[key] = {"tok_s": round((b - a) / dt, 2), "GBps": round(byt / dt / 1e9, 1),
+                        "frac_of_peak": round(byt / dt / 1e9 / HBM_PEAK_GBPS, 4),
+                        "tok_s_min": round((b - a) / max(dts), 2), "tok_s_max": round((b - a) / min(dts), 2)}
+        if kernel_timing:  # the same positions once more, every launch timed (deterministic: same rows)
+            ks = kernel_table(cfg, model.profile(tok, a, b - a), list(range(a, b)))
+            win_kernels[key] = {k: v["avg_us"] for k, v in ks.items()}
+        tok, pos = int(toks[-1]), b
+    out["per_position"] = per_pos
+    if win_kernels:
+        out["kernels_by_window_us"] = win_kernels
+
+    # kernel durations over the value's positions, every launch timed with HIP events
+    if kernel_timing:  # rows start.. are rewritten with the values they hold
+        n_prof = min(steps, span)
+        out["kernels"] = kernel_table(cfg, model.profile(first_tok, start, n_prof), list(range(start, start + n_prof)))
+    out["first_token"] = first_tok
+    return out
+
+
+def read_ceiling(pkg, torch):
+    """The practical read ceiling: a plain streaming read of a 4 GiB buffer,
+    the best of 3 rounds of 10 reads, timed with HIP events."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    sums = torch.empty(pkg.ld.LD_STREAM_READ_BLOCKS, dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+    reps, dts = 10, []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        dts.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    dt = min(dts)
+    c_gbps = nbytes / dt / 1e9
+    del buf, sums
+    torch.cuda.empty_cache()
+    out = {"kernel": "stream_read_kernel", "bytes_per_launch": nbytes, "avg_us": round(dt * 1e6, 1),
+           "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4)}
+    print(f"# read ceiling: {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
+
+
+def roofline_of(kernels, cfg):
+    dom = max(kernels, key=lambda k: kernels[k]["share_of_time"])
+    kd = kernels[dom]
+    return {"bound": "hbm", "kernel": dom, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4), "traffic": load_traffic(dom, cfg.name),
+            "bytes_per_launch": kd["bytes_per_launch"], "avg_us": kd["avg_us"]}
 
 
 def main() -> int:
@@ -139,6 +280,12 @@ def main() -> int:
                     help="comma-separated batch sizes of the timed batch-decode leg ('' to skip)")
     ap.add_argument("--sampled-steps", type=int, default=256,
                     help="steps of the temperature / top-p generation loop timed beside greedy decode (0: skip)")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="times the timed decode and each per-position window are run; the median is reported")
+    ap.add_argument("--long-context", default=None,
+                    help="second workload timed after the first (default: the 70B-layer workload after the 7B-shaped "
+                         "one, none otherwise; 'none' to skip): its cache fill, then its timed decode, windows and "
+                         "kernel durations")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes three times (reference for "
                          "scaling the HBM byte counters of a profiler) and exit")
@@ -189,106 +336,24 @@ def main() -> int:
     # warm-up: instantiates the per-token graph and touches every kernel
     if warm:
         model.generate(1, 0, min(warm, S))
-    model.reset()
-    tok = 1
-    if start:
-        prefill = synth.prefill_tokens(cfg, start)
-        t = time.time()
-        for p in range(start):
-            model.forward_async(int(prefill[p]), p)
-        tok = model.argmax_last()
-        print(f"# cache filled by {start} forward calls in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    first_tok = tok
-
-    # ---- the practical read ceiling: a plain streaming read, timed just before the decode ----
-    ceiling = None
-    if not args.no_read_ceiling:
-        nbytes = 4 << 30
-        buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
-        sums = torch.empty(pkg.ld.LD_STREAM_READ_BLOCKS, dtype=torch.float32, device="cuda:0")
-        st = torch.cuda.current_stream()
-        for _ in range(3):
-            pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
-        reps, dts = 10, []
-        for _ in range(3):  # the best of 3 rounds of 10 reads: the ceiling is what the read can reach
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(reps):
-                pkg.ld.ld_op_stream_read(buf.data_ptr(), nbytes, sums.data_ptr(), st.cuda_stream)
-            e1.record(st)
-            torch.cuda.synchronize()
-            dts.append(e0.elapsed_time(e1) * 1e-3 / reps)
-        dt = min(dts)
-        c_gbps = nbytes / dt / 1e9
-        ceiling = {"kernel": "stream_read_kernel", "bytes_per_launch": nbytes, "avg_us": round(dt * 1e6, 1),
-                   "GBps": round(c_gbps, 1), "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4)}
-        del buf, sums
-        torch.cuda.empty_cache()
-        print(f"# read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
-
-    # ---- timed region: greedy decode of `steps` tokens from (tok, start) ----
-    chunks = []
-    done, t_total = 0, 0.0
-    while done < steps:
-        n_pass = min(S - start, steps - done)
-        if done:  # a second pass over the context (only when more steps than positions are asked for)
-            model.reset()
-            tok = 1
-            if start:
-                for p in range(start):
-                    model.forward_async(int(prefill[p]), p)
-                tok = model.argmax_last()
-        for a, b in windows_for(S, n_pass, start=start):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            toks = model.generate(tok, a, b - a)
-            t1 = time.perf_counter()
-            tok = int(toks[-1])
-            chunks.append((a, b, t1 - t0))
-            t_total += t1 - t0
-        done += n_pass
     torch.cuda.synchronize()
 
-    total_bytes = sum(bytes_per_token(cfg, p) for a, b, _ in chunks for p in range(a, b))
-    tok_s = steps / t_total
-    gbps = total_bytes / t_total / 1e9
-    per_pos = {}
-    for a, b, dt in chunks:
-        if b - a <= 16:
-            key = f"pos_{a}_{b - 1}"
-            byt = sum(bytes_per_token(cfg, p) for p in range(a, b))
-            per_pos[key] = {"tok_s": round((b - a) / dt, 2), "GBps": round(byt / dt / 1e9, 1),
-                            "frac_of_peak": round(byt / dt / 1e9 / HBM_PEAK_GBPS, 4)}
-    print(f"# timed {steps} steps in {t_total:.3f} s: {tok_s:.1f} tok/s, {gbps:.0f} GB/s", file=sys.stderr,
-          flush=True)
+    ceiling = read_ceiling(pkg, torch) if not args.no_read_ceiling else None
 
-    # ---- kernel durations: the same workload, every launch timed with HIP events ----
-    roofline = None
-    kernels = None
-    if not args.no_kernel_timing:
-        # same positions as the timed pass; a prefilled prefix stays in the cache
-        n_prof = min(steps, S - start)
-        stats = model.profile(first_tok, start, n_prof)
-        pos_list = list(range(start, start + n_prof))
-        kernels = {}
-        for s in stats:
-            if s["launches"]:
-                avg_ms = s["total_ms"] / s["launches"]
-                byt = kernel_bytes(cfg, s["name"], pos_list)
-                kernels[s["name"]] = {"launches": s["launches"], "avg_us": round(avg_ms * 1e3, 2),
-                                      "bytes_per_launch": int(byt), "GBps": round(byt / (avg_ms * 1e-3) / 1e9, 1),
-                                      "share_of_time": round(s["total_ms"], 3)}
-        tot = sum(k["share_of_time"] for k in kernels.values())
-        for k in kernels.values():
-            k["share_of_time"] = round(k["share_of_time"] / tot, 4)
-        dom = max(kernels, key=lambda k: kernels[k]["share_of_time"])
-        kd = kernels[dom]
-        traffic = load_traffic(dom, cfg.name)
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": kd["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(kd["GBps"] / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "bytes_per_launch": kd["bytes_per_launch"], "avg_us": kd["avg_us"]}
+    # ---- timed region: `steps` greedy decode steps, `repeats` times; windows; kernel durations ----
+    leg = decode_legs(model, cfg, start, steps, args.repeats, torch, kernel_timing=not args.no_kernel_timing)
+    first_tok = leg["first_token"]
+    tok_s, gbps = leg["tok_s"], leg["hbm_GBps"]
+    t_total = steps / tok_s
+    per_pos = leg["per_position"]
+    print(f"# timed {steps} steps x {args.repeats}: median {tok_s:.1f} tok/s "
+          f"({leg['tok_s_min']:.1f}-{leg['tok_s_max']:.1f}), {gbps:.0f} GB/s; windows {json.dumps(per_pos)}",
+          file=sys.stderr, flush=True)
+    kernels = leg.get("kernels")
+    roofline = roofline_of(kernels, cfg) if kernels else None
+    if kernels:
         print(f"# kernels: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+        print(f"# kernels by window (us): {json.dumps(leg.get('kernels_by_window_us'))}", file=sys.stderr, flush=True)
 
     # ---- the sampling generation loop beside greedy decode, same positions ----
     sampled = None
@@ -402,6 +467,37 @@ def main() -> int:
                "GBps": round(sum(bytes_per_token(cfg, p) for p in cpu_pos) / dt / 1e9, 2),
                "host_cores_available": os.cpu_count(), "pinned_core": min(allowed), "cpu_model": cpu_model}
 
+    # ---- the long-context workload: the 70B-layer model, decode from 3584 to 4095 ----
+    long_ctx = None
+    lc_name = args.long_context or ("llama70b_8l" if cfg.name == "llama7b" else "none")
+    if lc_name != "none":
+        del blob
+        lcfg = synth.CONFIGS[lc_name]
+        lstart = START.get(lcfg.name, 0)
+        t = time.time()
+        lblob = synth.make_blob(lcfg)
+        lweights = torch.from_numpy(lblob).to("cuda:0")
+        del lblob
+        torch.cuda.synchronize()
+        print(f"# {lcfg.name}: weights generated and uploaded in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
+        with pkg.Model(lcfg, lweights, graph=not args.no_graph) as lm:
+            if warm:
+                lm.generate(1, 0, min(warm, lcfg.seq_len))
+            t = time.time()
+            lsteps = lcfg.seq_len - lstart
+            lleg = decode_legs(lm, lcfg, lstart, lsteps, args.repeats, torch,
+                               kernel_timing=not args.no_kernel_timing)
+        del lweights
+        torch.cuda.empty_cache()
+        long_ctx = {"workload": f"{lcfg.name}: {lstart} seeded prompt tokens through forward calls (untimed), "
+                                f"then greedy decode of positions {lstart}-{lcfg.seq_len - 1}, batch 1, dim {lcfg.dim}, "
+                                f"hidden {lcfg.hidden_dim}, {lcfg.n_layers} layers, {lcfg.n_heads}/{lcfg.n_kv_heads} "
+                                f"heads, vocab {lcfg.vocab_size}, fp32 N(0,0.02) weights (seed {lcfg.seed})"}
+        long_ctx.update({k: v for k, v in lleg.items() if k != "first_token"})
+        if lleg.get("kernels"):
+            long_ctx["roofline"] = roofline_of(lleg["kernels"], lcfg)
+        print(f"# long context: {json.dumps(long_ctx)}", file=sys.stderr, flush=True)
+
     if ceiling:
         ceiling["decode_frac_of_ceiling"] = round(gbps / ceiling["GBps"], 4)
         if roofline:
@@ -414,7 +510,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": steps,
         "warmup": warm,
-        "ms_per_step": round(1e3 * t_total / steps, 4),
+        "ms_per_step": leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -430,12 +526,16 @@ def main() -> int:
         "hbm_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_token_pos0": bytes_per_token(cfg, 0),
+        "repeats": {"n": args.repeats, "seconds": leg["seconds"], "tok_s_min": leg["tok_s_min"],
+                    "tok_s_max": leg["tok_s_max"]},
         "per_position": per_pos,
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_by_window_us": leg.get("kernels_by_window_us"),
         "generation_loop": sampled,
         "prefill": prefill,
         "batch_decode": batch,
+        "long_context": long_ctx,
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }

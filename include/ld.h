@@ -225,11 +225,11 @@ const char* ld_last_error_detail(void);
 /* ---------------------------------------------------------------------------
  * Kernel timing.  Runs n_steps greedy decode steps from (token, pos) with
  * every kernel launched directly and timed with HIP events on the model's
- * stream: the GEMV kernels with events recorded by their own dispatch (their
- * interval is the kernel's execution), attention (its split kernel, plus the
- * merge kernel where the partials of a kv group are too many for the split
- * kernel's last block to merge) and the classifier (GEMV and next-token
- * kernels) between events recorded on the stream around them.  Reports per kernel kind the launch count
+ * stream: the GEMV kernels and attention (its split kernel, plus the merge
+ * kernel where the partials of a kv group are too many for the split
+ * kernel's last block to merge) with events recorded by their own dispatch
+ * (their interval is the kernels' execution), the classifier (GEMV and
+ * next-token kernels) between events recorded on the stream around them.  Reports per kernel kind the launch count
  * and the summed event time.  Kinds: "qkv_rope_append", "attention", "wo_residual",
  * "w1w3_swiglu", "w2_residual", "classifier_argmax".  stats must hold
  * max_stats entries; *n_stats_out receives the number filled.  Synchronous.

@@ -111,8 +111,9 @@ struct AttnParams {
     int n_heads;
     int n_kv_heads;
     int kv_dim;
-    int nsplit;            // grid.y
-    int chunk;             // keys per split (set by the launcher)
+    int nsplit;            // grid.y: the most splits a kv head's keys are cut into at this launch
+    int chunk;             // keys per tile, the unit splits are made of (set by the launcher)
+    int min_tiles;         // fewest tiles a split takes (set by the launcher)
     int fuse;              // 1: the last split block of a kv group merges it (set by the launcher)
     // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
     // out and state are b * q_stride floats / b states further, its caches
@@ -198,9 +199,14 @@ hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan);
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr);
 
-int attn_chunk(int head_size);  // keys per tile (0 = unsupported head size)
-int attn_splits(int head_size, int seq_len, int n_heads, int n_kv_heads);  // grid.y of the attention kernel
-hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s);  // attention (+ merge)
+int attn_chunk(int head_size);  // > 0 for a head size the attention kernels cover
+// grid.y of the attention kernel for a context of seq_len positions (the
+// splits of the longest context; shorter ones use fewer, the rest exit)
+int attn_splits(int head_size, int seq_len, int n_heads, int n_kv_heads);
+// attention (+ merge); start / stop (optional) as for gemv_launch: taken by the
+// attention kernel's dispatch and by the last kernel's (the merge, when it runs)
+hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s, hipEvent_t start = nullptr,
+                       hipEvent_t stop = nullptr);
 
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
 hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s);

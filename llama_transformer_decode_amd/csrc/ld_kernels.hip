@@ -1013,49 +1013,37 @@ __global__ void set_state_kernel(StepState* st, int token, int pos) {
 // Causal grouped-query attention at one position ("run.c 逐行解讀" §4 step
 // 2e), split along the key axis (flash-decoding).
 //
-// The n = pos+1 keys form tiles of CH rows.  Block (g, s) serves kv head g and
-// a contiguous run of tiles; at small n each block gets one tile and blocks
-// past the last tile exit at once, so one launch shape serves every position.
-// For each tile the block stages the key and value rows in LDS (coalesced
-// 16-byte loads), scores them against every query head h with
-// floor(h*KV/H) = g (the group shares the staged rows), and folds them into a
-// running max m, exp-sum l and unnormalised value sum (online softmax: when m
-// grows, l and the sum are rescaled by e^{m_old - m_new}).  The next tile's
-// loads are issued before the current tile is computed, so the block keeps
-// HBM requests in flight throughout.  Each block leaves (m, l, sum) as a
-// partial, and they are combined exactly,
-// out = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, M = max_s m_s:
+// The n = pos+1 keys form tiles of CH keys.  Block (g, s) serves kv head g and
+// a contiguous run of tiles: the launch has grid.y = nsplit blocks per kv
+// head, each split takes at least min_tiles tiles, and blocks past the last
+// split exit at once, so one launch shape serves every position up to its
+// context.  Every query head h with floor(h*KV/H) = g shares the block's key
+// and value reads.  A block folds its keys into a running max m, exp-sum l
+// and unnormalised value sum per head (online softmax: when m grows, l and the
+// sum are rescaled by 2^{m_old - m_new}; scores are kept in base-2 units,
+// s * log2(e) / sqrt(head_size), so every exponential is one exp2).  Each
+// block leaves (m, l, sum) as a partial, and they are combined exactly,
+// out = sum_s 2^{m_s - M} acc_s / sum_s 2^{m_s - M} l_s, M = max_s m_s:
 // by the last block of the kv group to finish (merge_group) when each thread
 // of that block folds a few splits, else by attn_merge_kernel, one block per
-// query head.
-//
-// All 256 threads work in every phase: a (head, key) score is split over up to
-// 16 threads when the group is small, and the value sum over key groups whose
-// float4 partials are added through LDS at the end.
+// query head.  With one split the block writes the output itself.
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32; 0 at -inf
 
 __device__ __forceinline__ void group_of(int g, int H, int KV, int& h_lo, int& G) {
     h_lo = (g * H + KV - 1) / KV;              // ceil(g H / KV)
     G = ((g + 1) * H + KV - 1) / KV - h_lo;    // query heads with floor(h KV / H) = g
 }
 
-// Fewest keys a split takes (below that one split serves all keys).  64 keys
-// measured best for both kernels: one-tile (32-key) splits of the head-size
-// 128 kernel cost 0.4% at positions below 512 (7B shape), and one-tile
-// (64-key) splits of the generic kernel gained 7% over two-tile ones on the
-// GQA-small workload.
-#ifndef LD_ATTN_MIN_KEYS
-#define LD_ATTN_MIN_KEYS 64
-#endif
-
-__host__ __device__ constexpr int attn_min_tiles(int ch) {
-    return (LD_ATTN_MIN_KEYS + ch - 1) / ch;
-}
-
 // Tiles of a position: `per` consecutive tiles per split (at least
-// attn_min_tiles), `nact` splits in use.
-__device__ __forceinline__ void split_of(int n, int ch, int nsplit, int& tiles, int& per, int& nact) {
+// min_tiles), `nact` splits in use.
+__host__ __device__ __forceinline__ void split_of(int n, int ch, int nsplit, int min_tiles, int& tiles, int& per,
+                                                  int& nact) {
     tiles = (n + ch - 1) / ch;
-    per = max((tiles + nsplit - 1) / nsplit, attn_min_tiles(ch));
+    per = (tiles + nsplit - 1) / nsplit;
+    if (per < min_tiles) per = min_tiles;
     nact = (tiles + per - 1) / per;
 }
 
@@ -1111,73 +1099,91 @@ __device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
     return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
 }
 
+// Most splits one thread of a merging block folds (the last split block
+// merges its kv group only when this covers every split).
+constexpr int kMaxFold = 4;
+
 // Exact merge of the split partials of query heads h_lo .. h_lo + G - 1 into
-// the output: with M = max_s m_s, out = sum_s e^{m_s - M} acc_s /
-// sum_s e^{m_s - M} l_s.  Thread (kg, o) folds splits kg, kg + KG, ... of
-// float4 output slot o into its own running (m, l, acc) (the online-softmax
-// rescaling, so every split's loads are independent of the others and all go
-// out at once); the KG key groups are then combined through LDS the same way.
-template <int HS>
+// the output: with M = max_s m_s, out = sum_s 2^{m_s - M} acc_s /
+// sum_s 2^{m_s - M} l_s.  Thread (kg, o) of the NT threads takes splits kg,
+// kg + KG, ... (at most kMaxFold) of float4 output slot o: it issues all their
+// loads at once, then folds them into its own running (m, l, acc); the key
+// groups that hold splits are then combined through LDS the same way.
+template <int HS, int NT>
 __device__ void merge_group(const AttnParams& p, int h_lo, int G, int nact) {
     constexpr int H4 = HS / 4;
-    __shared__ float4 acc_s[kAttnThreads];
-    __shared__ float m_s[kAttnThreads], l_s[kAttnThreads];
+    __shared__ float4 acc_s[NT];
+    __shared__ float m_s[NT], l_s[NT];
     const int tid = threadIdx.x;
     const int slots = G * H4;  // float4 outputs of the group
-    const int KG = slots < kAttnThreads ? kAttnThreads / slots : 1;
-    for (int o0 = 0; o0 < slots; o0 += kAttnThreads) {
-        const int o = o0 + (slots < kAttnThreads ? tid % slots : tid), kg = slots < kAttnThreads ? tid / slots : 0;
+    const int KG = slots < NT ? NT / slots : 1;
+    const int kgn = KG < nact ? KG : nact;  // key groups that hold a split
+    for (int o0 = 0; o0 < slots; o0 += NT) {
+        const int o = o0 + (slots < NT ? tid % slots : tid), kg = slots < NT ? tid / slots : 0;
         const int h = h_lo + o / H4, c = o % H4;
         float m = -INFINITY, l = 0.f;
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (o < slots && kg < KG) {
+        if (o < slots && kg < kgn) {
             const float2* ml = p.part_ml + (size_t)h * p.nsplit;
             const float4* ah = reinterpret_cast<const float4*>(p.part_acc) + (size_t)h * p.nsplit * H4 + c;
-#pragma unroll 8
-            for (int sp = kg; sp < nact; sp += KG) {
-                const float2 e = load_coherent(ml + sp);
-                const float4 v = load_coherent(ah + (size_t)sp * H4);
-                const float mn = fmaxf(m, e.x);
-                const float r = __expf(m - mn), w = __expf(e.x - mn);  // r = 0 for the first split
-                l = fmaf(l, r, e.y * w);
-                a = fma4(w, v, make_float4(a.x * r, a.y * r, a.z * r, a.w * r));
+            float2 e[kMaxFold];
+            float4 v[kMaxFold];
+#pragma unroll
+            for (int i = 0; i < kMaxFold; ++i) {  // every load in flight together (a split past nact re-reads the last)
+                const int sp = min(kg + i * KG, nact - 1);
+                e[i] = load_coherent(ml + sp);
+                v[i] = load_coherent(ah + (size_t)sp * H4);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxFold; ++i) {
+                if (kg + i * KG >= nact) break;
+                const float mn = fmaxf(m, e[i].x);
+                const float r = exp2_fast(m - mn), w = exp2_fast(e[i].x - mn);  // r = 0 for the first split
+                l = fmaf(l, r, e[i].y * w);
+                a = fma4(w, v[i], make_float4(a.x * r, a.y * r, a.z * r, a.w * r));
                 m = mn;
             }
         }
-        if (KG > 1) {
+        if (kgn > 1) {
             acc_s[tid] = a;
             m_s[tid] = m;
             l_s[tid] = l;
             __syncthreads();
             if (tid < slots) {
                 float M = m;
-                for (int k = 1; k < KG; ++k) M = fmaxf(M, m_s[k * slots + tid]);
+                for (int k = 1; k < kgn; ++k) M = fmaxf(M, m_s[k * slots + tid]);
                 l = 0.f;
                 a = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int k = 0; k < KG; ++k) {
-                    const float e = __expf(m_s[k * slots + tid] - M);  // 0 for a group without splits
+                for (int k = 0; k < kgn; ++k) {
+                    const float e = exp2_fast(m_s[k * slots + tid] - M);
                     l = fmaf(l_s[k * slots + tid], e, l);
                     a = fma4(e, acc_s[k * slots + tid], a);
                 }
             }
+            __syncthreads();  // the next pass reuses the LDS slots
         }
-        if (o < slots && (KG == 1 || tid < slots)) {
+        if (o < slots && (kgn == 1 || tid < slots)) {
             const float il = 1.0f / l;
             reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + c] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
         }
     }
 }
 
+// Wait until this thread's vector memory operations have completed
+// (s_waitcnt vmcnt(0)).  The memory clobber also keeps the compiler from
+// moving any load or store across it.
+__device__ __forceinline__ void wait_vector_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Called by every thread of a split block after it has stored its partial
 // (coherent stores).  Each thread waits for its stores to complete before
-// thread 0 counts the block's arrival; the block that brings the count to nact
-// resets the counter for the next launch and merges the group, whose partials
-// it then reads with coherent loads.  No block waits for another, so the grid
-// always drains.
-template <int HS>
+// thread 0 counts the block's arrival with an atomic add; the block that
+// brings the count to nact resets the counter for the next launch and merges
+// the group, whose partials it then reads with coherent loads.  No block waits
+// for another, so the grid always drains.
+template <int HS, int NT>
 __device__ void arrive_and_merge(const AttnParams& p, int g, int h_lo, int G, int nact) {
     __shared__ int last_s;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+    wait_vector_memory();
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned before = atomicAdd(p.arrive + g, 1u);
@@ -1187,7 +1193,7 @@ __device__ void arrive_and_merge(const AttnParams& p, int g, int h_lo, int G, in
     }
     __syncthreads();
     if (!last_s) return;
-    merge_group<HS>(p, h_lo, G, nact);
+    merge_group<HS, NT>(p, h_lo, G, nact);
 }
 
 template <int HS, int CH>
@@ -1208,7 +1214,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
     const int lane = tid & 63, wave = tid >> 6;
     const int n = p.state->pos + 1;
     int tiles, per, nact;
-    split_of(n, CH, p.nsplit, tiles, per, nact);
+    split_of(n, CH, p.nsplit, p.min_tiles, tiles, per, nact);
     if (s >= nact) return;
     const int tile0 = s * per, tile1 = min(tiles, tile0 + per);
     int h_lo, G;
@@ -1250,7 +1256,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
     int tpp = 1;
     while (tpp < 16 && P * tpp * 2 <= kAttnThreads) tpp *= 2;
     const int per_pass = kAttnThreads / tpp, passes = (P + per_pass - 1) / per_pass, sub = tid % tpp;
-    const float scale = 1.0f / sqrtf((float)HS);
+    const float scale = kLog2e / sqrtf((float)HS);  // base-2 units
 
     for (int tile = tile0; tile < tile1; ++tile) {
         const int t0 = tile * CH, nt = min(CH, n - t0);
@@ -1267,7 +1273,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
         __syncthreads();
         if (tile + 1 < tile1) load_tile(tile + 1);  // in flight while this tile is computed
 
-        // scores s_t = q_h . k_t / sqrt(head_size)
+        // scores s_t = q_h . k_t / sqrt(head_size), times log2(e)
         for (int it = 0; it < passes; ++it) {
             const int pair = it * per_pass + tid / tpp;
             const int hh = pair / CH, t = pair % CH;
@@ -1281,16 +1287,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
         }
         __syncthreads();
 
-        // online softmax: new running max, weights e^{s - m}, rescale factor
+        // online softmax: new running max, weights 2^{s - m}, rescale factor
         for (int hh = wave; hh < G; hh += kAttnThreads / 64) {
             const float sc = lane < CH ? p_s[hh][lane] : -INFINITY;
             const float m_old = m_s[hh];
             const float m_new = fmaxf(m_old, wave_max(sc));
-            const float e = lane < nt ? __expf(sc - m_new) : 0.f;
+            const float e = lane < nt ? exp2_fast(sc - m_new) : 0.f;
             const float sum = wave_sum(e);
             if (lane < CH) p_s[hh][lane] = e;
             if (lane == 0) {
-                const float r = __expf(m_old - m_new);  // 0 on the first tile
+                const float r = exp2_fast(m_old - m_new);  // 0 on the first tile
                 r_s[hh] = r;
                 l_s[hh] = l_s[hh] * r + sum;
                 m_s[hh] = m_new;
@@ -1359,16 +1365,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
         return;
     }
     if (tid < G) store_coherent(p.part_ml + (size_t)(h_lo + tid) * p.nsplit + s, make_float2(m_s[tid], l_s[tid]));
-    if (p.fuse) arrive_and_merge<HS>(p, g, h_lo, G, nact);
+    if (p.fuse) arrive_and_merge<HS, kAttnThreads>(p, g, h_lo, G, nact);
 }
 
-// Head size 128: a register-only variant.  Each wave is an independent
-// flash-decoding worker over its own batches of 2U keys: one key row (512 B)
-// per half-wave and U rows per half in flight, the next batch loaded while
-// the current one is scored, q of every head of the group held in registers,
-// scores reduced across the 32 lanes of a half with DPP, and the online
-// softmax state (m, l per head) wave-uniform.  No LDS and no barrier inside the
-// key loop; the four waves merge once at the end of the block.
+// Register-only attention for head sizes up to 128.  A key row of HS floats
+// is held by LPK lanes (HS/4 float4 columns, rounded up to a power of two;
+// lanes past the row re-read its last column and have q = 0 there), so a wave
+// holds KPW = 64/LPK keys per load, and U such loads form a wave batch of
+// KPW*U keys.  Each of the NW waves is an independent flash-decoding worker
+// over its batches: the next batch is loaded while the current one is scored,
+// q of every head of the group stays in registers, a score is reduced over
+// its LPK lanes with DPP, every lane turns its own key's score into a weight,
+// and the running max m is wave-uniform.  No LDS and no barrier in the key
+// loop; the waves merge once at the end of the block.  A round of the block
+// (every wave one batch) is the tile of CH = NW*KPW*U keys.
+__host__ __device__ constexpr int attn_lanes_per_key(int hs) { return hs <= 16 ? 4 : hs <= 32 ? 8 : hs <= 64 ? 16 : 32; }
+
 __device__ __forceinline__ float half_sum(float v) {  // lanes 16-31: sum of 0-31; lanes 48-63: of 32-63
     v += dpp<kQuadSwap1>(0.f, v);
     v += dpp<kQuadSwap2>(0.f, v);
@@ -1378,133 +1390,173 @@ __device__ __forceinline__ float half_sum(float v) {  // lanes 16-31: sum of 0-3
     return v;
 }
 
-template <int GMAX, int U>
-__global__ __launch_bounds__(kAttnThreads) void attn128_kernel(AttnParams pb) {
-    constexpr int HS = 128, CH = 32, NW = kAttnThreads / 64;
+// Sum over aligned groups of LPK <= 16 lanes, left in every lane of the group.
+template <int LPK>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    v += dpp<kQuadSwap1>(0.f, v);
+    v += dpp<kQuadSwap2>(0.f, v);
+    if (LPK >= 8) v += dpp<kRowHalfMirror>(0.f, v);
+    if (LPK >= 16) v += dpp<kRowMirror>(0.f, v);
+    return v;
+}
+
+template <int HS, int GMAX, int U, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
+    constexpr int H4 = HS / 4, LPK = attn_lanes_per_key(HS), KPW = 64 / LPK;
+    constexpr int BK = KPW * U;  // keys of one wave batch
+    constexpr int CH = NW * BK;  // keys of one round of the block
+    static_assert(H4 <= LPK && LPK <= 32, "a key row within one lane group of at most half a wave");
     const AttnParams p = seq_view<HS>(pb);
-    __shared__ float ms_s[NW][GMAX], ls_s[NW][GMAX];
-    __shared__ float4 acc_s[NW][GMAX][32];
+    __shared__ float4 acc_s[NW][GMAX][H4];
+    __shared__ float ms_s[NW][GMAX], ls_s[NW][GMAX], w_s[NW][GMAX], M_s[GMAX];
     const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, c = lane & 31;
-    const int n = p.state->pos + 1;
-    int tiles, per, nact;
-    split_of(n, CH, p.nsplit, tiles, per, nact);
-    if (s >= nact) return;
-    const int kb = s * per * CH, ke = min(n, (s + 1) * per * CH);  // this block's keys
+    const int lane = tid & 63, wave = tid >> 6, sub = lane / LPK, c = lane % LPK;
+    const int cc = c < H4 ? c : H4 - 1;
     int h_lo, G;
     group_of(g, p.n_heads, p.n_kv_heads, h_lo, G);
 
-    const float* kbase = p.kc + (size_t)g * HS + 4 * c;
-    const float* vbase = p.vc + (size_t)g * HS + 4 * c;
+    // q does not depend on the position: its loads go out beside the state's
+    float4 q[GMAX];
+    const float4* q4 = reinterpret_cast<const float4*>(p.q);
+#pragma unroll
+    for (int hh = 0; hh < GMAX; ++hh)
+        q[hh] = hh < G && c < H4 ? q4[(size_t)(h_lo + hh) * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const int n = p.state->pos + 1;
+    int tiles, per, nact;
+    split_of(n, CH, p.nsplit, p.min_tiles, tiles, per, nact);
+    if (s >= nact) return;
+    const int kb = s * per * CH, ke = min(n, (s + 1) * per * CH);  // this block's keys
+
+    const float* kbase = p.kc + (size_t)g * HS + 4 * cc;
+    const float* vbase = p.vc + (size_t)g * HS + 4 * cc;
     float4 K[U], V[U];
     auto load = [&](int b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = min(kb + b * 2 * U + 2 * u + half, n - 1);  // past the end: re-read the last key
+            const int t = min(kb + b * BK + u * KPW + sub, n - 1);  // past the end: re-read the last key
             K[u] = *reinterpret_cast<const float4*>(kbase + (size_t)t * p.kv_dim);
             V[u] = *reinterpret_cast<const float4*>(vbase + (size_t)t * p.kv_dim);
         }
     };
     int b = wave;
-    if (kb + b * 2 * U < ke) load(b);
+    if (kb + b * BK < ke) load(b);
 
-    float4 q[GMAX], acc[GMAX];
-    float m[GMAX], l[GMAX];
-    const float4* q4 = reinterpret_cast<const float4*>(p.q);
+    float4 acc[GMAX];
+    float m[GMAX], l[GMAX];  // m wave-uniform; l sums this lane's own keys' weights
 #pragma unroll
     for (int hh = 0; hh < GMAX; ++hh) {
-        q[hh] = hh < G ? q4[(size_t)(h_lo + hh) * 32 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
         acc[hh] = make_float4(0.f, 0.f, 0.f, 0.f);
         m[hh] = -INFINITY;
         l[hh] = 0.f;
     }
-    const float scale = 1.0f / sqrtf((float)HS);
+    const float scale = kLog2e / sqrtf((float)HS);  // scores in base-2 units
 
-    for (; kb + b * 2 * U < ke; b += NW) {
+    for (; kb + b * BK < ke; b += NW) {
         float4 Kc[U], Vc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             Kc[u] = K[u];
             Vc[u] = V[u];
         }
-        if (kb + (b + NW) * 2 * U < ke) load(b + NW);  // in flight while this batch is scored
-        const int key0 = kb + b * 2 * U;
+        if (kb + (b + NW) * BK < ke) load(b + NW);  // in flight while this batch is scored
+        const int key0 = kb + b * BK;
         // every head slot of the template is computed (a slot past the group has
         // q = 0 and is never written), so the loop has no per-head branch
 #pragma unroll
         for (int hh = 0; hh < GMAX; ++hh) {
-            {
-                float se[U], so[U];
-                float mb = -INFINITY;
+            float sc[U];
+            float mb = -INFINITY;
+            if constexpr (LPK == 32) {
+                // the two halves hold two keys; their scores become wave-uniform by readlane
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const float d = half_sum(dot4(Kc[u], q[hh], 0.f));
-                    se[u] = key0 + 2 * u < ke ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 31)) * scale
-                                             : -INFINITY;
-                    so[u] = key0 + 2 * u + 1 < ke
-                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 63)) * scale
-                                : -INFINITY;
-                    mb = fmaxf(mb, fmaxf(se[u], so[u]));
+                    const float se = key0 + 2 * u < ke
+                                         ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 31)) * scale
+                                         : -INFINITY;
+                    const float so = key0 + 2 * u + 1 < ke
+                                         ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d), 63)) * scale
+                                         : -INFINITY;
+                    sc[u] = sub ? so : se;
+                    mb = fmaxf(mb, fmaxf(se, so));
                 }
-                const float mn = fmaxf(m[hh], mb);
-                const float r = __expf(m[hh] - mn);
-                float4 a = make_float4(acc[hh].x * r, acc[hh].y * r, acc[hh].z * r, acc[hh].w * r);
-                float ls = 0.f;
+            } else {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const float ee = __expf(se[u] - mn), eo = __expf(so[u] - mn);
-                    ls += ee + eo;
-                    a = fma4(half ? eo : ee, Vc[u], a);
+                    const float d = lane_group_sum<LPK>(dot4(Kc[u], q[hh], 0.f));
+                    sc[u] = key0 + u * KPW + sub < ke ? d * scale : -INFINITY;
+                    mb = fmaxf(mb, sc[u]);
                 }
-                acc[hh] = a;
-                l[hh] = l[hh] * r + ls;
-                m[hh] = mn;
+                mb = wave_max(mb);
             }
+            const float mn = fmaxf(m[hh], mb);
+            const float r = exp2_fast(m[hh] - mn);  // 0 on the first batch
+            float4 a = make_float4(acc[hh].x * r, acc[hh].y * r, acc[hh].z * r, acc[hh].w * r);
+            float ls = l[hh] * r;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float e = exp2_fast(sc[u] - mn);
+                ls += e;
+                a = fma4(e, Vc[u], a);
+            }
+            acc[hh] = a;
+            l[hh] = ls;
+            m[hh] = mn;
         }
     }
 
-    // the halves hold different keys of the same columns: add them, then merge the waves
+    // lanes c, c + LPK, ... hold the same column over different keys: add them,
+    // then merge the waves through LDS
 #pragma unroll
     for (int hh = 0; hh < GMAX; ++hh) {
-        {
-            const float4 o = make_float4(__shfl_xor(acc[hh].x, 32), __shfl_xor(acc[hh].y, 32), __shfl_xor(acc[hh].z, 32),
-                                         __shfl_xor(acc[hh].w, 32));
-            if (half == 0) acc_s[wave][hh][c] = make_float4(acc[hh].x + o.x, acc[hh].y + o.y, acc[hh].z + o.z, acc[hh].w + o.w);
-            if (lane == 0) {
-                ms_s[wave][hh] = m[hh];
-                ls_s[wave][hh] = l[hh];
-            }
+#pragma unroll
+        for (int off = LPK; off < 64; off *= 2) {
+            acc[hh] = make_float4(acc[hh].x + __shfl_xor(acc[hh].x, off), acc[hh].y + __shfl_xor(acc[hh].y, off),
+                                  acc[hh].z + __shfl_xor(acc[hh].z, off), acc[hh].w + __shfl_xor(acc[hh].w, off));
+            l[hh] += __shfl_xor(l[hh], off);
+        }
+        if (lane < H4) acc_s[wave][hh][lane] = acc[hh];
+        if (lane == 0) {
+            ms_s[wave][hh] = m[hh];
+            ls_s[wave][hh] = l[hh];
         }
     }
     __syncthreads();
-    if (tid < G * 32) {
-        const int hh = tid / 32, cc = tid % 32;
+    if (tid < NW * GMAX) {  // each wave's weight 2^{m_w - M} (0 for a wave without keys)
+        const int w = tid / GMAX, hh = tid % GMAX;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ms_s[w][hh]);
+        for (int k = 0; k < NW; ++k) M = fmaxf(M, ms_s[k][hh]);
+        w_s[w][hh] = exp2_fast(ms_s[w][hh] - M);
+        if (w == 0) M_s[hh] = M;
+    }
+    __syncthreads();
+    if (tid < G * H4) {
+        const int hh = tid / H4, col = tid % H4;
         float L = 0.f;
         float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float e = __expf(ms_s[w][hh] - M);  // 0 for a wave without keys
+            const float e = w_s[w][hh];
             L = fmaf(ls_s[w][hh], e, L);
-            A = fma4(e, acc_s[w][hh][cc], A);
+            A = fma4(e, acc_s[w][hh][col], A);
         }
         const int h = h_lo + hh;
-        if (nact == 1) {
+        if (nact == 1) {  // one split holds every key: this is the output
             const float il = 1.0f / L;
-            reinterpret_cast<float4*>(p.out)[(size_t)h * 32 + cc] = make_float4(A.x * il, A.y * il, A.z * il, A.w * il);
+            reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + col] = make_float4(A.x * il, A.y * il, A.z * il, A.w * il);
         } else {
-            store_coherent(reinterpret_cast<float4*>(p.part_acc) + ((size_t)h * p.nsplit + s) * 32 + cc, A);
-            if (cc == 0) store_coherent(p.part_ml + (size_t)h * p.nsplit + s, make_float2(M, L));
+            store_coherent(reinterpret_cast<float4*>(p.part_acc) + ((size_t)h * p.nsplit + s) * H4 + col, A);
+            if (col == 0) store_coherent(p.part_ml + (size_t)h * p.nsplit + s, make_float2(M_s[hh], L));
         }
     }
-    if (nact > 1 && p.fuse) arrive_and_merge<HS>(p, g, h_lo, G, nact);
+    if (nact > 1 && p.fuse) arrive_and_merge<HS, NW * 64>(p, g, h_lo, G, nact);
 }
 
 // Exact merge of the split partials of query head blockIdx.x, one block per
 // query head, for groups whose partials are too many for one block to fold.
-// Wave 0 finds M = max_s m_s and L = sum_s e^{m_s - M} l_s over the splits
+// Wave 0 finds M = max_s m_s and L = sum_s 2^{m_s - M} l_s over the splits
 // (lane-strided loads); then every column's float4 is summed over split
 // groups, 8 loads in flight per thread, and the groups are added through LDS.
 template <int HS>
@@ -1516,7 +1568,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb)
     __shared__ float4 red_s[kAttnThreads];
     const int tid = threadIdx.x, lane = tid & 63, h = blockIdx.x;
     int tiles, per, nact;
-    split_of(p.state->pos + 1, p.chunk, p.nsplit, tiles, per, nact);
+    split_of(p.state->pos + 1, p.chunk, p.nsplit, p.min_tiles, tiles, per, nact);
     if (nact == 1) return;  // the attention kernel wrote the output itself
     const float2* ml = p.part_ml + (size_t)h * p.nsplit;
     if (tid < 64) {
@@ -1526,7 +1578,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb)
         float l = 0.f;
         for (int sp = lane; sp < nact; sp += 64) {
             const float2 e = ml[sp];
-            l = fmaf(e.y, __expf(e.x - m), l);
+            l = fmaf(e.y, exp2_fast(e.x - m), l);
         }
         l = wave_sum(l);
         if (lane == 0) {
@@ -1542,7 +1594,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb)
     if (kg < KG) {
 #pragma unroll 8
         for (int sp = kg; sp < nact; sp += KG) {
-            const float wgt = __expf(ml[sp].x - M);
+            const float wgt = exp2_fast(ml[sp].x - M);
             a = fma4(wgt, acc4[(size_t)sp * H4], a);
         }
     }
@@ -1806,104 +1858,135 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s
     return hipGetLastError();
 }
 
+// ---- attention launch shapes ----
+// Head sizes up to 128 take the register kernel with 4 waves per block; its
+// instance follows the query heads per kv head: one or two heads with 4 key
+// loads per wave batch, four or eight heads with 2 (registers grow with the
+// heads).  Head size 256 takes the LDS-staged kernel (16-key tiles).
+//
+// A split takes at least kSplitBytes of keys and values: the keys of one
+// block stream at a few tens of GB/s (one compute unit's share), so a split
+// of that size costs about what merging one more split costs.  The grid aims
+// at about kAttnBlocks blocks at the longest context (two per compute unit).
+constexpr int kSplitBytes = 64 << 10;
+constexpr int kAttnBlocks = 512;
+
+struct AttnShape {
+    int reg;        // 1: register kernel
+    int gmax, u;
+    int chunk;      // keys per tile (one round of the block)
+    int min_tiles;  // fewest tiles of a split
+};
+
+AttnShape attn_shape(int hs, int group) {
+    AttnShape a{};
+    if (hs <= 128) {
+        a.reg = 1;
+        a.gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
+        a.u = a.gmax <= 2 ? 4 : 2;
+        a.chunk = (kAttnThreads / 64) * (64 / attn_lanes_per_key(hs)) * a.u;
+    } else {
+        a.chunk = 16;
+    }
+    const int keys = (kSplitBytes + 8 * hs - 1) / (8 * hs);  // keys whose K and V rows of one head fill a split
+    a.min_tiles = (keys + a.chunk - 1) / a.chunk;
+    if (a.min_tiles < 1) a.min_tiles = 1;
+    return a;
+}
+
 int attn_chunk(int hs) {
     switch (hs) {
-        case 16:
-        case 32:
-        case 48:
-        case 64:
-        case 80:
-        case 96: return 64;
-        case 128: return 32;
-        case 256: return 16;
+        case 16: case 32: case 48: case 64: case 80: case 96: case 128: case 256: return attn_shape(hs, 1).chunk;
     }
     return 0;
 }
 
-#ifndef LD_ATTN_BLOCKS
-#define LD_ATTN_BLOCKS 512
-#endif
+// Whether the last split block of a kv group merges the group's partials:
+// when each thread of that block folds at most kMaxFold splits (the merge
+// launch costs more than such a tail).  Larger groups of partials go to the
+// merge kernel.
+bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit) {
+    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
+    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    return nsplit > 1 && (nsplit + kg - 1) / kg <= kMaxFold;
+}
 
 #ifndef LD_ATTN_ONE_BLOCK_BYTES
 #define LD_ATTN_ONE_BLOCK_BYTES (128 << 10)
 #endif
 
-#ifndef LD_ATTN_FUSE_FOLDS
-#define LD_ATTN_FUSE_FOLDS 4  // most splits a thread of the merging block folds
-#endif
-
-// Whether the last split block of a kv group merges the group's partials:
-// when each thread of that block folds at most LD_ATTN_FUSE_FOLDS splits (the
-// merge launch costs more than such a tail).  Larger groups of partials go to
-// the merge kernel.
-bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit) {
-    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
-    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
-    return nsplit > 1 && (nsplit + kg - 1) / kg <= LD_ATTN_FUSE_FOLDS;
-}
-
 int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
-    const int ch = attn_chunk(hs);
-    if (!ch) return 0;
-    const int tiles = (seq_len + ch - 1) / ch;
-    // about LD_ATTN_BLOCKS blocks at the longest context (two per compute
-    // unit), and no split shorter than attn_min_tiles(ch) tiles
-    int want = (LD_ATTN_BLOCKS + n_kv_heads - 1) / n_kv_heads;
-    const int most = (tiles + attn_min_tiles(ch) - 1) / attn_min_tiles(ch);
+    if (!attn_chunk(hs)) return 0;
+    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
+    const AttnShape a = attn_shape(hs, group);
+    const int tiles = (seq_len + a.chunk - 1) / a.chunk;
+    const int most = (tiles + a.min_tiles - 1) / a.min_tiles;
+    int want = (kAttnBlocks + n_kv_heads - 1) / n_kv_heads;
     if (want > most) want = most;
     if (want < 1) want = 1;
-    // where the partials would need the merge launch (~4 us even with nothing
-    // to do) and a kv head's whole cache fits one block, one block per kv head
-    // serves it.  A split merged by its last block beats one block per kv head
-    // (stories15M-shaped workload: 6% more tokens/s).
+    // where the partials would need the merge launch (a few us even with
+    // nothing to do) and a kv head's whole cache fits one block, one block per
+    // kv head serves it
     if (want > 1 && !attn_fused(hs, n_heads, n_kv_heads, want) &&
         (long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES)
         return 1;
     return want;
 }
 
-#ifndef LD_ATTN_REG128
-#define LD_ATTN_REG128 1  // head size 128 takes the register-only kernel
-#endif
+// Launch one attention kernel (and the merge after it): with events, through
+// hipExtLaunchKernelGGL so that `start` is taken by the attention kernel's own
+// dispatch and `stop` by the last kernel's, bracketing their execution alone.
+template <class K>
+void attn_dispatch(K kernel, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop, const AttnParams& p) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, dim3(kAttnThreads), 0, s, start, stop, 0, p);
+    else
+        hipLaunchKernelGGL(kernel, grid, dim3(kAttnThreads), 0, s, p);
+}
 
-hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s) {
+template <int HS>
+void attn_reg_dispatch(const AttnShape& a, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                       const AttnParams& p) {
+    constexpr int NW = kAttnThreads / 64;
+    switch (a.gmax) {
+        case 1: attn_dispatch(attn_reg_kernel<HS, 1, 4, NW>, grid, s, start, stop, p); break;
+        case 2: attn_dispatch(attn_reg_kernel<HS, 2, 4, NW>, grid, s, start, stop, p); break;
+        case 4: attn_dispatch(attn_reg_kernel<HS, 4, 2, NW>, grid, s, start, stop, p); break;
+        default: attn_dispatch(attn_reg_kernel<HS, 8, 2, NW>, grid, s, start, stop, p); break;
+    }
+}
+
+hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     AttnParams p = p0;
-    p.chunk = attn_chunk(hs);
-    const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
-    const dim3 grid(p.n_kv_heads, p.nsplit, nb), block(kAttnThreads), mgrid(p.n_heads, 1, nb);
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
+    if (group > kMaxGroup || p.nsplit < 1) return hipErrorInvalidValue;
+    const AttnShape a = attn_shape(hs, group);
+    p.chunk = a.chunk;
+    p.min_tiles = a.min_tiles;
+    const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
+    const dim3 grid(p.n_kv_heads, p.nsplit, nb), mgrid(p.n_heads, 1, nb);
     p.fuse = attn_fused(hs, p.n_heads, p.n_kv_heads, p.nsplit);
     if (p.fuse && !p.arrive) return hipErrorInvalidValue;  // split blocks count their arrivals there
     const bool merge = p.nsplit > 1 && !p.fuse;
-    if (hs == 128 && LD_ATTN_REG128) {
-        // 4 key pairs per wave batch for one or two heads per kv head, 2 for
-        // larger groups (whose per-batch register and ALU load is larger)
-        if (group <= 1)
-            hipLaunchKernelGGL((attn128_kernel<1, 4>), grid, block, 0, s, p);
-        else if (group <= 2)
-            hipLaunchKernelGGL((attn128_kernel<2, 4>), grid, block, 0, s, p);
-        else if (group <= 4)
-            hipLaunchKernelGGL((attn128_kernel<4, 2>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((attn128_kernel<8, 2>), grid, block, 0, s, p);
-        if (merge) hipLaunchKernelGGL((attn_merge_kernel<128>), mgrid, block, 0, s, p);
-        return hipGetLastError();
-    }
+    hipEvent_t stop1 = merge ? nullptr : stop;  // the attention kernel's own stop event when nothing follows it
     switch (hs) {
-#define LD_ATTN_CASE(HS, CH)                                                       \
-    case HS:                                                                       \
-        hipLaunchKernelGGL((attn_kernel<HS, CH>), grid, block, 0, s, p);           \
-        if (merge) hipLaunchKernelGGL((attn_merge_kernel<HS>), mgrid, block, 0, s, p); \
+#define LD_ATTN_REG_CASE(HS)                                                                      \
+    case HS:                                                                                      \
+        attn_reg_dispatch<HS>(a, grid, s, start, stop1, p);                                       \
+        if (merge) attn_dispatch(attn_merge_kernel<HS>, mgrid, s, nullptr, stop, p);               \
         break;
-        LD_ATTN_CASE(16, 64)
-        LD_ATTN_CASE(32, 64)
-        LD_ATTN_CASE(48, 64)
-        LD_ATTN_CASE(64, 64)
-        LD_ATTN_CASE(80, 64)
-        LD_ATTN_CASE(96, 64)
-        LD_ATTN_CASE(128, 32)
-        LD_ATTN_CASE(256, 16)
-#undef LD_ATTN_CASE
+        LD_ATTN_REG_CASE(16)
+        LD_ATTN_REG_CASE(32)
+        LD_ATTN_REG_CASE(48)
+        LD_ATTN_REG_CASE(64)
+        LD_ATTN_REG_CASE(80)
+        LD_ATTN_REG_CASE(96)
+        LD_ATTN_REG_CASE(128)
+#undef LD_ATTN_REG_CASE
+        case 256:
+            attn_dispatch(attn_kernel<256, 16>, grid, s, start, stop1, p);
+            if (merge) attn_dispatch(attn_merge_kernel<256>, mgrid, s, nullptr, stop, p);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

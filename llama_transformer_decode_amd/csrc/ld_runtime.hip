@@ -305,9 +305,8 @@ int launch_step(ld_model* m, Timer* timer) {
             a.n_kv_heads = c.n_kv_heads;
             a.kv_dim = m->kv_dim;
             a.nsplit = m->nsplit;
-            mark(timer, s, KATTN, true);
-            HIP_TRY(attn_launch(m->hs, a, s));
-            mark(timer, s, KATTN, false);
+            const auto ev = pair_for(timer, KATTN);
+            HIP_TRY(attn_launch(m->hs, a, s, ev.first, ev.second));
         }
         {
             GemvParams p = base_params(m);

@@ -144,6 +144,12 @@ ATTN_CASES = [  # (n_heads, n_kv_heads, head_size, pos)
     # split partials merged by the last block of each kv group: 256 and 512
     # float4 outputs per group (one and two passes of the block), four splits
     (8, 2, 256, 90), (16, 2, 256, 70), (64, 8, 128, 200),
+    # the register kernel at every head size and group width, with several
+    # splits merged by the last block (hs 48, 16, 32, 96, 80, 64) or by the
+    # merge kernel (eight heads per kv head, many splits), ragged in every tile
+    (6, 6, 48, 1500), (4, 4, 16, 3000), (3, 2, 32, 2500), (4, 1, 96, 1000), (2, 1, 80, 300),
+    (16, 2, 64, 777), (32, 4, 128, 1234), (6, 4, 48, 2047), (32, 32, 128, 255), (32, 32, 128, 256),
+    (32, 32, 128, 1025),
 ]
 
 
