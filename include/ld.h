@@ -277,6 +277,25 @@ int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d
 int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
                     int32_t n_kv_heads, int32_t head_size, int32_t pos, float* d_out, void* hip_stream);
 
+/* ld_op_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same result, bit for bit, with the split partials,
+ * the arrival counts and the position kept in a device array of
+ * LD_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends (looked up on the first call on a GPU; nothing is
+ * allocated).  The caller passes the inputs and the output as for
+ * ld_op_attention.  Every call on one GPU uses that GPU's array and leaves its
+ * contents there: calls that overlap on one GPU (on different streams, or from
+ * different threads) race and must not be made.  Asynchronous on hip_stream
+ * (NULL = the null stream): the output is ready in stream order; no call waits
+ * for the stream.  Errors: those of ld_op_attention, and LD_E_SIZE when the
+ * partials of (n_heads, head_size, pos) need more than the array holds
+ * (ld_last_error_detail gives the bytes); LD_E_HIP if the array's address
+ * cannot be found. */
+#define LD_NOALLOC_SCRATCH_BYTES (4u << 20)
+int ld_op_attention_noalloc(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_size, int32_t pos, float* d_out, void* hip_stream);
+
 /* d_out (m x n) = d_a (m x k) * d_w (n x k)^T, all fp32 row-major: the
  * matrix product of prefill, out[i][j] = sum_t a[i][t] w[j][t] ("run.c 逐行解讀"
  * §4 Matmul, for m input vectors at once).  k % 4 == 0 (else LD_E_CONFIG);

@@ -209,6 +209,8 @@ hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s, hipEve
                        hipEvent_t stop = nullptr);
 
 hipError_t set_state_launch(StepState* st, int token, int pos, hipStream_t s);
+// st->pos = pos and arrive[0 .. n_kv_heads) = 0, for one attention launch at pos
+hipError_t attn_op_init_launch(StepState* st, int pos, unsigned* arrive, int n_kv_heads, hipStream_t s);
 hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s);
 // per-block bests of v (the classifier kernel writes its own)
 hipError_t argmax_partial_launch(const float* v, int n, float2* best, int nblocks, hipStream_t s);

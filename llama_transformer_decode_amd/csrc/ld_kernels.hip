@@ -1009,6 +1009,17 @@ __global__ void set_state_kernel(StepState* st, int token, int pos) {
     st->stopped = 0;
 }
 
+// The position of a single attention launch and its zeroed split arrival counts.
+__global__ void attn_op_init_kernel(StepState* st, int pos, unsigned* arrive, int n_kv_heads) {
+    for (int i = threadIdx.x; i < n_kv_heads; i += blockDim.x) arrive[i] = 0u;
+    if (threadIdx.x == 0) {
+        st->token = 0;
+        st->pos = pos;
+        st->next = -1;
+        st->stopped = 0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Causal grouped-query attention at one position ("run.c 逐行解讀" §4 step
 // 2e), split along the key axis (flash-decoding).
@@ -2006,6 +2017,11 @@ hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* 
 
 hipError_t set_control_launch(GenControl* dst, const GenControl& c, hipStream_t s) {
     hipLaunchKernelGGL(set_control_kernel, dim3(1), dim3(1), 0, s, dst, c);
+    return hipGetLastError();
+}
+
+hipError_t attn_op_init_launch(StepState* st, int pos, unsigned* arrive, int n_kv_heads, hipStream_t s) {
+    hipLaunchKernelGGL(attn_op_init_kernel, dim3(1), dim3(256), 0, s, st, pos, arrive, n_kv_heads);
     return hipGetLastError();
 }
 

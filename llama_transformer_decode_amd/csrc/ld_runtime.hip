@@ -21,6 +21,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <map>
+#include <mutex>
 #include <utility>
 #include <new>
 #include <vector>
@@ -34,6 +35,15 @@ namespace {
 
 thread_local char g_detail[256] = "";
 
+// Device memory of ld_op_attention_noalloc: one array per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel or a
+// copy (on the host it only stands for the symbol): it uses the device
+// address hipGetSymbolAddress gives for the current GPU, looked up once per
+// device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch_ptr[kMaxDevices] = {};
+
 int fail_hip(hipError_t e, const char* what) {
     std::snprintf(g_detail, sizeof(g_detail), "%s: %s", what, hipGetErrorString(e));
     return e == hipErrorOutOfMemory ? LD_E_OOM : LD_E_HIP;
@@ -46,6 +56,35 @@ int fail_hip(hipError_t e, const char* what) {
     } while (0)
 
 bool supported_head_size(int hs) { return attn_chunk(hs) > 0; }
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[LD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).
+int scratch_for_current_device(unsigned char** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) {
+        std::snprintf(g_detail, sizeof(g_detail), "device %d beyond the %d the scratch table holds", dev, kMaxDevices);
+        return LD_E_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) {
+            std::snprintf(g_detail, sizeof(g_detail), "hipGetSymbolAddress(scratch) gave a null address");
+            return LD_E_HIP;
+        }
+        g_scratch_ptr[dev] = static_cast<unsigned char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return LD_OK;
+}
 
 int validate(const ld_config* c, const ld_options* o) {
     if (!c || !o) return LD_E_NULL;
@@ -1292,6 +1331,60 @@ int op_next_token(const float* d_v, int n, const GenControl& c, float coin, int3
     return LD_OK;
 }
 
+int op_attention_check(const float* d_q, const float* d_kc, const float* d_vc, int n_heads, int n_kv_heads,
+                       int head_size, int pos, const float* d_out) {
+    if (!d_q || !d_kc || !d_vc || !d_out) return LD_E_NULL;
+    if (n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || head_size <= 0 || head_size % 2)
+        return LD_E_CONFIG;
+    if (!supported_head_size(head_size)) return LD_E_UNSUPPORTED;
+    if ((n_heads + n_kv_heads - 1) / n_kv_heads > kMaxGroup) return LD_E_UNSUPPORTED;
+    if (pos < 0) return LD_E_RANGE;
+    if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc)) return LD_E_ALIGN;
+    return LD_OK;
+}
+
+// One attention launch at pos over caches of pos + 1 rows, with the split
+// partials, arrival counts and state in the given device buffers.  Queued on
+// s; does not wait for it.
+int op_attention_launch(const float* d_q, const float* d_kc, const float* d_vc, int n_heads, int n_kv_heads,
+                        int head_size, int pos, float* d_out, int nsplit, float2* ml, float* acc, unsigned* arrive,
+                        StepState* st, hipStream_t s) {
+    HIP_TRY(attn_op_init_launch(st, pos, arrive, n_kv_heads, s));
+    AttnParams a{};
+    a.q = d_q;
+    a.kc = d_kc;
+    a.vc = d_vc;
+    a.out = d_out;
+    a.part_ml = ml;
+    a.part_acc = acc;
+    a.arrive = arrive;
+    a.state = st;
+    a.n_heads = n_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.kv_dim = n_kv_heads * head_size;
+    a.nsplit = nsplit;
+    HIP_TRY(attn_launch(head_size, a, s));
+    return LD_OK;
+}
+
+// Where ld_op_attention_noalloc keeps its temporaries within the scratch
+// array: the state, the arrival counts, the (m, l) pairs and the value sums of
+// the split partials, each 256-byte aligned.
+struct ScratchPlan {
+    size_t state = 0, arrive = 0, ml = 0, acc = 0, bytes = 0;
+};
+
+bool plan_attention_scratch(int n_heads, int n_kv_heads, int head_size, int nsplit, ScratchPlan* p) {
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t pairs = (size_t)n_heads * nsplit;
+    p->state = 0;
+    p->arrive = up(sizeof(StepState));
+    p->ml = p->arrive + up(sizeof(unsigned) * (size_t)n_kv_heads);
+    p->acc = p->ml + up(sizeof(float2) * pairs);
+    p->bytes = p->acc + sizeof(float) * pairs * (size_t)head_size;
+    return p->bytes <= (size_t)LD_NOALLOC_SCRATCH_BYTES;
+}
+
 int op_shape_ok(int rows, int n) {
     if (rows <= 0 || n <= 0 || (n % 4)) return LD_E_CONFIG;
     if (n > kMaxN) return LD_E_UNSUPPORTED;
@@ -1413,43 +1506,42 @@ int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d
 
 int ld_op_attention(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads, int32_t n_kv_heads,
                     int32_t head_size, int32_t pos, float* d_out, void* hip_stream) {
-    if (!d_q || !d_kc || !d_vc || !d_out) return LD_E_NULL;
-    if (n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || head_size <= 0 || head_size % 2)
-        return LD_E_CONFIG;
-    if (!supported_head_size(head_size)) return LD_E_UNSUPPORTED;
-    if ((n_heads + n_kv_heads - 1) / n_kv_heads > kMaxGroup) return LD_E_UNSUPPORTED;
-    if (pos < 0) return LD_E_RANGE;
-    if (!aligned16(d_q) || !aligned16(d_kc) || !aligned16(d_vc)) return LD_E_ALIGN;
+    if (int rc = op_attention_check(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out)) return rc;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int nsplit = attn_splits(head_size, pos + 1, n_heads, n_kv_heads);
     Temps tmp;
     float2* ml = nullptr;
     float* acc = nullptr;
     StepState* st = nullptr;
+    unsigned* arrive = nullptr;
     HIP_TRY(tmp.get(&ml, (size_t)n_heads * nsplit));
     HIP_TRY(tmp.get(&acc, (size_t)n_heads * nsplit * head_size));
-    unsigned* arrive = nullptr;
     HIP_TRY(tmp.get(&arrive, (size_t)n_kv_heads));
-    HIP_TRY(hipMemsetAsync(arrive, 0, sizeof(unsigned) * n_kv_heads, s));
     HIP_TRY(tmp.get(&st, 1));
-    StepState hs_state{0, pos, -1, 0};
-    HIP_TRY(hipMemcpy(st, &hs_state, sizeof(hs_state), hipMemcpyHostToDevice));
-    AttnParams a{};
-    a.q = d_q;
-    a.kc = d_kc;
-    a.vc = d_vc;
-    a.out = d_out;
-    a.part_ml = ml;
-    a.part_acc = acc;
-    a.arrive = arrive;
-    a.state = st;
-    a.n_heads = n_heads;
-    a.n_kv_heads = n_kv_heads;
-    a.kv_dim = n_kv_heads * head_size;
-    a.nsplit = nsplit;
-    HIP_TRY(attn_launch(head_size, a, s));
+    if (int rc = op_attention_launch(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out, nsplit, ml, acc,
+                                     arrive, st, s))
+        return rc;
     HIP_TRY(hipStreamSynchronize(s));
     return LD_OK;
+}
+
+int ld_op_attention_noalloc(const float* d_q, const float* d_kc, const float* d_vc, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_size, int32_t pos, float* d_out, void* hip_stream) {
+    if (int rc = op_attention_check(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out)) return rc;
+    const int nsplit = attn_splits(head_size, pos + 1, n_heads, n_kv_heads);
+    ScratchPlan plan;
+    if (!plan_attention_scratch(n_heads, n_kv_heads, head_size, nsplit, &plan)) {
+        std::snprintf(g_detail, sizeof(g_detail),
+                      "ld_op_attention_noalloc: %zu bytes of scratch needed, the limit is %zu", plan.bytes,
+                      (size_t)LD_NOALLOC_SCRATCH_BYTES);
+        return LD_E_SIZE;
+    }
+    unsigned char* base = nullptr;
+    if (int rc = scratch_for_current_device(&base)) return rc;
+    return op_attention_launch(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out, nsplit,
+                               reinterpret_cast<float2*>(base + plan.ml), reinterpret_cast<float*>(base + plan.acc),
+                               reinterpret_cast<unsigned*>(base + plan.arrive),
+                               reinterpret_cast<StepState*>(base + plan.state), static_cast<hipStream_t>(hip_stream));
 }
 
 int ld_op_gemm(const float* d_a, const float* d_w, int32_t m, int32_t n, int32_t k, float* d_out, void* hip_stream) {
