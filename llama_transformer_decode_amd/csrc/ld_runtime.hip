@@ -49,6 +49,15 @@ int fail_hip(hipError_t e, const char* what) {
     return e == hipErrorOutOfMemory ? LD_E_OOM : LD_E_HIP;
 }
 
+// A copy of `count` elements through a staging or device buffer of `capacity`
+// elements (checked at every copy through pinned host memory, so that no
+// argument combination can reach past one).
+int check_copy(size_t count, size_t capacity, const char* what) {
+    if (count <= capacity) return 0;
+    std::snprintf(g_detail, sizeof(g_detail), "%s: %zu elements into a buffer of %zu", what, count, capacity);
+    return LD_E_RANGE;
+}
+
 #define HIP_TRY(call)                                         \
     do {                                                      \
         hipError_t e_ = (call);                               \
@@ -801,6 +810,7 @@ int run_batch_step(ld_model* m, int n) {
 
 // Stage the batch's (token, pos) pairs into the device states.
 int set_batch_states(ld_model* m, const int32_t* h_tokens, const int32_t* h_pos, int n) {
+    if (int rc = check_copy((size_t)n, (size_t)m->max_batch, "batch states")) return rc;
     if (m->bstate_pending) HIP_TRY(hipEventSynchronize(m->ev_bstate));
     for (int b = 0; b < n; ++b) m->h_bstate[b] = StepState{h_tokens[b], h_pos[b], -1, 0};
     HIP_TRY(hipMemcpyAsync(m->bstate, m->h_bstate, sizeof(StepState) * (size_t)n, hipMemcpyHostToDevice,
@@ -1031,6 +1041,7 @@ int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps,
     int rc = enter(m);
     if (rc) return rc;
     if ((rc = set_control(m, kGreedy))) return rc;
+    if ((rc = check_copy((size_t)pos + n_steps, (size_t)m->cfg.seq_len, "generated tokens"))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     for (int i = 0; i < n_steps; ++i) {
         rc = run_step(m);
@@ -1069,6 +1080,11 @@ int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t 
     // the step at position p takes forced[p + 1] while p + 1 < force_end
     const GenControl ctl = {T > 0.f ? T : 0.f, sampling->topp, sampling->stop_token, pos + 1 + n_forced};
     if ((rc = set_control(m, ctl))) return rc;
+    // staging: forced tokens at positions pos+1 .. pos+n_forced (seq_len + 1 slots), coins and tokens at
+    // positions pos .. pos+n_steps-1 (seq_len slots)
+    if ((rc = check_copy((size_t)pos + 1 + n_forced, (size_t)c.seq_len + 1, "forced tokens")) ||
+        (rc = check_copy((size_t)pos + n_steps, (size_t)c.seq_len, "coins and tokens")))
+        return rc;
     if (n_forced > 0) {
         std::memcpy(m->h_forced, h_prompt + 1, sizeof(int32_t) * (size_t)n_forced);
         HIP_TRY(hipMemcpyAsync(m->forced + pos + 1, m->h_forced, sizeof(int32_t) * (size_t)n_forced,
@@ -1131,6 +1147,7 @@ int ld_prefill_seq(ld_model* m, int32_t seq, const int32_t* h_tokens, int32_t n_
     if ((rc = set_control(m, kGreedy))) return rc;
     const int chunk = n_tokens < kPrefillChunk ? n_tokens : kPrefillChunk;
     if ((rc = prefill_workspace(m, chunk))) return rc;
+    if ((rc = check_copy((size_t)pos + n_tokens, (size_t)c.seq_len, "prompt tokens"))) return rc;
     // the staging buffer is free once the previous prefill's copy has run
     if (m->ptok_pending) HIP_TRY(hipEventSynchronize(m->ev_ptok));
     std::memcpy(m->h_ptok, h_tokens, sizeof(int32_t) * (size_t)n_tokens);
@@ -1193,6 +1210,7 @@ int ld_generate_greedy_batch(ld_model* m, const int32_t* h_tokens, const int32_t
     for (int i = 0; i < n_steps; ++i)
         if ((rc = run_batch_step(m, n))) return rc;
     const int S = m->cfg.seq_len;
+    if ((rc = check_copy((size_t)n * S, (size_t)m->max_batch * S, "batch tokens"))) return rc;
     HIP_TRY(hipMemcpyAsync(m->h_btokens, m->btokens, sizeof(int32_t) * (size_t)n * S, hipMemcpyDeviceToHost,
                            m->stream));
     HIP_TRY(hipStreamSynchronize(m->stream));
