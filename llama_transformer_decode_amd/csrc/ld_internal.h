@@ -114,6 +114,7 @@ struct AttnParams {
     int nsplit;            // grid.y: the most splits a kv head's keys are cut into at this launch
     int chunk;             // keys per tile, the unit splits are made of (set by the launcher)
     int min_tiles;         // fewest tiles a split takes (set by the launcher)
+    int waves;             // waves per block: attn_waves(...) of the model (0 = 4)
     int fuse;              // 1: the last split block of a kv group merges it (set by the launcher)
     // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
     // out and state are b * q_stride floats / b states further, its caches
@@ -203,6 +204,9 @@ int attn_chunk(int head_size);  // > 0 for a head size the attention kernels cov
 // grid.y of the attention kernel for a context of seq_len positions (the
 // splits of the longest context; shorter ones use fewer, the rest exit)
 int attn_splits(int head_size, int seq_len, int n_heads, int n_kv_heads);
+// waves per attention block for a context of seq_len positions: 4, or more
+// where the whole grid would be small (few kv heads, short context)
+int attn_waves(int head_size, int seq_len, int n_heads, int n_kv_heads);
 // attention (+ merge); start / stop (optional) as for gemv_launch: taken by the
 // attention kernel's dispatch and by the last kernel's (the merge, when it runs)
 hipError_t attn_launch(int head_size, const AttnParams& p, hipStream_t s, hipEvent_t start = nullptr,

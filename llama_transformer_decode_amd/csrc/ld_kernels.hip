@@ -1886,10 +1886,15 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s
 }
 
 // ---- attention launch shapes ----
-// Head sizes up to 128 take the register kernel with 4 waves per block; its
-// instance follows the query heads per kv head: one or two heads with 4 key
-// loads per wave batch, four or eight heads with 2 (registers grow with the
-// heads).  Head size 256 takes the LDS-staged kernel (16-key tiles).
+// Head sizes up to 128 take the register kernel; its instance follows the
+// query heads per kv head: one or two heads with 4 key loads per wave batch,
+// four or eight heads with 2 (registers grow with the heads).  Head size 256
+// takes the LDS-staged kernel (16-key tiles).
+//
+// Blocks have 4 waves where the grid is large.  Where 4-wave blocks would
+// make at most kSmallGrid blocks (few kv heads, a short context: the small
+// models), a block has 16 waves (8 for eight heads per kv head, whose merge
+// slots would not fit 16), so the few blocks cover their keys in fewer rounds.
 //
 // A split takes at least kSplitBytes of keys and values: the keys of one
 // block stream at a few tens of GB/s (one compute unit's share), so a split
@@ -1897,22 +1902,25 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s
 // at about kAttnBlocks blocks at the longest context (two per compute unit).
 constexpr int kSplitBytes = 64 << 10;
 constexpr int kAttnBlocks = 512;
+constexpr int kSmallGrid = 64;
 
 struct AttnShape {
     int reg;        // 1: register kernel
-    int gmax, u;
+    int gmax, u, nw;
     int chunk;      // keys per tile (one round of the block)
     int min_tiles;  // fewest tiles of a split
 };
 
-AttnShape attn_shape(int hs, int group) {
+AttnShape attn_shape(int hs, int group, int waves) {
     AttnShape a{};
     if (hs <= 128) {
         a.reg = 1;
         a.gmax = group <= 1 ? 1 : group <= 2 ? 2 : group <= 4 ? 4 : 8;
         a.u = a.gmax <= 2 ? 4 : 2;
-        a.chunk = (kAttnThreads / 64) * (64 / attn_lanes_per_key(hs)) * a.u;
+        a.nw = waves <= 4 ? 4 : a.gmax <= 4 ? 16 : 8;
+        a.chunk = a.nw * (64 / attn_lanes_per_key(hs)) * a.u;
     } else {
+        a.nw = kAttnThreads / 64;
         a.chunk = 16;
     }
     const int keys = (kSplitBytes + 8 * hs - 1) / (8 * hs);  // keys whose K and V rows of one head fill a split
@@ -1923,7 +1931,7 @@ AttnShape attn_shape(int hs, int group) {
 
 int attn_chunk(int hs) {
     switch (hs) {
-        case 16: case 32: case 48: case 64: case 80: case 96: case 128: case 256: return attn_shape(hs, 1).chunk;
+        case 16: case 32: case 48: case 64: case 80: case 96: case 128: case 256: return attn_shape(hs, 1, 4).chunk;
     }
     return 0;
 }
@@ -1932,9 +1940,10 @@ int attn_chunk(int hs) {
 // when each thread of that block folds at most kMaxFold splits (the merge
 // launch costs more than such a tail).  Larger groups of partials go to the
 // merge kernel.
-bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit) {
+bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit, int waves) {
     const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
-    const int slots = group * (hs / 4), kg = slots < kAttnThreads ? kAttnThreads / slots : 1;
+    const int nt = attn_shape(hs, group, waves).nw * 64;
+    const int slots = group * (hs / 4), kg = slots < nt ? nt / slots : 1;
     return nsplit > 1 && (nsplit + kg - 1) / kg <= kMaxFold;
 }
 
@@ -1942,10 +1951,9 @@ bool attn_fused(int hs, int n_heads, int n_kv_heads, int nsplit) {
 #define LD_ATTN_ONE_BLOCK_BYTES (128 << 10)
 #endif
 
-int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
-    if (!attn_chunk(hs)) return 0;
+int splits_for(int hs, int seq_len, int n_heads, int n_kv_heads, int waves) {
     const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
-    const AttnShape a = attn_shape(hs, group);
+    const AttnShape a = attn_shape(hs, group, waves);
     const int tiles = (seq_len + a.chunk - 1) / a.chunk;
     const int most = (tiles + a.min_tiles - 1) / a.min_tiles;
     int want = (kAttnBlocks + n_kv_heads - 1) / n_kv_heads;
@@ -1954,32 +1962,56 @@ int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
     // where the partials would need the merge launch (a few us even with
     // nothing to do) and a kv head's whole cache fits one block, one block per
     // kv head serves it
-    if (want > 1 && !attn_fused(hs, n_heads, n_kv_heads, want) &&
+    if (want > 1 && !attn_fused(hs, n_heads, n_kv_heads, want, waves) &&
         (long long)seq_len * hs * 2 * (long long)sizeof(float) <= LD_ATTN_ONE_BLOCK_BYTES)
         return 1;
     return want;
+}
+
+int attn_waves(int hs, int seq_len, int n_heads, int n_kv_heads) {
+    if (hs > 128) return kAttnThreads / 64;
+    return n_kv_heads * splits_for(hs, seq_len, n_heads, n_kv_heads, 4) <= kSmallGrid ? 16 : 4;
+}
+
+int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
+    if (!attn_chunk(hs)) return 0;
+    return splits_for(hs, seq_len, n_heads, n_kv_heads, attn_waves(hs, seq_len, n_heads, n_kv_heads));
 }
 
 // Launch one attention kernel (and the merge after it): with events, through
 // hipExtLaunchKernelGGL so that `start` is taken by the attention kernel's own
 // dispatch and `stop` by the last kernel's, bracketing their execution alone.
 template <class K>
-void attn_dispatch(K kernel, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop, const AttnParams& p) {
+void attn_dispatch(K kernel, dim3 grid, int threads, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                   const AttnParams& p) {
     if (start || stop)
-        hipExtLaunchKernelGGL(kernel, grid, dim3(kAttnThreads), 0, s, start, stop, 0, p);
+        hipExtLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, start, stop, 0, p);
     else
-        hipLaunchKernelGGL(kernel, grid, dim3(kAttnThreads), 0, s, p);
+        hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, p);
+}
+
+template <int HS, int NW>
+void attn_reg_dispatch_nw(int gmax, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                          const AttnParams& p) {
+    switch (gmax) {
+        case 1: attn_dispatch(attn_reg_kernel<HS, 1, 4, NW>, grid, NW * 64, s, start, stop, p); break;
+        case 2: attn_dispatch(attn_reg_kernel<HS, 2, 4, NW>, grid, NW * 64, s, start, stop, p); break;
+        default: attn_dispatch(attn_reg_kernel<HS, 4, 2, NW>, grid, NW * 64, s, start, stop, p); break;
+    }
 }
 
 template <int HS>
 void attn_reg_dispatch(const AttnShape& a, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop,
                        const AttnParams& p) {
-    constexpr int NW = kAttnThreads / 64;
-    switch (a.gmax) {
-        case 1: attn_dispatch(attn_reg_kernel<HS, 1, 4, NW>, grid, s, start, stop, p); break;
-        case 2: attn_dispatch(attn_reg_kernel<HS, 2, 4, NW>, grid, s, start, stop, p); break;
-        case 4: attn_dispatch(attn_reg_kernel<HS, 4, 2, NW>, grid, s, start, stop, p); break;
-        default: attn_dispatch(attn_reg_kernel<HS, 8, 2, NW>, grid, s, start, stop, p); break;
+    if (a.gmax == 8) {
+        if (a.nw == 4)
+            attn_dispatch(attn_reg_kernel<HS, 8, 2, 4>, grid, 256, s, start, stop, p);
+        else
+            attn_dispatch(attn_reg_kernel<HS, 8, 2, 8>, grid, 512, s, start, stop, p);
+    } else if (a.nw == 4) {
+        attn_reg_dispatch_nw<HS, 4>(a.gmax, grid, s, start, stop, p);
+    } else {
+        attn_reg_dispatch_nw<HS, 16>(a.gmax, grid, s, start, stop, p);
     }
 }
 
@@ -1987,20 +2019,21 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s, hipEvent_t s
     AttnParams p = p0;
     const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
     if (group > kMaxGroup || p.nsplit < 1) return hipErrorInvalidValue;
-    const AttnShape a = attn_shape(hs, group);
+    const int waves = p.waves > 0 ? p.waves : 4;
+    const AttnShape a = attn_shape(hs, group, waves);
     p.chunk = a.chunk;
     p.min_tiles = a.min_tiles;
     const unsigned nb = p.batch > 1 ? (unsigned)p.batch : 1u;
     const dim3 grid(p.n_kv_heads, p.nsplit, nb), mgrid(p.n_heads, 1, nb);
-    p.fuse = attn_fused(hs, p.n_heads, p.n_kv_heads, p.nsplit);
+    p.fuse = attn_fused(hs, p.n_heads, p.n_kv_heads, p.nsplit, waves);
     if (p.fuse && !p.arrive) return hipErrorInvalidValue;  // split blocks count their arrivals there
     const bool merge = p.nsplit > 1 && !p.fuse;
     hipEvent_t stop1 = merge ? nullptr : stop;  // the attention kernel's own stop event when nothing follows it
     switch (hs) {
-#define LD_ATTN_REG_CASE(HS)                                                                      \
-    case HS:                                                                                      \
-        attn_reg_dispatch<HS>(a, grid, s, start, stop1, p);                                       \
-        if (merge) attn_dispatch(attn_merge_kernel<HS>, mgrid, s, nullptr, stop, p);               \
+#define LD_ATTN_REG_CASE(HS)                                                                            \
+    case HS:                                                                                            \
+        attn_reg_dispatch<HS>(a, grid, s, start, stop1, p);                                             \
+        if (merge) attn_dispatch(attn_merge_kernel<HS>, mgrid, kAttnThreads, s, nullptr, stop, p);       \
         break;
         LD_ATTN_REG_CASE(16)
         LD_ATTN_REG_CASE(32)
@@ -2011,8 +2044,8 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s, hipEvent_t s
         LD_ATTN_REG_CASE(128)
 #undef LD_ATTN_REG_CASE
         case 256:
-            attn_dispatch(attn_kernel<256, 16>, grid, s, start, stop1, p);
-            if (merge) attn_dispatch(attn_merge_kernel<256>, mgrid, s, nullptr, stop, p);
+            attn_dispatch(attn_kernel<256, 16>, grid, kAttnThreads, s, start, stop1, p);
+            if (merge) attn_dispatch(attn_merge_kernel<256>, mgrid, kAttnThreads, s, nullptr, stop, p);
             break;
         default: return hipErrorInvalidValue;
     }

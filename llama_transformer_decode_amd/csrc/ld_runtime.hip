@@ -149,7 +149,7 @@ struct ld_model {
     ld_config cfg{};
     ld_options opt{};
     int device = 0;
-    int hs = 0, kv_dim = 0, nsplit = 0;
+    int hs = 0, kv_dim = 0, nsplit = 0, attn_waves = 4;
     const float *emb = nullptr, *rms_att = nullptr, *wq = nullptr, *wk = nullptr, *wv = nullptr, *wo = nullptr,
                 *rms_ffn = nullptr, *w1 = nullptr, *w2 = nullptr, *w3 = nullptr, *rms_final = nullptr,
                 *wcls = nullptr;
@@ -353,6 +353,7 @@ int launch_step(ld_model* m, Timer* timer) {
             a.n_kv_heads = c.n_kv_heads;
             a.kv_dim = m->kv_dim;
             a.nsplit = m->nsplit;
+            a.waves = m->attn_waves;
             const auto ev = pair_for(timer, KATTN);
             HIP_TRY(attn_launch(m->hs, a, s, ev.first, ev.second));
         }
@@ -574,6 +575,7 @@ hipError_t launch_batch_attention(ld_model* m, int n, int l) {
     a.n_kv_heads = c.n_kv_heads;
     a.kv_dim = m->kv_dim;
     a.nsplit = m->nsplit;
+    a.waves = m->attn_waves;
     a.batch = n;
     a.q_stride = c.dim;
     a.seq_stride = (size_t)c.n_layers * cache_layer;
@@ -881,6 +883,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
         m->hs = cfg->dim / cfg->n_heads;
         m->kv_dim = cfg->dim * cfg->n_kv_heads / cfg->n_heads;
         m->nsplit = attn_splits(m->hs, cfg->seq_len, cfg->n_heads, cfg->n_kv_heads);
+        m->attn_waves = attn_waves(m->hs, cfg->seq_len, cfg->n_heads, cfg->n_kv_heads);
 
         // weight pointers: 64-bit offsets into the blob
         const float* w = static_cast<const float*>(d_weights);
@@ -1381,6 +1384,7 @@ int op_attention_launch(const float* d_q, const float* d_kc, const float* d_vc, 
     a.n_kv_heads = n_kv_heads;
     a.kv_dim = n_kv_heads * head_size;
     a.nsplit = nsplit;
+    a.waves = attn_waves(head_size, pos + 1, n_heads, n_kv_heads);
     HIP_TRY(attn_launch(head_size, a, s));
     return LD_OK;
 }
