@@ -162,15 +162,20 @@ def kernel_table(cfg, stats, pos_list):
     return out
 
 
-def decode_legs(model, cfg, start: int, steps: int, reps: int, torch, kernel_timing: bool = True):
+def decode_legs(model, cfg, start: int, steps: int, reps: int, torch, kernel_timing: bool = True,
+                windows: bool = True):
     """The timed decode of one workload on a model whose weights are resident:
     `steps` greedy steps from `start` (the first token after the cache fill),
     timed `reps` times (the median is the value); the per-position windows,
     each timed `reps` times after decoding up to it untimed; and the kernel
     durations of the timed positions and of each window.  Returns a dict."""
     S = cfg.seq_len
+    t_fill = time.time()
     first_tok = fill_cache(model, cfg, start)
     torch.cuda.synchronize()
+    if start:
+        print(f"# {cfg.name}: cache filled by {start} forward calls in {time.time() - t_fill:.1f} s", file=sys.stderr,
+              flush=True)
     span = S - start
     passes = [span] * (steps // span) + ([steps % span] if steps % span else [])
     rep_times = []
@@ -185,6 +190,7 @@ def decode_legs(model, cfg, start: int, steps: int, reps: int, torch, kernel_tim
     if len(passes) > 1:
         fill_cache(model, cfg, start)
     t_med = median(rep_times)
+    print(f"# {cfg.name}: {reps} x {steps} timed steps, median {steps / t_med:.1f} tok/s", file=sys.stderr, flush=True)
     pos_all = [start + (i % span) for i in range(steps)]
     total_bytes = sum(bytes_per_token(cfg, p) for p in pos_all)
     out = {"steps": steps, "positions": [start, start + min(steps, span) - 1], "repeats": reps,
@@ -196,7 +202,7 @@ def decode_legs(model, cfg, start: int, steps: int, reps: int, torch, kernel_tim
     # per-position windows, decoding through the gaps untimed
     per_pos, win_kernels = {}, {}
     tok, pos = first_tok, start
-    for a, b in windows_for(S, start):
+    for a, b in (windows_for(S, start) if windows else []):
         if pos < a:
             tok = int(model.generate(tok, pos, a - pos)[-1])
             pos = a
@@ -280,6 +286,8 @@ def main() -> int:
                     help="comma-separated batch sizes of the timed batch-decode leg ('' to skip)")
     ap.add_argument("--sampled-steps", type=int, default=256,
                     help="steps of the temperature / top-p generation loop timed beside greedy decode (0: skip)")
+    ap.add_argument("--no-windows", action="store_true",
+                    help="skip the per-position windows (which decode the whole context): for profiler runs")
     ap.add_argument("--repeats", type=int, default=5,
                     help="times the timed decode and each per-position window are run; the median is reported")
     ap.add_argument("--long-context", default=None,
@@ -341,7 +349,8 @@ def main() -> int:
     ceiling = read_ceiling(pkg, torch) if not args.no_read_ceiling else None
 
     # ---- timed region: `steps` greedy decode steps, `repeats` times; windows; kernel durations ----
-    leg = decode_legs(model, cfg, start, steps, args.repeats, torch, kernel_timing=not args.no_kernel_timing)
+    leg = decode_legs(model, cfg, start, steps, args.repeats, torch, kernel_timing=not args.no_kernel_timing,
+                      windows=not args.no_windows)
     first_tok = leg["first_token"]
     tok_s, gbps = leg["tok_s"], leg["hbm_GBps"]
     t_total = steps / tok_s
@@ -486,7 +495,7 @@ def main() -> int:
             t = time.time()
             lsteps = lcfg.seq_len - lstart
             lleg = decode_legs(lm, lcfg, lstart, lsteps, args.repeats, torch,
-                               kernel_timing=not args.no_kernel_timing)
+                               kernel_timing=not args.no_kernel_timing, windows=not args.no_windows)
         del lweights
         torch.cuda.empty_cache()
         long_ctx = {"workload": f"{lcfg.name}: {lstart} seeded prompt tokens through forward calls (untimed), "
