@@ -70,6 +70,10 @@ def kernel_bytes(c, kind: str, pos_list) -> float:
         return 4.0 * (d * h + h + 2 * d)
     if kind == "classifier_argmax":  # Wcls + x + gain; logits written
         return 4.0 * (V * d + 2 * d + V)
+    if kind == "qkv_attention":  # the q/k/v product (q handed over on chip) and the attention: Wq, Wk, Wv + x +
+        # gain, the cache row written, key and value rows 0..pos-1 read, output
+        mean_rows = sum(p for p in pos_list) / len(pos_list)
+        return 4.0 * ((d + 2 * kv) * d + 2 * d + 2 * kv + 2 * kv * mean_rows + d)
     if kind == "attention":  # q, key and value rows 0..pos of one layer, output
         mean_rows = sum(p + 1 for p in pos_list) / len(pos_list)
         return 4.0 * (2 * d + 2 * kv * mean_rows)
@@ -272,6 +276,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps before the timed pass")
     ap.add_argument("--config", default="llama7b", help="workload: tiny, stories15m, gqa_small, llama7b, llama70b_8l")
     ap.add_argument("--no-graph", action="store_true", help="launch kernels directly instead of graph replay")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="launch every layer's attention on its own, also at short contexts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
@@ -340,7 +346,7 @@ def main() -> int:
     print(f"# {cfg.name}: {blob.nbytes / 1e9:.2f} GB of weights generated in {t_gen:.1f} s, uploaded in {t_up:.1f} s",
           file=sys.stderr, flush=True)
 
-    model = pkg.Model(cfg, weights, graph=not args.no_graph)
+    model = pkg.Model(cfg, weights, graph=not args.no_graph, fuse=not args.no_fuse)
     # warm-up: instantiates the per-token graph and touches every kernel
     if warm:
         model.generate(1, 0, min(warm, S))
@@ -489,7 +495,7 @@ def main() -> int:
         del lblob
         torch.cuda.synchronize()
         print(f"# {lcfg.name}: weights generated and uploaded in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
-        with pkg.Model(lcfg, lweights, graph=not args.no_graph) as lm:
+        with pkg.Model(lcfg, lweights, graph=not args.no_graph, fuse=not args.no_fuse) as lm:
             if warm:
                 lm.generate(1, 0, min(warm, lcfg.seq_len))
             t = time.time()

@@ -73,6 +73,15 @@ typedef struct ld_options {
 /* Replay-free mode: launch every kernel of a step directly instead of
  * replaying the captured per-token HIP graph.  Results are bit-identical. */
 #define LD_OPT_NO_GRAPH 1
+/* Every decode step launches the attention kernel of each layer on its own.
+ * Without this flag, models with dim <= 256 (where the fused launch measured
+ * faster; the fused kernel also needs head size 16, 32, 48, 64 or 128 and at
+ * most two query heads per kv head) run each layer's q/k/v product and
+ * attention as one launch (ld_op_qkv_attention) at short contexts, where the
+ * keys and values of one kv head fill at most 64 KB.  Both compute the same
+ * attention; the sums are taken in a different order, so results agree to
+ * rounding. */
+#define LD_OPT_NO_FUSE 2
 
 typedef struct ld_model ld_model;
 
@@ -231,7 +240,9 @@ const char* ld_last_error_detail(void);
  * (their interval is the kernels' execution), the classifier (GEMV and
  * next-token kernels) between events recorded on the stream around them.  Reports per kernel kind the launch count
  * and the summed event time.  Kinds: "qkv_rope_append", "attention", "wo_residual",
- * "w1w3_swiglu", "w2_residual", "classifier_argmax".  stats must hold
+ * "w1w3_swiglu", "w2_residual", "classifier_argmax", and "qkv_attention" (the
+ * q/k/v product with the attention in the same launch, at short contexts
+ * unless LD_OPT_NO_FUSE).  stats must hold
  * max_stats entries; *n_stats_out receives the number filled.  Synchronous.
  */
 typedef struct ld_kernel_stat {
@@ -270,6 +281,21 @@ int ld_op_swiglu(const float* d_x, const float* d_g, float eps, const float* d_w
 int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d_wq, const float* d_wk,
                    const float* d_wv, int32_t dim, int32_t n_heads, int32_t n_kv_heads, int32_t pos,
                    float theta, float* d_q, float* d_k, float* d_v, void* hip_stream);
+
+/* The q/k/v product and the attention of one layer at pos in one launch
+ * (§4 steps 2a-2e), the kernel of the decode step at short contexts: x' =
+ * RMSNorm(x, g) (no norm when d_g == NULL), q = Wq x', k = Wk x', v = Wv x',
+ * RoPE at pos on q and k, k and v written to row pos of d_kc / d_vc (rows of
+ * kv_dim floats; rows 0..pos-1 are read as the earlier keys and values), then
+ * d_out (dim floats) = the causal attention of every query head over rows
+ * 0..pos, query head h on kv head floor(h*n_kv/n_heads).  q itself is not
+ * returned.  Synchronous.  Errors: LD_E_NULL, LD_E_CONFIG, LD_E_RANGE (pos <
+ * 0), LD_E_ALIGN, LD_E_UNSUPPORTED for a shape without the fused kernel (head
+ * size other than 16/32/48/64/128, more than two query heads per kv head or 64
+ * kv heads, dim > 4096), LD_E_HIP. */
+int ld_op_qkv_attention(const float* d_x, const float* d_g, float eps, const float* d_wq, const float* d_wk,
+                        const float* d_wv, int32_t dim, int32_t n_heads, int32_t n_kv_heads, int32_t pos,
+                        float theta, float* d_kc, float* d_vc, float* d_out, void* hip_stream);
 
 /* Causal GQA attention of one layer at pos (§4 step 2e): d_q (n_heads *
  * head_size), d_kc / d_vc (at least pos+1 rows of kv_dim floats), d_out

@@ -14,7 +14,7 @@ import numpy as np
 
 from . import ld
 from .ld import (LD_E_ALIGN, LD_E_CONFIG, LD_E_HIP, LD_E_NULL, LD_E_OOM, LD_E_RANGE, LD_E_SIZE,
-                 LD_E_UNSUPPORTED, LD_OK, LD_OPT_NO_GRAPH, LdError, library)
+                 LD_E_UNSUPPORTED, LD_OK, LD_OPT_NO_FUSE, LD_OPT_NO_GRAPH, LdError, library)
 
 __all__ = ["ld", "Model", "LdError", "library", "copy_from_device", "copy_to_device"]
 
@@ -72,7 +72,7 @@ class Model:
     """
 
     def __init__(self, cfg, weights, *, graph: bool = True, shared_classifier=None, norm_eps=None,
-                 rope_theta=None, stream=None, max_batch: int = 1):
+                 rope_theta=None, stream=None, max_batch: int = 1, fuse: bool = True):
         import torch
         if not (weights.is_cuda and weights.dtype == torch.float32 and weights.is_contiguous()):
             raise ValueError("weights must be a contiguous float32 CUDA tensor")
@@ -82,7 +82,8 @@ class Model:
         eps = getattr(cfg, "norm_eps", 1e-5) if norm_eps is None else norm_eps
         theta = getattr(cfg, "rope_theta", 10000.0) if rope_theta is None else rope_theta
         self.c = ld.make_config(cfg)
-        self.o = ld.make_options(eps, theta, int(shared), 0 if graph else LD_OPT_NO_GRAPH, int(max_batch))
+        flags = (0 if graph else LD_OPT_NO_GRAPH) | (0 if fuse else LD_OPT_NO_FUSE)
+        self.o = ld.make_options(eps, theta, int(shared), flags, int(max_batch))
         self.max_batch = max(1, int(max_batch))
         self.stream = stream or torch.cuda.current_stream()
         self.kv_dim = cfg.dim * cfg.n_kv_heads // cfg.n_heads

@@ -53,6 +53,8 @@ enum GemvKind : int {
     K_QKV = 2,     // [Wq;Wk;Wv] x', RoPE on q and k, k/v into cache row pos
     K_SWIGLU = 3,  // hb[e] = silu(W1 x')[e] * (W3 x')[e]
     K_CLS = 4,     // logits[r] = Wcls x', then the greedy argmax
+    K_QKV_ATT = 5, // K_QKV, q/k/v also handed to the attention of the same
+                   // launch (qkv_attention_launch); q itself is not stored
 };
 
 // Launch geometry: `nt` threads per block, each holding `nx` float4 of x;
@@ -90,6 +92,17 @@ struct GemvParams {
     const float2* rope;    // K_QKV: (position, head_size/2) -> (cos, sin)
     StepState* state;
     float2* best;          // K_CLS: per-block (value, index bits)
+    // K_QKV_ATT: row r of [Wq;Wk;Wv] x' (after RoPE) also goes to
+    // stage[(r / head_size) * stage_sh + r % head_size] (one slot per q head,
+    // then per k head, then per v head; stage_sh a multiple of 64 floats); the
+    // block that completes a kv group's rows (count in arrive[group], zero
+    // before and after every launch) writes that group's attention to att_out
+    float* stage;
+    int stage_sh;
+    unsigned* arrive;
+    float* att_out;
+    int n_heads;
+    int n_kv_heads;
     // the batch kernel (GemvPlan.nb > 0): vectors 0..nb-1, vector b at x + b ldx
     // (out + b ldo, x_resid + b ldr); K_QKV: vector b is sequence b at
     // row_state[b].pos, its caches seq_stride floats after sequence b-1's
@@ -116,6 +129,7 @@ struct AttnParams {
     int min_tiles;         // fewest tiles a split takes (set by the launcher)
     int waves;             // waves per block: attn_waves(...) of the model (0 = 4)
     int fuse;              // 1: the last split block of a kv group merges it (set by the launcher)
+    int stage_sh;          // q/k/v from a hand-off stage (the fused q/k/v kernel): its slot stride
     // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
     // out and state are b * q_stride floats / b states further, its caches
     // b * seq_stride floats, its split partials b * (n_heads * nsplit) pairs
@@ -199,6 +213,18 @@ hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan);
 // their interval is the kernel's execution alone
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s, hipEvent_t start = nullptr,
                        hipEvent_t stop = nullptr);
+
+// The q/k/v kernel with the layer's attention in the same launch (kind
+// K_QKV_ATT): whether (rows n of x, head size, query heads per kv head) has a
+// compiled kernel, the floats of its hand-off stage, and its launch (the plan
+// from gemv_plan(K_QKV_ATT, ...)).
+bool qkv_attention_supported(int n, int head_size, int n_heads, int n_kv_heads);
+bool qkv_attention_pays(int n);  // whether the decode step should use it (measured)
+hipError_t qkv_attention_plan(int n, int head_size, int n_heads, int n_kv_heads, GemvPlan* plan);
+size_t qkv_attention_stage_floats(int head_size, int n_heads, int n_kv_heads);
+int qkv_attention_stage_stride(int head_size);
+hipError_t qkv_attention_launch(const GemvPlan& plan, const GemvParams& p, hipStream_t s, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
 
 int attn_chunk(int head_size);  // > 0 for a head size the attention kernels cover
 // grid.y of the attention kernel for a context of seq_len positions (the

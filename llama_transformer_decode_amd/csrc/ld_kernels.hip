@@ -568,6 +568,46 @@ __global__ __launch_bounds__(NT) void next_token_kernel(NextTokenParams p) {
 #define LD_NT_LOADS 1  // weight loads carry the non-temporal hint (each is used once)
 #endif
 
+// Data handed between blocks of one launch (attention split partials, the
+// fused q/k/v kernel's stage), which may run on different XCDs with separate
+// L2 caches.  They are stored and loaded with agent-scope relaxed atomics (32
+// or 64 bits at a time), which the compiler issues with the coherence bit set:
+// stores write through the L2 and loads read past stale lines, so no
+// cache-wide write-back or invalidate is needed.
+__device__ __forceinline__ unsigned long long pack2(float a, float b) {
+    return ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
+}
+__device__ __forceinline__ float2 unpack2(unsigned long long v) {
+    return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), pack2(v.x, v.y), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float4* p, float4 v) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    __hip_atomic_store(q, pack2(v.x, v.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, pack2(v.z, v.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent(const float2* p) {
+    return unpack2(
+        __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float4 load_coherent(const float4* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const float2 a = unpack2(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float2 b = unpack2(__hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
+// Wait until this thread's vector memory operations have completed
+// (s_waitcnt vmcnt(0)).  The memory clobber also keeps the compiler from
+// moving any load or store across it.
+__device__ __forceinline__ void wait_vector_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 typedef float native_float4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 load_w(const float4* p) {
@@ -579,6 +619,8 @@ __device__ __forceinline__ float4 load_w(const float4* p) {
 #endif
 }
 
+constexpr bool is_qkv_kind(int kind) { return kind == K_QKV || kind == K_QKV_ATT; }
+
 // Rows of row group u.  K_SWIGLU interleaves w1 and w3 rows of the same
 // hidden unit; K_QKV walks the three matrices wq | wk | wv as one.
 template <int RPI, int KIND>
@@ -589,7 +631,7 @@ __device__ __forceinline__ void group_rows(const GemvParams& p, int u, const flo
         if constexpr (KIND == K_SWIGLU) {
             const int e = min(u * (RPI / 2) + r / 2, p.rows - 1);
             wr[r] = ((r & 1) ? p.w1 : p.w0) + (size_t)e * n;
-        } else if constexpr (KIND == K_QKV) {
+        } else if constexpr (is_qkv_kind(KIND)) {
             const int row = min(u * RPI + r, p.rows - 1);
             wr[r] = row < p.seg1   ? p.w0 + (size_t)row * n
                     : row < p.seg2 ? p.w1 + (size_t)(row - p.seg1) * n
@@ -624,7 +666,7 @@ __device__ __forceinline__ void load_group(const GemvParams& p, int u, int n4, f
 }
 
 template <int NT, int NX, int RPI, int KIND>
-__global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
+__device__ void gemv_body(const GemvParams& p) {
     constexpr int NW = NT / 64;
     __shared__ float red[2][NW][RPI];
     __shared__ float ss_part[NW];
@@ -638,7 +680,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
 
     int pos = 0, token = 0, stopped = 0;
-    if constexpr (KIND == K_QKV || KIND == K_CLS) {
+    if constexpr (is_qkv_kind(KIND) || KIND == K_CLS) {
         pos = p.state->pos;
         token = p.state->token;
         stopped = p.state->stopped;
@@ -646,7 +688,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
 
     // ---- prologue: x (layer 0 of the q/k/v kernel reads the embedding row) ----
     const float* xsrc = p.x;
-    if constexpr (KIND == K_QKV) {
+    if constexpr (is_qkv_kind(KIND)) {
         if (p.emb) xsrc = p.emb + (size_t)token * (size_t)p.n;
     }
     const float4* x4 = reinterpret_cast<const float4*>(xsrc);
@@ -656,7 +698,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
         const int idx = tid + k * NT;
         xr[k] = zero_unless(idx < n4, x4[min(idx, n4 - 1)]);
     }
-    if constexpr (KIND == K_QKV) {
+    if constexpr (is_qkv_kind(KIND)) {
         if (p.emb && blockIdx.x == 0) {
             float4* xo = reinterpret_cast<float4*>(p.x_resid);
 #pragma unroll
@@ -738,32 +780,37 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
         } else if constexpr (KIND == K_RESID) {
             const int row = u * RPI + tid;
             if (tid < RPI && row < p.rows) p.x_resid[row] = res_cur + total;
-        } else if constexpr (KIND == K_QKV) {
+        } else if constexpr (is_qkv_kind(KIND)) {
             // RoPE ("run.c 逐行解讀" §4 step 2d): rows 2j, 2j+1 of a head form
             // one pair, turned by the angle pos * theta^(-2j/head_size); the
             // (cos, sin) of that angle come from the table.  q rows are
             // rotated, k rows are rotated and written to cache row pos, v rows
-            // go to the value cache unrotated (step 2b).
+            // go to the value cache unrotated (step 2b).  K_QKV_ATT hands
+            // every row to the attention through the stage as well, and keeps
+            // q there only.
             const float other = __shfl_xor(total, 1);
             const int row = u * RPI + tid;
             if (tid < RPI && row < p.rows) {
                 const bool odd = tid & 1;
+                const int hs = p.head_size;
+                float v = total;
                 if (row < p.seg2) {
                     const bool is_q = row < p.seg1;
                     const int local = is_q ? row : row - p.seg1;
-                    const int hs = p.head_size;
                     const int j = (local % hs) >> 1;
                     const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + j];
                     const float a = odd ? other : total;  // element 2j
                     const float b = odd ? total : other;  // element 2j+1
-                    const float v = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
-                    if (is_q)
-                        p.out[row] = v;
-                    else if (!stopped)
+                    v = odd ? (a * cs.y + b * cs.x) : (a * cs.x - b * cs.y);
+                    if (is_q) {
+                        if constexpr (KIND == K_QKV) p.out[row] = v;
+                    } else if (!stopped) {
                         p.kc[(size_t)pos * p.kv_stride + local] = v;
+                    }
                 } else if (!stopped) {
                     p.vc[(size_t)pos * p.kv_stride + (row - p.seg2)] = total;
                 }
+                if constexpr (KIND == K_QKV_ATT) store_coherent(p.stage + (size_t)(row / hs) * p.stage_sh + row % hs, v);
             }
         } else if constexpr (KIND == K_SWIGLU) {
             // hb = silu(w1 x) * (w3 x), silu(u) = u * 1/(1 + e^-u) ("run.c
@@ -790,6 +837,11 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
     }
 
     if constexpr (KIND == K_CLS) publish_best<NT>(bv, bi, p.best);
+}
+
+template <int NT, int NX, int RPI, int KIND>
+__global__ __launch_bounds__(NT) void gemv_kernel(GemvParams p) {
+    gemv_body<NT, NX, RPI, KIND>(p);
 }
 
 // The same product for a few vectors at once (a decode batch of up to NB
@@ -1091,37 +1143,6 @@ __device__ __forceinline__ AttnParams seq_view(const AttnParams& p) {
     return v;
 }
 
-// Split partials pass between blocks of one launch, which may run on
-// different XCDs with separate L2 caches.  They are stored and loaded with
-// agent-scope relaxed atomics (64 bits at a time), which the compiler issues
-// with the coherence bit set: stores write through the L2 and loads read past
-// stale lines, so no cache-wide write-back or invalidate is needed.
-__device__ __forceinline__ unsigned long long pack2(float a, float b) {
-    return ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
-}
-__device__ __forceinline__ float2 unpack2(unsigned long long v) {
-    return make_float2(__uint_as_float((unsigned)v), __uint_as_float((unsigned)(v >> 32)));
-}
-__device__ __forceinline__ void store_coherent(float2* p, float2 v) {
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), pack2(v.x, v.y), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(float4* p, float4 v) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
-    __hip_atomic_store(q, pack2(v.x, v.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, pack2(v.z, v.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_coherent(const float2* p) {
-    return unpack2(
-        __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ float4 load_coherent(const float4* p) {
-    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
-    const float2 a = unpack2(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const float2 b = unpack2(__hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    return make_float4(a.x, a.y, b.x, b.y);
-}
-
 __device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
     return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
 }
@@ -1195,11 +1216,6 @@ __device__ void merge_group(const AttnParams& p, int h_lo, int G, int nact) {
         }
     }
 }
-
-// Wait until this thread's vector memory operations have completed
-// (s_waitcnt vmcnt(0)).  The memory clobber also keeps the compiler from
-// moving any load or store across it.
-__device__ __forceinline__ void wait_vector_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Called by every thread of a split block after it has stored its partial
 // (coherent stores).  Each thread waits for its stores to complete before
@@ -1427,16 +1443,21 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
-template <int HS, int GMAX, int U, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
+// Block (kv head g, split s) of the register kernel.  STAGED: the tail of the
+// fused q/k/v kernel, one split over every key.  q and the key and value rows
+// of the current position were written by other blocks of that launch and are
+// read from its stage with coherent loads; the rows before the position come
+// from the cache (written by earlier launches).  The block's key loop covers
+// the cached rows, and wave 0 folds the current position's key in at the end.
+template <int HS, int GMAX, int U, int NW, bool STAGED>
+__device__ void attend_reg(const AttnParams& p, int g, int s) {
     constexpr int H4 = HS / 4, LPK = attn_lanes_per_key(HS), KPW = 64 / LPK;
     constexpr int BK = KPW * U;  // keys of one wave batch
     constexpr int CH = NW * BK;  // keys of one round of the block
     static_assert(H4 <= LPK && LPK <= 32, "a key row within one lane group of at most half a wave");
-    const AttnParams p = seq_view<HS>(pb);
     __shared__ float4 acc_s[NW][GMAX][H4];
     __shared__ float ms_s[NW][GMAX], ls_s[NW][GMAX], w_s[NW][GMAX], M_s[GMAX];
-    const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, sub = lane / LPK, c = lane % LPK;
     const int cc = c < H4 ? c : H4 - 1;
     int h_lo, G;
@@ -1444,16 +1465,30 @@ __global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
 
     // q does not depend on the position: its loads go out beside the state's
     float4 q[GMAX];
-    const float4* q4 = reinterpret_cast<const float4*>(p.q);
+    float4 k_cur = make_float4(0.f, 0.f, 0.f, 0.f), v_cur = k_cur;
+    if constexpr (STAGED) {
+        const float4* st4 = reinterpret_cast<const float4*>(p.q);
+        const int sh4 = p.stage_sh / 4;
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh)
-        q[hh] = hh < G && c < H4 ? q4[(size_t)(h_lo + hh) * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int hh = 0; hh < GMAX; ++hh)
+            q[hh] = hh < G && c < H4 ? load_coherent(st4 + (size_t)(h_lo + hh) * sh4 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (wave == 0) {
+            k_cur = load_coherent(st4 + (size_t)(p.n_heads + g) * sh4 + cc);
+            v_cur = load_coherent(st4 + (size_t)(p.n_heads + p.n_kv_heads + g) * sh4 + cc);
+        }
+    } else {
+        const float4* q4 = reinterpret_cast<const float4*>(p.q);
+#pragma unroll
+        for (int hh = 0; hh < GMAX; ++hh)
+            q[hh] = hh < G && c < H4 ? q4[(size_t)(h_lo + hh) * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     const int n = p.state->pos + 1;
     int tiles, per, nact;
     split_of(n, CH, p.nsplit, p.min_tiles, tiles, per, nact);
     if (s >= nact) return;
-    const int kb = s * per * CH, ke = min(n, (s + 1) * per * CH);  // this block's keys
+    // this block's keys from the cache (STAGED: all but the current position's)
+    const int kb = s * per * CH, ke = min(STAGED ? n - 1 : n, (s + 1) * per * CH);
 
     const float* kbase = p.kc + (size_t)g * HS + 4 * cc;
     const float* vbase = p.vc + (size_t)g * HS + 4 * cc;
@@ -1461,7 +1496,7 @@ __global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
     auto load = [&](int b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = min(kb + b * BK + u * KPW + sub, n - 1);  // past the end: re-read the last key
+            const int t = min(kb + b * BK + u * KPW + sub, ke - 1);  // past the end: re-read the block's last key
             K[u] = *reinterpret_cast<const float4*>(kbase + (size_t)t * p.kv_dim);
             V[u] = *reinterpret_cast<const float4*>(vbase + (size_t)t * p.kv_dim);
         }
@@ -1533,6 +1568,28 @@ __global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
         }
     }
 
+    if constexpr (STAGED) {
+        // the current position's key, scored by every lane group of wave 0
+        // (each holds the whole row) and added by key slot 0
+        if (wave == 0) {
+#pragma unroll
+            for (int hh = 0; hh < GMAX; ++hh) {
+                float sc;
+                if constexpr (LPK == 32)
+                    sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(half_sum(dot4(k_cur, q[hh], 0.f))), 31));
+                else
+                    sc = lane_group_sum<LPK>(dot4(k_cur, q[hh], 0.f));
+                sc *= scale;
+                const float mn = fmaxf(m[hh], sc);
+                const float r = exp2_fast(m[hh] - mn);  // 0 when no cached key came before
+                const float e = sub == 0 ? exp2_fast(sc - mn) : 0.f;
+                acc[hh] = fma4(e, v_cur, make_float4(acc[hh].x * r, acc[hh].y * r, acc[hh].z * r, acc[hh].w * r));
+                l[hh] = fmaf(l[hh], r, e);
+                m[hh] = mn;
+            }
+        }
+    }
+
     // lanes c, c + LPK, ... hold the same column over different keys: add them,
     // then merge the waves through LDS
 #pragma unroll
@@ -1579,6 +1636,78 @@ __global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
         }
     }
     if (nact > 1 && p.fuse) arrive_and_merge<HS, NW * 64>(p, g, h_lo, G, nact);
+}
+
+template <int HS, int GMAX, int U, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_reg_kernel(AttnParams pb) {
+    const AttnParams p = seq_view<HS>(pb);
+    attend_reg<HS, GMAX, U, NW, false>(p, blockIdx.x, blockIdx.y);
+}
+
+// The q/k/v product and the layer's attention in one launch ("run.c 逐行解讀"
+// §4 steps 2a-2e; kind K_QKV_ATT).  Each block runs the q/k/v GEMV on its row
+// groups, which also stores every row to the stage with coherent stores.  It
+// then waits until those stores have completed and counts, per kv group, the
+// rows it wrote of that group (the q rows of its query heads, its k and v
+// rows) into arrive[group] with an atomic add.  The block whose add completes
+// a group's (G + 2) * HS rows resets the counter for the next launch and runs
+// the group's attention with all its threads (attend_reg, STAGED), reading
+// the stage with coherent loads.  No block waits for another, so the grid
+// always drains.  One block per kv group streams its keys: the launch serves
+// short contexts.
+constexpr int kMaxFusedKv = 64;   // kv heads a fused launch covers
+
+// Key loads per lane of a wave batch: 2 for blocks of 4 waves or more (the
+// q/k/v product keeps its occupancy), 4 for the narrow blocks of the small
+// models' products.
+constexpr int fused_u(int nt) { return nt >= 256 ? 2 : 4; }
+
+template <int NT, int NX, int RPI, int HS, int GMAX>
+__global__ __launch_bounds__(NT) void qkv_attention_kernel(GemvParams p) {
+    gemv_body<NT, NX, RPI, K_QKV_ATT>(p);
+    __shared__ int groups_s[kMaxFusedKv];
+    __shared__ int ngroups_s;
+    const int tid = threadIdx.x;
+    const int u0 = (int)(((long long)blockIdx.x * p.units) / gridDim.x);
+    const int u1 = (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    const int r0 = u0 * RPI, r1 = min(u1 * RPI, p.rows);  // the rows this block wrote
+    const int H = p.n_heads, KV = p.n_kv_heads;
+    if (tid == 0) ngroups_s = 0;
+    wait_vector_memory();
+    __syncthreads();
+    auto overlap = [&](int a, int b) { return max(0, min(b, r1) - max(a, r0)); };
+    for (int g = tid; g < KV; g += NT) {
+        int h_lo, G;
+        group_of(g, H, KV, h_lo, G);
+        const int cnt = overlap(h_lo * HS, (h_lo + G) * HS) + overlap(p.seg1 + g * HS, p.seg1 + (g + 1) * HS) +
+                        overlap(p.seg2 + g * HS, p.seg2 + (g + 1) * HS);
+        if (cnt > 0) {
+            const unsigned before = atomicAdd(p.arrive + g, (unsigned)cnt);
+            if (before + (unsigned)cnt == (unsigned)((G + 2) * HS)) {
+                atomicExch(p.arrive + g, 0u);
+                groups_s[atomicAdd(&ngroups_s, 1)] = g;
+            }
+        }
+    }
+    __syncthreads();
+    const int ng = ngroups_s;
+    if (ng == 0) return;
+    AttnParams a{};
+    a.q = p.stage;
+    a.kc = p.kc;
+    a.vc = p.vc;
+    a.out = p.att_out;
+    a.state = p.state;
+    a.n_heads = H;
+    a.n_kv_heads = KV;
+    a.kv_dim = p.kv_stride;
+    a.nsplit = 1;
+    a.min_tiles = 1;
+    a.stage_sh = p.stage_sh;
+    for (int i = 0; i < ng; ++i) {
+        attend_reg<HS, GMAX, fused_u(NT), NT / 64, true>(a, groups_s[i], 0);
+        __syncthreads();  // the next group reuses the attention's LDS
+    }
 }
 
 // Exact merge of the split partials of query head blockIdx.x, one block per
@@ -1693,7 +1822,7 @@ constexpr Tpl kTpl[] = {
 constexpr int kNumTpl = sizeof(kTpl) / sizeof(kTpl[0]);
 
 constexpr int rows_per_group(int t, int kind) {
-    return (kind == K_QKV || kind == K_SWIGLU) && kTpl[t].rpi < 2 ? 2 : kTpl[t].rpi;
+    return (is_qkv_kind(kind) || kind == K_SWIGLU) && kTpl[t].rpi < 2 ? 2 : kTpl[t].rpi;
 }
 
 using GemvFn = void (*)(GemvParams);
@@ -1781,6 +1910,45 @@ GemvFn gemv_batch_fn_kind(int kind, int t) {
     return nullptr;
 }
 
+// The fused q/k/v + attention kernels: GEMV shapes up to n = 4096 (kTpl[0..3]),
+// head sizes 16 / 32 / 48 / 64 / 128, one or two query heads per kv head.
+constexpr int kFusedTpl = 4;
+
+bool fused_head_size(int hs) { return hs == 16 || hs == 32 || hs == 48 || hs == 64 || hs == 128; }
+
+template <int T, int HS, int GMAX>
+GemvFn qkv_att_fn_t() {
+    return qkv_attention_kernel<kTpl[T].nt, kTpl[T].nx, rows_per_group(T, K_QKV_ATT), HS, GMAX>;
+}
+
+template <int T, int HS>
+GemvFn qkv_att_fn_g(int gmax) {
+    return gmax <= 1 ? qkv_att_fn_t<T, HS, 1>() : qkv_att_fn_t<T, HS, 2>();
+}
+
+template <int T>
+GemvFn qkv_att_fn_h(int hs, int gmax) {
+    switch (hs) {
+        case 16: return qkv_att_fn_g<T, 16>(gmax);
+        case 32: return qkv_att_fn_g<T, 32>(gmax);
+        case 48: return qkv_att_fn_g<T, 48>(gmax);
+        case 64: return qkv_att_fn_g<T, 64>(gmax);
+        case 128: return qkv_att_fn_g<T, 128>(gmax);
+    }
+    return nullptr;
+}
+
+GemvFn qkv_att_fn(int t, int hs, int gmax) {
+    if (gmax > 2) return nullptr;
+    switch (t) {
+        case 0: return qkv_att_fn_h<0>(hs, gmax);
+        case 1: return qkv_att_fn_h<1>(hs, gmax);
+        case 2: return qkv_att_fn_h<2>(hs, gmax);
+        case 3: return qkv_att_fn_h<3>(hs, gmax);
+    }
+    return nullptr;
+}
+
 int template_for(const GemvPlan& pl) {
     if (pl.nb) {
         for (int t = 0; t < kNumTplB; ++t)
@@ -1803,6 +1971,7 @@ int divisor_in(int units, int lo, int hi) {
 
 hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan) {
     if (n <= 0 || rows <= 0 || (n & 3) || n > kMaxN) return hipErrorInvalidValue;
+    if (kind == K_QKV_ATT) return hipErrorInvalidValue;  // qkv_attention_plan
     const int n4 = n / 4;
     int t = 0;
     while (t < kNumTpl && kTpl[t].nt * kTpl[t].nx < n4) ++t;
@@ -1868,7 +2037,79 @@ hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan) {
     return hipSuccess;
 }
 
+bool qkv_attention_supported(int n, int head_size, int n_heads, int n_kv_heads) {
+    if (n <= 0 || (n & 3) || head_size <= 0 || n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads) return false;
+    if (n_kv_heads > kMaxFusedKv || !fused_head_size(head_size)) return false;
+    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
+    return group <= 2 && n <= kTpl[kFusedTpl - 1].nt * kTpl[kFusedTpl - 1].nx * 4;
+}
+
+// Measured on whole decode steps (kernel events, positions 0-15): the fused
+// launch took 7.5 against 4.5 + 4.3 us per layer for the tiny shape (dim 64,
+// single-wave q/k/v blocks), but 10.4 against 4.7 + 4.3 us (stories15M
+// shape), 9.5 against 4.3 + 4.3 (GQA-small) and 39.2 against 31.8 + 4.2 (7B
+// shape).  The hand-off (stores written through to memory and waited for, the
+// arrival count, the coherent loads of the last block) costs more than the
+// kernel boundary it replaces wherever the product's blocks have more than one
+// wave, so the decode step uses it only where they have one.
+bool qkv_attention_pays(int n) { return n > 0 && n <= kTpl[0].nt * kTpl[0].nx * 4; }
+
+int qkv_attention_stage_stride(int head_size) { return (head_size + 63) / 64 * 64; }
+
+size_t qkv_attention_stage_floats(int head_size, int n_heads, int n_kv_heads) {
+    return (size_t)(n_heads + 2 * n_kv_heads) * (size_t)qkv_attention_stage_stride(head_size);
+}
+
+hipError_t qkv_attention_plan(int n, int head_size, int n_heads, int n_kv_heads, GemvPlan* plan) {
+    if (!qkv_attention_supported(n, head_size, n_heads, n_kv_heads)) return hipErrorInvalidValue;
+    const int n4 = n / 4;
+    int t = 0;
+    while (kTpl[t].nt * kTpl[t].nx < n4) ++t;
+    const int rows = (n_heads + 2 * n_kv_heads) * head_size;
+    const int rpi = rows_per_group(t, K_QKV_ATT);
+    plan->kind = K_QKV_ATT;
+    plan->nt = kTpl[t].nt;
+    plan->nx = kTpl[t].nx;
+    plan->rpi = rpi;
+    plan->nb = 0;
+    plan->units = (rows + rpi - 1) / rpi;
+    const int group = (n_heads + n_kv_heads - 1) / n_kv_heads;
+    int dev = 0, cus = 0, occ = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, qkv_att_fn(t, head_size, group), plan->nt, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    const int slots = cus * occ;
+    plan->grid = plan->units <= slots ? plan->units : slots;
+    return hipSuccess;
+}
+
+hipError_t qkv_attention_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s, hipEvent_t start,
+                                hipEvent_t stop) {
+    const int t = template_for(plan);
+    if (plan.kind != K_QKV_ATT || t < 0 || t >= kFusedTpl) return hipErrorInvalidValue;
+    GemvParams p = p0;
+    p.units = plan.units;
+    if (!p.stage || !p.arrive || !p.att_out || p.stage_sh < p.head_size || (p.stage_sh & 63)) return hipErrorInvalidValue;
+    if (!qkv_attention_supported(p.n, p.head_size, p.n_heads, p.n_kv_heads) ||
+        p.rows != (p.n_heads + 2 * p.n_kv_heads) * p.head_size || p.seg1 != p.n_heads * p.head_size ||
+        p.seg2 != p.seg1 + p.n_kv_heads * p.head_size)
+        return hipErrorInvalidValue;
+    const int group = (p.n_heads + p.n_kv_heads - 1) / p.n_kv_heads;
+    GemvFn fn = qkv_att_fn(t, p.head_size, group);
+    if (!fn) return hipErrorInvalidValue;
+    if (start || stop)
+        hipExtLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.nt), 0, s, start, stop, 0, p);
+    else
+        hipLaunchKernelGGL(fn, dim3(plan.grid), dim3(plan.nt), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    if (plan.kind == K_QKV_ATT) return qkv_attention_launch(plan, p0, s, start, stop);
     const int t = template_for(plan);
     if (t < 0) return hipErrorInvalidValue;
     GemvParams p = p0;

@@ -132,9 +132,17 @@ long long blob_floats(const ld_config* c, const ld_options* o) {
     return f;
 }
 
-enum Kind { KQKV = 0, KATTN, KWO, KFFN, KW2, KCLS, KNUM };
-const char* kKindName[KNUM] = {"qkv_rope_append", "attention", "wo_residual",
-                               "w1w3_swiglu",     "w2_residual", "classifier_argmax"};
+enum Kind { KQKV = 0, KATTN, KWO, KFFN, KW2, KCLS, KQKVA, KNUM };
+const char* kKindName[KNUM] = {"qkv_rope_append", "attention",         "wo_residual",  "w1w3_swiglu",
+                               "w2_residual",     "classifier_argmax", "qkv_attention"};
+
+// Steps whose context holds at most this many bytes of keys and values per kv
+// head run the q/k/v product and the attention as one launch (one block per kv
+// group streams the keys) where that launch pays (qkv_attention_pays); longer
+// contexts launch the split attention kernel.
+#ifndef LD_FUSE_KEY_BYTES
+#define LD_FUSE_KEY_BYTES (64 << 10)
+#endif
 
 // Events around each launch, for ld_profile_steps.
 struct Timer {
@@ -201,6 +209,14 @@ struct ld_model {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     bool use_graph = true;
+    // short contexts: the q/k/v kernel with the attention in the same launch
+    // (positions pos with pos + 1 <= fuse_keys), its own captured step
+    int fuse_keys = 0;
+    GemvPlan pqa{};
+    float* stage = nullptr;
+    unsigned* qkv_arrive = nullptr;  // (n_kv_heads) kept at zero between launches
+    hipGraph_t graph_f = nullptr;
+    hipGraphExec_t exec_f = nullptr;
     std::vector<void*> dev_allocs;
 };
 
@@ -222,6 +238,8 @@ void release(ld_model* m) {
     if (m->stream) (void)hipStreamSynchronize(m->stream);
     if (m->exec) (void)hipGraphExecDestroy(m->exec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
+    if (m->exec_f) (void)hipGraphExecDestroy(m->exec_f);
+    if (m->graph_f) (void)hipGraphDestroy(m->graph_f);
     for (auto& g : m->batch_graphs) {
         if (g.second.second) (void)hipGraphExecDestroy(g.second.second);
         if (g.second.first) (void)hipGraphDestroy(g.second.first);
@@ -310,14 +328,44 @@ std::pair<hipEvent_t, hipEvent_t> pair_for(Timer* t, int kind) {
     return {t->ev[i], t->ev[i + 1]};
 }
 
-// One decode step, reading (token, pos) from m->state.
-int launch_step(ld_model* m, Timer* timer) {
+// Whether the step at position pos takes the fused q/k/v + attention launch.
+bool fused_at(const ld_model* m, long long pos) { return pos + 1 <= m->fuse_keys; }
+
+// One decode step, reading (token, pos) from m->state.  fused: the q/k/v
+// kernel also runs the attention (for positions with fused_at).
+int launch_step(ld_model* m, Timer* timer, bool fused) {
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
     const size_t cache_layer = (size_t)c.seq_len * kv;
     hipStream_t s = m->stream;
     for (int l = 0; l < c.n_layers; ++l) {
-        {
+        if (fused) {
+            GemvParams p = base_params(m);
+            p.x = m->x;
+            p.emb = l == 0 ? m->emb : nullptr;
+            p.x_resid = m->x;
+            p.gain = m->rms_att + (size_t)l * d;
+            p.n = c.dim;
+            p.rows = c.dim + 2 * m->kv_dim;
+            p.w0 = m->wq + (size_t)l * d * d;
+            p.w1 = m->wk + (size_t)l * kv * d;
+            p.w2 = m->wv + (size_t)l * kv * d;
+            p.seg1 = c.dim;
+            p.seg2 = c.dim + m->kv_dim;
+            p.kc = m->kc + (size_t)l * cache_layer;
+            p.vc = m->vc + (size_t)l * cache_layer;
+            p.kv_stride = m->kv_dim;
+            p.head_size = m->hs;
+            p.rope = m->rope;
+            p.stage = m->stage;
+            p.stage_sh = qkv_attention_stage_stride(m->hs);
+            p.arrive = m->qkv_arrive;
+            p.att_out = m->xb;
+            p.n_heads = c.n_heads;
+            p.n_kv_heads = c.n_kv_heads;
+            const auto ev = pair_for(timer, KQKVA);
+            HIP_TRY(qkv_attention_launch(m->pqa, p, s, ev.first, ev.second));
+        } else {
             GemvParams p = base_params(m);
             p.x = m->x;
             p.emb = l == 0 ? m->emb : nullptr;
@@ -339,7 +387,7 @@ int launch_step(ld_model* m, Timer* timer) {
             const auto ev = pair_for(timer, KQKV);
             HIP_TRY(gemv_launch(m->pq, p, s, ev.first, ev.second));
         }
-        {
+        if (!fused) {
             AttnParams a{};
             a.q = m->q;
             a.kc = m->kc + (size_t)l * cache_layer;
@@ -415,10 +463,12 @@ int launch_step(ld_model* m, Timer* timer) {
     return LD_OK;
 }
 
-int ensure_graph(ld_model* m) {
-    if (m->exec) return LD_OK;
+int ensure_graph(ld_model* m, bool fused) {
+    hipGraph_t& graph = fused ? m->graph_f : m->graph;
+    hipGraphExec_t& exec = fused ? m->exec_f : m->exec;
+    if (exec) return LD_OK;
     HIP_TRY(hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
-    int rc = launch_step(m, nullptr);
+    int rc = launch_step(m, nullptr, fused);
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamEndCapture(m->stream, &g);
     if (rc != LD_OK) {
@@ -426,19 +476,23 @@ int ensure_graph(ld_model* m) {
         return rc;
     }
     if (e != hipSuccess) return fail_hip(e, "hipStreamEndCapture");
-    m->graph = g;
-    HIP_TRY(hipGraphInstantiate(&m->exec, m->graph, nullptr, nullptr, 0));
+    graph = g;
+    HIP_TRY(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
     return LD_OK;
 }
 
-int run_step(ld_model* m) {
+// The step at position pos (the position the device state holds when the
+// step runs; after a stop token the state stays put, and either launch
+// sequence leaves it so).
+int run_step(ld_model* m, long long pos) {
+    const bool fused = fused_at(m, pos);
     if (m->use_graph) {
-        int rc = ensure_graph(m);
+        int rc = ensure_graph(m, fused);
         if (rc != LD_OK) return rc;
-        HIP_TRY(hipGraphLaunch(m->exec, m->stream));
+        HIP_TRY(hipGraphLaunch(fused ? m->exec_f : m->exec, m->stream));
         return LD_OK;
     }
-    return launch_step(m, nullptr);
+    return launch_step(m, nullptr, fused);
 }
 
 // Tokens per prefill chunk: chunks run one after another, each attending to
@@ -943,6 +997,18 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             break;
         rc = dalloc(m, &m->best, (size_t)m->pcls.grid);
         if (rc) break;
+        if (!(opt->flags & LD_OPT_NO_FUSE) && qkv_attention_pays(cfg->dim) &&
+            qkv_attention_supported(cfg->dim, m->hs, cfg->n_heads, cfg->n_kv_heads)) {
+            e = qkv_attention_plan(cfg->dim, m->hs, cfg->n_heads, cfg->n_kv_heads, &m->pqa);
+            if (e != hipSuccess) { rc = fail_hip(e, "qkv_attention_plan"); break; }
+            if ((rc = dalloc(m, &m->stage, qkv_attention_stage_floats(m->hs, cfg->n_heads, cfg->n_kv_heads))) ||
+                (rc = dalloc(m, &m->qkv_arrive, (size_t)cfg->n_kv_heads)))
+                break;
+            e = hipMemset(m->qkv_arrive, 0, sizeof(unsigned) * (size_t)cfg->n_kv_heads);
+            if (e != hipSuccess) { rc = fail_hip(e, "hipMemset"); break; }
+            const int keys = LD_FUSE_KEY_BYTES / (8 * m->hs);
+            m->fuse_keys = keys < 1 ? 1 : keys < cfg->seq_len ? keys : cfg->seq_len;
+        }
         {  // batch buffers (also for max_batch 1, so a batch of one runs)
             const size_t B = m->max_batch;
             if ((rc = dalloc(m, &m->bx, B * d)) || (rc = dalloc(m, &m->bq, B * d)) ||
@@ -1019,7 +1085,7 @@ int ld_forward(ld_model* m, int32_t token, int32_t pos, const float** d_logits_o
     if (rc) return rc;
     if ((rc = set_control(m, kGreedy))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
-    rc = run_step(m);
+    rc = run_step(m, pos);
     if (rc) return rc;
     *d_logits_out = m->logits;
     return leave(m);
@@ -1047,7 +1113,7 @@ int ld_generate_greedy(ld_model* m, int32_t token, int32_t pos, int32_t n_steps,
     if ((rc = check_copy((size_t)pos + n_steps, (size_t)m->cfg.seq_len, "generated tokens"))) return rc;
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     for (int i = 0; i < n_steps; ++i) {
-        rc = run_step(m);
+        rc = run_step(m, (long long)pos + i);
         if (rc) return rc;
     }
     HIP_TRY(hipMemcpyAsync(m->h_tokens, m->tokens + pos, sizeof(int32_t) * (size_t)n_steps, hipMemcpyDeviceToHost,
@@ -1111,7 +1177,7 @@ int ld_generate(ld_model* m, const int32_t* h_prompt, int32_t n_prompt, int32_t 
     for (int chunk = 0; issued < n_steps; ++chunk) {
         const int k = n_steps - issued < kChunk ? n_steps - issued : kChunk;
         for (int i = 0; i < k; ++i)
-            if ((rc = run_step(m))) return rc;
+            if ((rc = run_step(m, (long long)pos + issued + i))) return rc;
         issued += k;
         if (!polls || issued >= n_steps) continue;
         const int slot = chunk & 1;
@@ -1259,14 +1325,14 @@ int ld_profile_steps(ld_model* m, int32_t token, int32_t pos, int32_t n_steps, l
     HIP_TRY(set_state_launch(m->state, token, pos, m->stream));
     for (int i = 0; i < n_steps && rc == LD_OK; ++i) {
         t.used = 0;
-        rc = launch_step(m, &t);
+        rc = launch_step(m, &t, fused_at(m, (long long)pos + i));
         if (rc) break;
         hipError_t err = hipStreamSynchronize(m->stream);
         if (err != hipSuccess) {
             rc = fail_hip(err, "hipStreamSynchronize");
             break;
         }
-        for (int k = 0; k < launches; ++k) {
+        for (int k = 0; k < (int)(t.used / 2); ++k) {
             float ms = 0.f;
             err = hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1]);
             if (err != hipSuccess) {
@@ -1522,6 +1588,65 @@ int ld_op_qkv_rope(const float* d_x, const float* d_g, float eps, const float* d
     p.rope = rope;
     p.state = st;
     HIP_TRY(gemv_launch(pl, p, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return LD_OK;
+}
+
+int ld_op_qkv_attention(const float* d_x, const float* d_g, float eps, const float* d_wq, const float* d_wk,
+                        const float* d_wv, int32_t dim, int32_t n_heads, int32_t n_kv_heads, int32_t pos, float theta,
+                        float* d_kc, float* d_vc, float* d_out, void* hip_stream) {
+    if (!d_x || !d_wq || !d_wk || !d_wv || !d_kc || !d_vc || !d_out) return LD_E_NULL;
+    if (dim <= 0 || n_heads <= 0 || n_kv_heads <= 0 || n_kv_heads > n_heads || dim % n_heads ||
+        ((long long)dim * n_kv_heads) % n_heads || ((dim / n_heads) % 2) || !(theta > 0.f))
+        return LD_E_CONFIG;
+    const int hs = dim / n_heads, kv = (int)((long long)dim * n_kv_heads / n_heads);
+    if ((dim % 4) || (kv % 4)) return LD_E_CONFIG;
+    if (pos < 0) return LD_E_RANGE;
+    if (!qkv_attention_supported(dim, hs, n_heads, n_kv_heads)) return LD_E_UNSUPPORTED;
+    if (!aligned16(d_x) || !aligned16(d_wq) || !aligned16(d_wk) || !aligned16(d_wv) || !aligned16(d_kc) ||
+        !aligned16(d_vc) || !aligned16(d_out) || (d_g && !aligned16(d_g)))
+        return LD_E_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    Temps tmp;
+    float2* rope = nullptr;
+    StepState* st = nullptr;
+    float* stage = nullptr;
+    unsigned* arrive = nullptr;
+    HIP_TRY(tmp.get(&rope, (size_t)(pos + 1) * (hs / 2)));
+    HIP_TRY(tmp.get(&st, 1));
+    HIP_TRY(tmp.get(&stage, qkv_attention_stage_floats(hs, n_heads, n_kv_heads)));
+    HIP_TRY(tmp.get(&arrive, (size_t)n_kv_heads));
+    std::vector<float2> rt = rope_table(pos + 1, hs, (double)theta);
+    HIP_TRY(hipMemcpy(rope, rt.data(), rt.size() * sizeof(float2), hipMemcpyHostToDevice));
+    StepState hs_state{0, pos, -1, 0};
+    HIP_TRY(hipMemcpy(st, &hs_state, sizeof(hs_state), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemset(arrive, 0, sizeof(unsigned) * (size_t)n_kv_heads));
+    GemvPlan pl;
+    HIP_TRY(qkv_attention_plan(dim, hs, n_heads, n_kv_heads, &pl));
+    GemvParams p{};
+    p.x = d_x;
+    p.gain = d_g;
+    p.eps = eps;
+    p.n = dim;
+    p.rows = dim + 2 * kv;
+    p.w0 = d_wq;
+    p.w1 = d_wk;
+    p.w2 = d_wv;
+    p.seg1 = dim;
+    p.seg2 = dim + kv;
+    p.kc = d_kc;
+    p.vc = d_vc;
+    p.kv_stride = kv;
+    p.head_size = hs;
+    p.rope = rope;
+    p.state = st;
+    p.stage = stage;
+    p.stage_sh = qkv_attention_stage_stride(hs);
+    p.arrive = arrive;
+    p.att_out = d_out;
+    p.n_heads = n_heads;
+    p.n_kv_heads = n_kv_heads;
+    HIP_TRY(qkv_attention_launch(pl, p, s));
     HIP_TRY(hipStreamSynchronize(s));
     return LD_OK;
 }

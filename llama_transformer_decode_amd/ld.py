@@ -23,6 +23,7 @@ LD_E_OOM = -6
 LD_E_HIP = -7
 LD_E_UNSUPPORTED = -8
 LD_OPT_NO_GRAPH = 1
+LD_OPT_NO_FUSE = 2
 LD_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every symbol include/ld.h declares.
@@ -31,7 +32,7 @@ EXPORTS = (
     "ld_generate", "ld_prefill", "ld_prefill_seq", "ld_forward_batch", "ld_generate_greedy_batch", "ld_kv_cache", "ld_destroy", "ld_strerror", "ld_last_error_detail",
     "ld_profile_steps", "ld_op_rmsnorm_gemv", "ld_op_gemv_residual", "ld_op_swiglu", "ld_op_qkv_rope",
     "ld_op_attention", "ld_op_gemm", "ld_op_attention_prefill", "ld_op_argmax", "ld_op_sample",
-    "ld_op_stream_read", "ld_op_attention_noalloc",
+    "ld_op_stream_read", "ld_op_attention_noalloc", "ld_op_qkv_attention",
 )
 
 
@@ -105,6 +106,7 @@ def library():
             "ld_op_gemv_residual": ([_P, _P, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_swiglu": ([_P, _P, _F, _P, _P, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_qkv_rope": ([_P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P], ctypes.c_int),
+            "ld_op_qkv_attention": ([_P, _P, _F, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P], ctypes.c_int),
             "ld_op_attention": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_attention_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], ctypes.c_int),
             "ld_op_gemm": ([_P, _P, _I, _I, _I, _P, _P], ctypes.c_int),
@@ -271,6 +273,12 @@ def ld_op_qkv_rope(d_x, d_g, eps, d_wq, d_wk, d_wv, dim, n_heads, n_kv_heads, po
                    stream=0):
     _check(library().ld_op_qkv_rope(d_x, d_g or None, eps, d_wq, d_wk, d_wv, dim, n_heads, n_kv_heads, pos, theta,
                                     d_q, d_k, d_v, stream or None), "ld_op_qkv_rope")
+
+
+def ld_op_qkv_attention(d_x, d_g, eps, d_wq, d_wk, d_wv, dim, n_heads, n_kv_heads, pos, theta, d_kc, d_vc, d_out,
+                        stream=0):
+    _check(library().ld_op_qkv_attention(d_x, d_g or None, eps, d_wq, d_wk, d_wv, dim, n_heads, n_kv_heads, pos,
+                                         theta, d_kc, d_vc, d_out, stream or None), "ld_op_qkv_attention")
 
 
 def ld_op_attention(d_q, d_kc, d_vc, n_heads, n_kv_heads, head_size, pos, d_out, stream=0):

@@ -187,10 +187,25 @@ def test_tied_classifier_reads_the_embedding_table():
 
 def test_profile_counts_every_launch():
     cfg, b, w = blob_of("gqa_small")
-    with pkg.Model(cfg, w) as m:
-        stats = {s["name"]: s for s in m.profile(1, 0, 4)}
     L = cfg.n_layers
-    want = {"qkv_rope_append": L, "attention": L, "wo_residual": L, "w1w3_swiglu": L, "w2_residual": L,
-            "classifier_argmax": 1}
-    for k, per_step in want.items():
-        assert stats[k]["launches"] == 4 * per_step and stats[k]["total_ms"] > 0
+    for fuse in (False, True):  # dim 288: the fused launch is not used either way
+        with pkg.Model(cfg, w, fuse=fuse) as m:
+            stats = {s["name"]: s for s in m.profile(1, 0, 4)}
+        want = {"qkv_rope_append": L, "attention": L, "wo_residual": L, "w1w3_swiglu": L, "w2_residual": L,
+                "classifier_argmax": 1}
+        for k, per_step in want.items():
+            assert stats[k]["launches"] == 4 * per_step and stats[k]["total_ms"] > 0
+        assert stats["qkv_attention"]["launches"] == 0
+
+
+def test_profile_counts_fused_launches():
+    # the tiny shape (dim 64) takes the fused q/k/v + attention launch at every
+    # position of its context (64 keys of 2 x 16 floats per kv head: 8 KB)
+    cfg, b, w = blob_of("tiny")
+    L = cfg.n_layers
+    with pkg.Model(cfg, w) as m:
+        stats = {s["name"]: s for s in m.profile(1, 60, 4)}
+    want = {"qkv_attention": 4 * L, "qkv_rope_append": 0, "attention": 0, "wo_residual": 4 * L,
+            "w1w3_swiglu": 4 * L, "w2_residual": 4 * L, "classifier_argmax": 4}
+    for k, n in want.items():
+        assert stats[k]["launches"] == n, k

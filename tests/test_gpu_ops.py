@@ -136,6 +136,110 @@ def test_qkv_rope(dim, H, KV, pos):
     assert np.all(np.abs(host(v) - v0) <= gemv_bound(wv, xp, v0))
 
 
+QKV_ATT_CASES = [  # (dim, n_heads, n_kv_heads, pos): the fused shapes of the workloads, and every
+    # head size and group width the fused kernel covers, at position 0 (no cached key), a few keys, and
+    # contexts of several key rounds of the block
+    (64, 4, 4, 0), (64, 4, 4, 1), (64, 4, 4, 63), (288, 6, 6, 0), (288, 6, 6, 100), (288, 6, 6, 255),
+    (288, 6, 4, 0), (288, 6, 4, 17), (288, 6, 4, 511), (4096, 32, 32, 0), (4096, 32, 32, 1), (4096, 32, 32, 63),
+    (4096, 32, 32, 200), (128, 4, 2, 9), (256, 4, 4, 30), (512, 8, 4, 40), (1024, 8, 8, 70), (96, 6, 3, 5),
+    (2048, 16, 16, 130),
+]
+
+
+@pytest.mark.parametrize("dim,H,KV,pos", QKV_ATT_CASES)
+def test_qkv_attention(dim, H, KV, pos):
+    """The fused q/k/v + attention launch against the oracle's q/k/v, RoPE and
+    attention (steps 2a-2e), with rows above pos poisoned and row pos poisoned
+    before the call (the kernel must write it, and take the current key and
+    value from its own hand-off).  Bound: the attention of exact inputs (as in
+    test_attention) plus the effect of the q/k/v products' rounding on the
+    scores, taken from the worst pair error seen over the key rows."""
+    hs, kv = dim // H, dim // H * KV
+    s = 7100 + dim + 3 * pos + KV
+    wq = _normal(dim * dim, s, 1, std=0.02).reshape(dim, dim)
+    wk = _normal(kv * dim, s, 2, std=0.02).reshape(kv, dim)
+    wv = _normal(kv * dim, s, 3, std=0.02).reshape(kv, dim)
+    x = _normal(dim, s, 4)
+    g = _normal(dim, s, 5, 1.0, 0.01)
+    rows = pos + 3
+    kc = _normal(rows * kv, s, 6).reshape(rows, kv)
+    vc = _normal(rows * kv, s, 7).reshape(rows, kv)
+    kc[pos:] = np.nan
+    vc[pos:] = np.nan
+    out = dev(np.full(dim, np.nan, np.float32))
+    dx, dg, dwq, dwk, dwv, dk, dv = dev(x), dev(g), dev(wq), dev(wk), dev(wv), dev(kc), dev(vc)
+    ld.ld_op_qkv_attention(dx.data_ptr(), dg.data_ptr(), 1e-5, dwq.data_ptr(), dwk.data_ptr(), dwv.data_ptr(), dim, H,
+                           KV, pos, 10000.0, dk.data_ptr(), dv.data_ptr(), out.data_ptr())
+    xp = oracle.rmsnorm(x, g, 1e-5)
+    q0, k0, v = oracle.matvec(wq, xp), oracle.matvec(wk, xp), oracle.matvec(wv, xp)
+    q, k = oracle.rope(q0, H, hs, pos), oracle.rope(k0, KV, hs, pos)
+
+    def rotated_bound(w, base):  # as in test_qkv_rope: a rotation mixes the bounds of a pair
+        e = gemv_bound(w, xp, base)
+        mag = np.hypot(base[0::2].astype(np.float64), base[1::2]).repeat(2)
+        return np.maximum(e[0::2], e[1::2]).repeat(2) * 2 + 4 * U32 * mag + 1e-30
+
+    kc_got, vc_got = host(dk), host(dv)
+    # row pos of the caches: the rotated k and the v of this position
+    kbound = rotated_bound(wk, k0)
+    assert np.all(np.abs(kc_got[pos] - k) <= kbound)
+    assert np.all(np.abs(vc_got[pos] - v) <= gemv_bound(wv, xp, v))
+    assert np.all(np.isnan(kc_got[pos + 1:])) and np.all(np.isnan(vc_got[pos + 1:]))
+    kc[pos], vc[pos] = k, v
+    ref = oracle.attention(q, kc[: pos + 1], vc[: pos + 1], H, KV, hs, pos)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    # scores move by at most |dq|.|k| + |q|.|dk| (scaled); softmax weights by a
+    # factor within exp(+-2 max shift)
+    qb = rotated_bound(wq, q0)
+    kk = np.abs(kc[: pos + 1].astype(np.float64))
+    shift = 0.0
+    for h in range(H):
+        gk = h * KV // H
+        sl, kl = slice(h * hs, (h + 1) * hs), slice(gk * hs, (gk + 1) * hs)
+        ds = kk[:, kl] @ qb[sl] + np.abs(q[sl]) @ kbound[kl]
+        shift = max(shift, float(np.max(ds)) / np.sqrt(hs))
+    vmax = float(np.max(np.abs(vc[: pos + 1])))
+    bound = 2e-5 * vmax + 2 * np.expm1(2 * shift) * vmax + float(np.max(gemv_bound(wv, xp, v)))
+    assert np.max(np.abs(got - ref)) <= bound, (float(np.max(np.abs(got - ref))), bound)
+
+
+def test_qkv_attention_matches_the_separate_kernels():
+    """Fused and separate launches compute the same q/k/v rows and attention:
+    the cache rows agree bit for bit, the attention to rounding."""
+    dim, H, KV, pos = 288, 6, 4, 40
+    hs, kv = dim // H, dim // H * KV
+    s = 7300
+    wq = _normal(dim * dim, s, 1, std=0.02).reshape(dim, dim)
+    wk = _normal(kv * dim, s, 2, std=0.02).reshape(kv, dim)
+    wv = _normal(kv * dim, s, 3, std=0.02).reshape(kv, dim)
+    x = _normal(dim, s, 4)
+    g = _normal(dim, s, 5, 1.0, 0.01)
+    kc = _normal((pos + 1) * kv, s, 6).reshape(pos + 1, kv)
+    vc = _normal((pos + 1) * kv, s, 7).reshape(pos + 1, kv)
+    dx, dg, dwq, dwk, dwv = dev(x), dev(g), dev(wq), dev(wk), dev(wv)
+    dk1, dv1, out1 = dev(kc), dev(vc), dev(np.zeros(dim, np.float32))
+    ld.ld_op_qkv_attention(dx.data_ptr(), dg.data_ptr(), 1e-5, dwq.data_ptr(), dwk.data_ptr(), dwv.data_ptr(), dim, H,
+                           KV, pos, 10000.0, dk1.data_ptr(), dv1.data_ptr(), out1.data_ptr())
+    q, k, v = (dev(np.zeros(m, np.float32)) for m in (dim, kv, kv))
+    ld.ld_op_qkv_rope(dx.data_ptr(), dg.data_ptr(), 1e-5, dwq.data_ptr(), dwk.data_ptr(), dwv.data_ptr(), dim, H, KV,
+                      pos, 10000.0, q.data_ptr(), k.data_ptr(), v.data_ptr())
+    kc[pos], vc[pos] = host(k), host(v)
+    assert np.array_equal(host(dk1), kc) and np.array_equal(host(dv1), vc)
+    dk2, dv2, out2 = dev(kc), dev(vc), dev(np.zeros(dim, np.float32))
+    ld.ld_op_attention(q.data_ptr(), dk2.data_ptr(), dv2.data_ptr(), H, KV, hs, pos, out2.data_ptr())
+    assert np.max(np.abs(host(out1) - host(out2))) <= 2e-6 * np.max(np.abs(vc))
+
+
+def test_qkv_attention_unsupported_shapes():
+    x = dev(np.zeros(8192, np.float32))
+    p = x.data_ptr()
+    for dim, H, KV in ((8192, 64, 8), (240, 3, 3), (512, 16, 2)):  # dim > 4096; head size 80; 8 heads per kv head
+        with pytest.raises(ld.LdError) as e:
+            ld.ld_op_qkv_attention(p, p, 1e-5, p, p, p, dim, H, KV, 0, 10000.0, p, p, p)
+        assert e.value.status == ld.LD_E_UNSUPPORTED
+
+
 ATTN_CASES = [  # (n_heads, n_kv_heads, head_size, pos)
     (4, 4, 16, 0), (4, 4, 16, 1), (4, 4, 16, 63), (6, 6, 48, 64), (6, 6, 48, 255), (6, 4, 48, 0), (6, 4, 48, 65),
     (6, 4, 48, 511), (32, 32, 128, 0), (32, 32, 128, 31), (32, 32, 128, 32), (32, 32, 128, 33),
