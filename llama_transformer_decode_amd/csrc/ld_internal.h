@@ -140,6 +140,47 @@ struct AttnParams {
     size_t seq_stride;
 };
 
+// Batch decode of up to kTiledBatch sequences on the matrix cores with
+// pre-tiled weights (tiled_launch).  Tiled weights: a product's rows and K
+// (both multiples of 16) form 16 x 16 tiles; tile (rt, kt) is 64 float4 at
+// float4 offset (rt * K/16 + kt) * 64, float4 l holding row 16 rt + l % 16 at
+// k = 16 kt + 4 (l / 16) + 0..3, times the gain of the product's RMSNorm at k.
+// Tiled activations: float4 (kt * 64 + l) = x[l % 16][16 kt + 4 (l / 16) + 0..3]
+// for sequences 0..15.
+constexpr int kTiledBatch = 16;
+
+struct TiledParams {
+    const float* w;        // tiled weights (gain folded in)
+    const float* x;        // input: tiled (x_tiled) or row-major with stride ldx
+    int x_tiled;
+    int ldx;
+    int k;                 // input length
+    int rows;              // output rows (K_SWIGLU: 2 x hidden, w1 and w3 rows interleaved)
+    int nb;                // sequences, 1..kTiledBatch
+    int norm;              // scale row b by 1/sqrt(mean(x_b^2) + eps) (the RMSNorm's row scale)
+    float eps;
+    float* out;            // K_PLAIN, K_QKV (q): out[b * ldo + r]
+    int ldo;
+    float* x_resid;        // K_RESID: x_resid[b * ldr + r] += C
+    int ldr;
+    float* out_t;          // K_RESID: the new residual, K_SWIGLU: hb, tiled (NULL: none)
+    int seg1, seg2;        // K_QKV as GemvParams
+    float* kc;
+    float* vc;
+    int kv_stride;
+    int head_size;
+    const float2* rope;
+    const StepState* row_state;  // K_QKV: sequence b at row_state[b].pos
+    size_t seq_stride;
+};
+
+// Pack rows x k weights into the tiled layout: kind K_PLAIN (w0), K_QKV (w0 |
+// w1 | w2 with the row segments seg1, seg2), K_SWIGLU (row 2u = w0 row u, 2u+1
+// = w1 row u), each column times gain[k] (gain may be NULL).
+hipError_t tile_weights_launch(int kind, const float* w0, const float* w1, const float* w2, int seg1, int seg2,
+                               const float* gain, int rows, int k, float* dst, hipStream_t s);
+hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s);
+
 // Prompt prefill (ld_prefill.hip).  C(M x N) = A(M x K) B(N x K)^T on the
 // matrix cores, A the T tokens' activations, B's rows the weight rows, with
 // the decode GEMVs' epilogues.
@@ -193,7 +234,9 @@ struct AttnPrefillParams {
 hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s);
 // a decode batch: x[b] = E[st[b].token]; the greedy token of every logits row,
 // tokens_out[b * tokens_stride + pos_b], and each sequence's state advances
-hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s);
+// xt (optional): the same rows in the tiled layout of TiledParams (batch <= kTiledBatch)
+hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s,
+                              float* xt = nullptr);
 hipError_t argmax_rows_launch(const float* logits, int batch, int n, StepState* st, int32_t* tokens_out,
                               int tokens_stride, hipStream_t s);
 hipError_t gemm_launch(int kind, const GemmParams& p, hipStream_t s);

@@ -983,6 +983,172 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
 // are measured against.  Block b sums its contiguous range of the buffer
 // (non-temporal 16-byte loads, 16 per thread in flight, like the weight
 // loads of the GEMVs) into sums[b]; the sums keep the loads live.
+// ---------------------------------------------------------------------------
+// Batch decode of up to 16 sequences on the matrix cores, weights pre-tiled
+// (TiledParams): the q/k/v, wo, w1/w3, w2 and classifier products of a decode
+// step over the batch's vectors, C(rows x nb) = W x_b.  Each wave loads whole
+// 1 KB tiles (64 lanes x 16 contiguous bytes) and feeds each lane's float4 to
+// four v_mfma_f32_16x16x4f32 steps as the A operand (rows 16 rt + l % 16, k
+// 16 kt + 4 (l / 16) + t at step t), with the tiled activations as the B
+// operand (sequence l % 16 at the same k).  Weights stream once for the whole
+// batch without an LDS stage.  A block takes RT row tiles over all of K: its
+// NW waves take the k tiles round robin (wave w: tiles w, w + NW, ..., so the
+// block reads NW consecutive tiles per step), then add their partial tiles
+// through LDS in wave order.  The output lane l holds rows 16 rt + 4 (l / 16)
+// + 0..3 of sequence l % 16: RoPE pairs and SwiGLU (w1, w3) pairs sit in one
+// lane.  RMSNorm: the gain is folded into the tiled weights, and each
+// sequence's sum of squares is accumulated from the same activations, so the
+// row scale multiplies the result.
+
+// float4 slot of x[b][k] (k a multiple of 4) in the tiled activations
+__host__ __device__ __forceinline__ size_t tiled_slot(int b, int k) {
+    return (size_t)(k >> 4) * 64 + ((k & 15) >> 2) * 16 + b;
+}
+
+__device__ __forceinline__ float f4c(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
+
+__global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float* __restrict__ w0,
+                                                           const float* __restrict__ w1,
+                                                           const float* __restrict__ w2, int seg1, int seg2,
+                                                           const float* __restrict__ gain, int rows, int k,
+                                                           float4* __restrict__ dst) {
+    const size_t n4 = (size_t)rows * (size_t)k / 4;
+    const int kt_n = k / 16;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        const size_t tile = i / 64;
+        const int l = (int)(i % 64);
+        const int rt = (int)(tile / kt_n), kt = (int)(tile % kt_n);
+        const int row = 16 * rt + (l & 15), col = 16 * kt + 4 * (l >> 4);
+        const float* src;
+        if (kind == K_QKV)
+            src = row < seg1 ? w0 + (size_t)row * k : row < seg2 ? w1 + (size_t)(row - seg1) * k : w2 + (size_t)(row - seg2) * k;
+        else if (kind == K_SWIGLU)
+            src = ((row & 1) ? w1 : w0) + (size_t)(row >> 1) * k;
+        else
+            src = w0 + (size_t)row * k;
+        float4 v = *reinterpret_cast<const float4*>(src + col);
+        if (gain) {
+            const float4 g = *reinterpret_cast<const float4*>(gain + col);
+            v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+        }
+        dst[i] = v;
+    }
+}
+
+template <int NW, int RT, int D, int KIND, int XT>
+__global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    __shared__ v4 red[NW][RT][64];
+    __shared__ float ss_s[NW][16];
+    const int KT = p.k >> 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, c = lane & 15;
+    const int rt0 = blockIdx.x * RT;
+    const float4* wt = reinterpret_cast<const float4*>(p.w) + (size_t)rt0 * KT * 64 + lane;
+    const float* xbase = XT ? p.x + 4 * lane : p.x + (size_t)min(c, p.nb - 1) * p.ldx + 4 * q;
+    const int nsteps = (KT + NW - 1) / NW;  // this wave: tiles wave, wave + NW, ... below KT
+
+    v4 acc[RT];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) acc[j] = v4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    float4 w[D][RT], xv[D];
+    auto load = [&](int kk0) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int kt = min((kk0 + d) * NW + wave, KT - 1);  // past the end: re-read the last tile (not used)
+#pragma unroll
+            for (int j = 0; j < RT; ++j) w[d][j] = wt[((size_t)j * KT + kt) * 64];
+            xv[d] = *reinterpret_cast<const float4*>(xbase + (XT ? (size_t)kt * 256 : (size_t)kt * 16));
+        }
+    };
+    load(0);
+    for (int kk = 0; kk < nsteps; kk += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if ((kk + d) * NW + wave < KT) {  // wave-uniform
+                if (p.norm) ss = dot4(xv[d], xv[d], ss);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int j = 0; j < RT; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4c(w[d][j], t), f4c(xv[d], t), acc[j], 0, 0, 0);
+            }
+        }
+        // keep the next loads after these products: hoisting them would hold
+        // two sets of tiles in registers at once (a second register set, loaded
+        // while the first is multiplied, measured no faster)
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + D < nsteps) load(kk + D);
+    }
+#pragma unroll
+    for (int j = 0; j < RT; ++j) red[wave][j][lane] = acc[j];
+    if (p.norm) {  // lanes c, c + 16, c + 32, c + 48 hold sequence c's k in parts
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (lane < 16) ss_s[wave][lane] = ss;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < RT * 64; e += NW * 64) {
+        const int j = e >> 6, l = e & 63, b = l & 15;
+        if (b >= p.nb) continue;
+        v4 sum = red[0][j][l];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][j][l];
+        if (p.norm) {
+            float t = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) t += ss_s[w2][b];
+            sum *= 1.0f / sqrtf(t / (float)p.k + p.eps);
+        }
+        const int r0 = 16 * (rt0 + j) + 4 * (l >> 4);  // rows r0 .. r0 + 3 of sequence b
+        if (r0 >= p.rows) continue;
+        if constexpr (KIND == K_PLAIN) {
+            *reinterpret_cast<float4*>(p.out + (size_t)b * p.ldo + r0) = make_float4(sum[0], sum[1], sum[2], sum[3]);
+        } else if constexpr (KIND == K_RESID) {
+            float4* xr = reinterpret_cast<float4*>(p.x_resid + (size_t)b * p.ldr + r0);
+            const float4 o = *xr;
+            const float4 v = make_float4(o.x + sum[0], o.y + sum[1], o.z + sum[2], o.w + sum[3]);
+            *xr = v;
+            if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(b, r0)] = v;
+        } else if constexpr (KIND == K_SWIGLU) {
+            // rows (w1 u, w3 u, w1 u+1, w3 u+1), u = r0 / 2: hb = silu(w1 x) (w3 x)
+            // ("run.c 逐行解讀" §4 step 2h)
+            const float a0 = sum[0], a1 = sum[2];
+            const float h0 = a0 * (1.0f / (1.0f + expf(-a0))) * sum[1];
+            const float h1 = a1 * (1.0f / (1.0f + expf(-a1))) * sum[3];
+            const int u = r0 >> 1;  // even: the pair (u, u + 1) is half of a tiled float4
+            *reinterpret_cast<float2*>(p.out_t + 4 * tiled_slot(b, u & ~3) + (u & 3)) = make_float2(h0, h1);
+        } else if constexpr (KIND == K_QKV) {
+            // RoPE at the sequence's own position on q and k rows (pairs
+            // (r0, r0+1) and (r0+2, r0+3)), k and v into its cache row
+            // ("run.c 逐行解讀" §4 steps 2b-2d)
+            const int pos = p.row_state[b].pos;
+            const size_t seq = (size_t)b * p.seq_stride;
+            float v[4] = {sum[0], sum[1], sum[2], sum[3]};
+            if (r0 < p.seg2) {
+                const bool is_q = r0 < p.seg1;
+                const int local = is_q ? r0 : r0 - p.seg1;
+                const int hs = p.head_size;
+#pragma unroll
+                for (int h = 0; h < 4; h += 2) {
+                    const float2 cs = p.rope[(size_t)pos * (size_t)(hs >> 1) + (((local + h) % hs) >> 1)];
+                    const float a = v[h], bb = v[h + 1];
+                    v[h] = a * cs.x - bb * cs.y;
+                    v[h + 1] = a * cs.y + bb * cs.x;
+                }
+                const float4 o = make_float4(v[0], v[1], v[2], v[3]);
+                if (is_q)
+                    *reinterpret_cast<float4*>(p.out + (size_t)b * p.ldo + r0) = o;
+                else
+                    *reinterpret_cast<float4*>(p.kc + seq + (size_t)pos * p.kv_stride + local) = o;
+            } else {
+                *reinterpret_cast<float4*>(p.vc + seq + (size_t)pos * p.kv_stride + (r0 - p.seg2)) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
 constexpr int kStreamThreads = 256, kStreamU = 16;
 
 __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const float4* __restrict__ src, long long n4,
@@ -1035,11 +1201,15 @@ __global__ void set_control_kernel(GenControl* dst, GenControl c) { *dst = c; }
 // x[b] = E[state[b].token]
 __global__ __launch_bounds__(256) void embed_state_kernel(const float* __restrict__ emb,
                                                           const StepState* __restrict__ st, int dim,
-                                                          float* __restrict__ x) {
+                                                          float* __restrict__ x, float* __restrict__ xt) {
     const int b = blockIdx.x;
     const float4* src = reinterpret_cast<const float4*>(emb + (size_t)st[b].token * dim);
     float4* dst = reinterpret_cast<float4*>(x + (size_t)b * dim);
-    for (int i = threadIdx.x; i < dim / 4; i += 256) dst[i] = src[i];
+    for (int i = threadIdx.x; i < dim / 4; i += 256) {
+        const float4 v = src[i];
+        dst[i] = v;
+        if (xt) reinterpret_cast<float4*>(xt)[tiled_slot(b, 4 * i)] = v;
+    }
 }
 
 // The greedy choice of every row of the batch's logits (one block per row, the
@@ -2108,6 +2278,79 @@ hipError_t qkv_attention_launch(const GemvPlan& plan, const GemvParams& p0, hipS
     return hipGetLastError();
 }
 
+hipError_t tile_weights_launch(int kind, const float* w0, const float* w1, const float* w2, int seg1, int seg2,
+                               const float* gain, int rows, int k, float* dst, hipStream_t s) {
+    if (rows <= 0 || k <= 0 || rows % 16 || k % 16 || !w0 || !dst) return hipErrorInvalidValue;
+    if ((kind == K_QKV && (!w1 || !w2)) || (kind == K_SWIGLU && !w1)) return hipErrorInvalidValue;
+    const size_t n4 = (size_t)rows * (size_t)k / 4;
+    const size_t blocks = (n4 + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    hipLaunchKernelGGL(tile_weights_kernel, dim3(grid), dim3(256), 0, s, kind, w0, w1, w2, seg1, seg2, gain, rows, k,
+                       reinterpret_cast<float4*>(dst));
+    return hipGetLastError();
+}
+
+// Tiled product shapes (waves, row tiles per block, steps of loads in flight),
+// chosen on whole 7B-shaped decode steps of 8 and 16 sequences: 8 waves of two
+// row tiles for 8192 rows or more, 8 waves of one row tile below.  Within 1%:
+// 4 waves of two tiles, 16 waves of one tile below 8192 rows, 2 steps in
+// flight instead of 4; 2-7% slower: 8 x 1 x 8 or 4 x 4 x 2 for the wide
+// products, 4 x 1 x 8 or 8 x 2 x 4 for the narrow ones.
+#ifndef LD_TILED_WIDE
+#define LD_TILED_WIDE 8, 2, 4
+#endif
+#ifndef LD_TILED_NARROW
+#define LD_TILED_NARROW 8, 1, 4
+#endif
+struct TiledShape {
+    int nw, rt, d;
+};
+constexpr TiledShape kTiledWide{LD_TILED_WIDE}, kTiledNarrow{LD_TILED_NARROW};
+
+template <int KIND, int XT>
+void tiled_dispatch(const TiledParams& p, hipStream_t s) {
+    constexpr TiledShape W = kTiledWide, N = kTiledNarrow;
+    if (p.rows >= 8192 && (p.rows / 16) % W.rt == 0)
+        hipLaunchKernelGGL((tiled_kernel<W.nw, W.rt, W.d, KIND, XT>), dim3(p.rows / 16 / W.rt), dim3(W.nw * 64), 0, s,
+                           p);
+    else if ((p.rows / 16) % N.rt == 0)
+        hipLaunchKernelGGL((tiled_kernel<N.nw, N.rt, N.d, KIND, XT>), dim3(p.rows / 16 / N.rt), dim3(N.nw * 64), 0, s,
+                           p);
+    else
+        hipLaunchKernelGGL((tiled_kernel<N.nw, 1, N.d, KIND, XT>), dim3(p.rows / 16), dim3(N.nw * 64), 0, s, p);
+}
+
+hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s) {
+    if (!p.w || !p.x || p.nb < 1 || p.nb > kTiledBatch || p.k <= 0 || p.k % 16 || p.rows <= 0 || p.rows % 16)
+        return hipErrorInvalidValue;
+    if (!p.x_tiled && (p.ldx < p.k || p.ldx % 4)) return hipErrorInvalidValue;
+    switch (kind) {
+        case K_PLAIN:
+            if (!p.out || p.ldo % 4) return hipErrorInvalidValue;
+            break;
+        case K_RESID:
+            if (!p.x_resid || p.ldr % 4) return hipErrorInvalidValue;
+            break;
+        case K_SWIGLU:
+            if (!p.out_t) return hipErrorInvalidValue;
+            break;
+        case K_QKV:
+            if (!p.out || !p.kc || !p.vc || !p.rope || !p.row_state || p.head_size % 4 || p.seg1 % 4 || p.seg2 % 4 ||
+                p.ldo % 4 || p.kv_stride % 4 || p.seq_stride % 4)
+                return hipErrorInvalidValue;
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    const bool xt = p.x_tiled != 0;
+    switch (kind) {
+        case K_PLAIN: xt ? tiled_dispatch<K_PLAIN, 1>(p, s) : tiled_dispatch<K_PLAIN, 0>(p, s); break;
+        case K_RESID: xt ? tiled_dispatch<K_RESID, 1>(p, s) : tiled_dispatch<K_RESID, 0>(p, s); break;
+        case K_SWIGLU: xt ? tiled_dispatch<K_SWIGLU, 1>(p, s) : tiled_dispatch<K_SWIGLU, 0>(p, s); break;
+        case K_QKV: xt ? tiled_dispatch<K_QKV, 1>(p, s) : tiled_dispatch<K_QKV, 0>(p, s); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     if (plan.kind == K_QKV_ATT) return qkv_attention_launch(plan, p0, s, start, stop);
     const int t = template_for(plan);
@@ -2293,8 +2536,10 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s, hipEvent_t s
     return hipGetLastError();
 }
 
-hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s) {
-    hipLaunchKernelGGL(embed_state_kernel, dim3(batch), dim3(256), 0, s, emb, st, dim, x);
+hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s,
+                              float* xt) {
+    if (xt && (batch > kTiledBatch || dim % 16)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(embed_state_kernel, dim3(batch), dim3(256), 0, s, emb, st, dim, x, xt);
     return hipGetLastError();
 }
 

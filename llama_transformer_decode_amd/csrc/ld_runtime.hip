@@ -204,6 +204,13 @@ struct ld_model {
     GemvPlan bpq{}, bpwo{}, bpffn{}, bpw2{}, bpcls{};  // batches of up to kGemvBatch
     bool bgemv = false;                                  //   (when every shape but the down projection has one)
     bool bgemv_w2 = false;                               //   the down projection has one too
+    // batches of kGemvBatch+1 .. kTiledBatch: the tiled matrix-core products
+    // (max_batch > kGemvBatch and every dimension a multiple of 16): the
+    // weights again in the tiled layout with the RMSNorm gains folded in, and
+    // the batch's residual and hidden vectors in the tiled layout
+    bool tiled = false;
+    float *t_qkv = nullptr, *t_wo = nullptr, *t_ffn = nullptr, *t_w2 = nullptr, *t_cls = nullptr;
+    float *bxt = nullptr, *bhbt = nullptr;
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
     hipGraph_t graph = nullptr;
@@ -733,12 +740,83 @@ int launch_batch_step_gemv(ld_model* m, int n) {
     return LD_OK;
 }
 
+// A decode step of kGemvBatch+1 .. kTiledBatch sequences with the tiled
+// matrix-core products: the single step's launches (each weight streamed once
+// for the batch, the RMSNorms fused), residual and hidden vectors handed on in
+// the tiled layout; attention as for the other batch paths.
+int launch_batch_step_tiled(ld_model* m, int n) {
+    const ld_config& c = m->cfg;
+    const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
+    const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
+    hipStream_t s = m->stream;
+    auto base = [&](const float* w, const float* x, int tiled_x, int k, int rows, int norm) {
+        TiledParams p{};
+        p.w = w;
+        p.x = x;
+        p.x_tiled = tiled_x;
+        p.ldx = k;
+        p.k = k;
+        p.rows = rows;
+        p.nb = n;
+        p.norm = norm;
+        p.eps = m->opt.norm_eps;
+        return p;
+    };
+    HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s, m->bxt));
+    for (int l = 0; l < c.n_layers; ++l) {
+        {
+            TiledParams p = base(m->t_qkv + (size_t)l * (d + 2 * kv) * d, m->bxt, 1, c.dim, c.dim + 2 * m->kv_dim, 1);
+            p.out = m->bq;
+            p.ldo = c.dim;
+            p.seg1 = c.dim;
+            p.seg2 = c.dim + m->kv_dim;
+            p.kc = m->kc + (size_t)l * cache_layer;
+            p.vc = m->vc + (size_t)l * cache_layer;
+            p.kv_stride = m->kv_dim;
+            p.head_size = m->hs;
+            p.rope = m->rope;
+            p.row_state = m->bstate;
+            p.seq_stride = seq_stride;
+            HIP_TRY(tiled_launch(K_QKV, p, s));
+        }
+        HIP_TRY(launch_batch_attention(m, n, l));
+        {
+            TiledParams p = base(m->t_wo + (size_t)l * d * d, m->batt, 0, c.dim, c.dim, 0);
+            p.x_resid = m->bx;
+            p.ldr = c.dim;
+            p.out_t = m->bxt;
+            HIP_TRY(tiled_launch(K_RESID, p, s));
+        }
+        {
+            TiledParams p = base(m->t_ffn + (size_t)l * 2 * h * d, m->bxt, 1, c.dim, 2 * c.hidden_dim, 1);
+            p.out_t = m->bhbt;
+            HIP_TRY(tiled_launch(K_SWIGLU, p, s));
+        }
+        {
+            TiledParams p = base(m->t_w2 + (size_t)l * d * h, m->bhbt, 1, c.hidden_dim, c.dim, 0);
+            p.x_resid = m->bx;
+            p.ldr = c.dim;
+            p.out_t = m->bxt;
+            HIP_TRY(tiled_launch(K_RESID, p, s));
+        }
+    }
+    {
+        TiledParams p = base(m->t_cls, m->bxt, 1, c.dim, c.vocab_size, 1);
+        p.out = m->blogits;
+        p.ldo = c.vocab_size;
+        HIP_TRY(tiled_launch(K_PLAIN, p, s));
+    }
+    HIP_TRY(argmax_rows_launch(m->blogits, n, c.vocab_size, m->bstate, m->btokens, c.seq_len, s));
+    return LD_OK;
+}
+
 // One decode step of sequences 0..n-1 of the batch, each reading (token, pos)
 // from m->bstate[b]: the single step's sequence of operations with the weight
 // matrices as matrix-core products of n rows (each RMSNorm fused into the
 // product it feeds), so every weight is read once for the whole batch.
 int launch_batch_step(ld_model* m, int n) {
     if (n <= kGemvBatch && m->bgemv) return launch_batch_step_gemv(m, n);
+    if (n <= kTiledBatch && m->tiled) return launch_batch_step_tiled(m, n);
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
     const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
@@ -1040,6 +1118,40 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
             // a hidden width beyond the batch kernel's shapes (the 70B layer's
             // 28672) takes the split-K product for the down projection alone
             m->bgemv_w2 = gemv_plan_batch(K_RESID, cfg->dim, cfg->hidden_dim, &m->bpw2) == hipSuccess;
+            // the tiled copies of the weights, for batches of kGemvBatch+1 .. kTiledBatch
+            const bool t16 = cfg->dim % 16 == 0 && cfg->hidden_dim % 16 == 0 && m->kv_dim % 16 == 0 &&
+                             cfg->vocab_size % 16 == 0 && m->hs % 4 == 0;
+            if (m->max_batch > kGemvBatch && t16) {
+                const size_t qkv = (d + 2 * kv) * d, ffn = 2 * h * d;
+                if ((rc = dalloc(m, &m->t_qkv, L * qkv)) || (rc = dalloc(m, &m->t_wo, L * d * d)) ||
+                    (rc = dalloc(m, &m->t_ffn, L * ffn)) || (rc = dalloc(m, &m->t_w2, L * d * h)) ||
+                    (rc = dalloc(m, &m->t_cls, V * d)) || (rc = dalloc(m, &m->bxt, (size_t)kTiledBatch * d)) ||
+                    (rc = dalloc(m, &m->bhbt, (size_t)kTiledBatch * h)))
+                    break;
+                for (size_t l = 0; l < L && e == hipSuccess; ++l) {
+                    e = tile_weights_launch(K_QKV, m->wq + l * d * d, m->wk + l * kv * d, m->wv + l * kv * d,
+                                            cfg->dim, cfg->dim + m->kv_dim, m->rms_att + l * d,
+                                            cfg->dim + 2 * m->kv_dim, cfg->dim, m->t_qkv + l * qkv, m->stream);
+                    if (e == hipSuccess)
+                        e = tile_weights_launch(K_PLAIN, m->wo + l * d * d, nullptr, nullptr, 0, 0, nullptr, cfg->dim,
+                                                cfg->dim, m->t_wo + l * d * d, m->stream);
+                    if (e == hipSuccess)
+                        e = tile_weights_launch(K_SWIGLU, m->w1 + l * h * d, m->w3 + l * h * d, nullptr, 0, 0,
+                                                m->rms_ffn + l * d, 2 * cfg->hidden_dim, cfg->dim, m->t_ffn + l * ffn,
+                                                m->stream);
+                    if (e == hipSuccess)
+                        e = tile_weights_launch(K_PLAIN, m->w2 + l * d * h, nullptr, nullptr, 0, 0, nullptr, cfg->dim,
+                                                cfg->hidden_dim, m->t_w2 + l * d * h, m->stream);
+                }
+                if (e == hipSuccess)
+                    e = tile_weights_launch(K_PLAIN, m->wcls, nullptr, nullptr, 0, 0, m->rms_final, cfg->vocab_size,
+                                            cfg->dim, m->t_cls, m->stream);
+                if (e == hipSuccess) e = hipMemsetAsync(m->bxt, 0, sizeof(float) * kTiledBatch * d, m->stream);
+                if (e == hipSuccess) e = hipMemsetAsync(m->bhbt, 0, sizeof(float) * kTiledBatch * h, m->stream);
+                if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
+                if (e != hipSuccess) { rc = fail_hip(e, "tiled weights"); break; }
+                m->tiled = true;
+            }
             e = hipHostMalloc((void**)&m->h_bstate, sizeof(StepState) * B, hipHostMallocDefault);
             if (e == hipSuccess)
                 e = hipHostMalloc((void**)&m->h_btokens, sizeof(int32_t) * B * cfg->seq_len, hipHostMallocDefault);

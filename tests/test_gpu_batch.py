@@ -8,7 +8,9 @@ sequences start from seeded cache prefixes of different lengths (installed in
 the GPU caches and in the oracle's), so one batched step mixes positions; the
 appended cache rows must match the oracle's, and no other sequence's rows may
 change.  Greedy generation in lockstep must reproduce each sequence's oracle
-tokens up to its first tie.
+tokens up to its first tie.  Batches of up to 4 sequences take the batch
+GEMV kernels, 5 to 16 the tiled matrix-core products, more the split-K
+matrix-core products.
 """
 import numpy as np
 import pytest
@@ -64,7 +66,11 @@ def install(m, cfg, caches):
 
 @pytest.mark.parametrize("graph", [True, False])
 @pytest.mark.parametrize("name,lengths", [("tiny", [0, 5, 17, 40]), ("tiny", [60, 0, 59]),
-                                          ("stories15m", [3, 0, 100, 31, 64]), ("gqa_small", [200, 7, 0, 508])])
+                                          ("stories15m", [3, 0, 100, 31, 64]), ("gqa_small", [200, 7, 0, 508]),
+                                          # 5..16 sequences: the tiled matrix-core products
+                                          ("tiny", [0, 1, 2, 3, 4, 5, 6, 7, 20, 30, 40, 59]),
+                                          ("gqa_small", [0, 9, 18, 27, 36, 45, 54, 63, 100, 200, 300, 400, 450, 480,
+                                                         500, 507])])
 def test_batch_steps_at_mixed_positions(name, lengths, graph):
     cfg, blob, w = blob_of(name)
     B = len(lengths)

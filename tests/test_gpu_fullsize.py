@@ -148,15 +148,15 @@ def test_long_prefill_equals_token_by_token_decode(big):
         assert np.max(np.abs(g - r)) <= 1e-4 * np.max(np.abs(r))
 
 
-@pytest.mark.parametrize("case", [0, 1])
+@pytest.mark.parametrize("case", [0, 1, 2])
 def test_batch_step_at_full_size(big, case):
     # one batched step of several sequences at different installed prefixes, each row against the oracle;
-    # 7B-shaped: 4 sequences (the batch GEMV kernels) and 6 (the split-K matrix-core products);
+    # 7B-shaped: 4 sequences (the batch GEMV kernels), 6 and 5 (the tiled matrix-core products);
     # 70B-layer: 2 and 3 sequences (the batch GEMV kernels, with the split-K product for the
-    # 28672-wide down projection, which has no batch GEMV shape)
+    # 28672-wide down projection, which has no batch GEMV shape) and 5 (the tiled products)
     cfg, blob, w = big
-    lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300]],
-               "llama70b_8l": [[4000, 1500], [100, 4095, 2048]]}[cfg.name][case]
+    lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300], [1, 0, 63, 64, 65]],
+               "llama70b_8l": [[4000, 1500], [100, 4095, 2048], [0, 3000, 4095, 17, 1024]]}[cfg.name][case]
     B = len(lengths)
     caches = [(_prefix(cfg, p, 900 + 50 * b) if p else oracle.KVCache(cfg)) for b, p in enumerate(lengths)]
     toks = synth.prefill_tokens(cfg, B)
