@@ -130,6 +130,7 @@ struct AttnParams {
     int waves;             // waves per block: attn_waves(...) of the model (0 = 4)
     int fuse;              // 1: the last split block of a kv group merges it (set by the launcher)
     int stage_sh;          // q/k/v from a hand-off stage (the fused q/k/v kernel): its slot stride
+    float* out_t;          // a decode batch of <= kTiledBatch: the outputs also in the tiled layout (or NULL)
     // a decode batch (grid.z = batch; 0 or 1: one sequence): sequence b's q,
     // out and state are b * q_stride floats / b states further, its caches
     // b * seq_stride floats, its split partials b * (n_heads * nsplit) pairs

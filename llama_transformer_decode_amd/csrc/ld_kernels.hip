@@ -1046,6 +1046,15 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     const float4* wt = reinterpret_cast<const float4*>(p.w) + (size_t)rt0 * KT * 64 + lane;
     const float* xbase = XT ? p.x + 4 * lane : p.x + (size_t)min(c, p.nb - 1) * p.ldx + 4 * q;
     const int nsteps = (KT + NW - 1) / NW;  // this wave: tiles wave, wave + NW, ... below KT
+    // the residual rows this thread adds to in the epilogue (entry threadIdx.x
+    // of the block's RT x 64; NW * 64 >= RT * 64 threads) are loaded now, so
+    // the epilogue does not wait on them
+    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (KIND == K_RESID) {
+        static_assert(NW >= RT, "one epilogue entry per thread");
+        const int e = threadIdx.x, b = e & 15, r0 = 16 * (rt0 + (e >> 6)) + 4 * ((e & 63) >> 4);
+        if (e < RT * 64 && b < p.nb && r0 < p.rows) res = *reinterpret_cast<const float4*>(p.x_resid + (size_t)b * p.ldr + r0);
+    }
 
     v4 acc[RT];
 #pragma unroll
@@ -1105,10 +1114,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
         if constexpr (KIND == K_PLAIN) {
             *reinterpret_cast<float4*>(p.out + (size_t)b * p.ldo + r0) = make_float4(sum[0], sum[1], sum[2], sum[3]);
         } else if constexpr (KIND == K_RESID) {
-            float4* xr = reinterpret_cast<float4*>(p.x_resid + (size_t)b * p.ldr + r0);
-            const float4 o = *xr;
-            const float4 v = make_float4(o.x + sum[0], o.y + sum[1], o.z + sum[2], o.w + sum[3]);
-            *xr = v;
+            const float4 v = make_float4(res.x + sum[0], res.y + sum[1], res.z + sum[2], res.w + sum[3]);
+            *reinterpret_cast<float4*>(p.x_resid + (size_t)b * p.ldr + r0) = v;
             if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(b, r0)] = v;
         } else if constexpr (KIND == K_SWIGLU) {
             // rows (w1 u, w3 u, w1 u+1, w3 u+1), u = r0 / 2: hb = silu(w1 x) (w3 x)
@@ -1313,6 +1320,14 @@ __device__ __forceinline__ AttnParams seq_view(const AttnParams& p) {
     return v;
 }
 
+// Output float4 c of query head h; for a decode batch whose outputs go on to
+// the tiled products (out_t), also the tiled copy of sequence blockIdx.z.
+template <int HS>
+__device__ __forceinline__ void put_out(const AttnParams& p, int h, int c, float4 v) {
+    reinterpret_cast<float4*>(p.out)[(size_t)h * (HS / 4) + c] = v;
+    if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(blockIdx.z, h * HS + 4 * c)] = v;
+}
+
 __device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
     return make_float4(fmaf(a, v.x, acc.x), fmaf(a, v.y, acc.y), fmaf(a, v.z, acc.z), fmaf(a, v.w, acc.w));
 }
@@ -1382,7 +1397,7 @@ __device__ void merge_group(const AttnParams& p, int h_lo, int G, int nact) {
         }
         if (o < slots && (kgn == 1 || tid < slots)) {
             const float il = 1.0f / l;
-            reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + c] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+            put_out<HS>(p, h, c, make_float4(a.x * il, a.y * il, a.z * il, a.w * il));
         }
     }
 }
@@ -1554,8 +1569,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
             }
             if (nact == 1) {  // one split holds every key: this is the output
                 const float il = 1.0f / l_s[tid / H4];
-                reinterpret_cast<float4*>(p.out)[(size_t)(h_lo + tid / H4) * H4 + tid % H4] =
-                    make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+                put_out<HS>(p, h_lo + tid / H4, tid % H4, make_float4(a.x * il, a.y * il, a.z * il, a.w * il));
             } else {
                 store_coherent(part4 + ((size_t)(h_lo + tid / H4) * p.nsplit + s) * H4 + tid % H4, a);
             }
@@ -1571,8 +1585,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams pb) {
             if (o < slots) {
                 const float il = 1.0f / l_s[o / H4];
                 const float4 a = acc[j];
-                reinterpret_cast<float4*>(p.out)[(size_t)(h_lo + o / H4) * H4 + o % H4] =
-                    make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+                put_out<HS>(p, h_lo + o / H4, o % H4, make_float4(a.x * il, a.y * il, a.z * il, a.w * il));
             }
         }
         return;
@@ -1799,7 +1812,7 @@ __device__ void attend_reg(const AttnParams& p, int g, int s) {
         const int h = h_lo + hh;
         if (nact == 1) {  // one split holds every key: this is the output
             const float il = 1.0f / L;
-            reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + col] = make_float4(A.x * il, A.y * il, A.z * il, A.w * il);
+            put_out<HS>(p, h, col, make_float4(A.x * il, A.y * il, A.z * il, A.w * il));
         } else {
             store_coherent(reinterpret_cast<float4*>(p.part_acc) + ((size_t)h * p.nsplit + s) * H4 + col, A);
             if (col == 0) store_coherent(p.part_ml + (size_t)h * p.nsplit + s, make_float2(M_s[hh], L));
@@ -1932,7 +1945,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(AttnParams pb)
             a = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
         }
         const float il = 1.0f / L_s;
-        reinterpret_cast<float4*>(p.out)[(size_t)h * H4 + tid] = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+        put_out<HS>(p, h, tid, make_float4(a.x * il, a.y * il, a.z * il, a.w * il));
     }
 }
 
@@ -2290,34 +2303,62 @@ hipError_t tile_weights_launch(int kind, const float* w0, const float* w1, const
     return hipGetLastError();
 }
 
-// Tiled product shapes (waves, row tiles per block, steps of loads in flight),
-// chosen on whole 7B-shaped decode steps of 8 and 16 sequences: 8 waves of two
-// row tiles for 8192 rows or more, 8 waves of one row tile below.  Within 1%:
-// 4 waves of two tiles, 16 waves of one tile below 8192 rows, 2 steps in
-// flight instead of 4; 2-7% slower: 8 x 1 x 8 or 4 x 4 x 2 for the wide
-// products, 4 x 1 x 8 or 8 x 2 x 4 for the narrow ones.
-#ifndef LD_TILED_WIDE
-#define LD_TILED_WIDE 8, 2, 4
+// Tiled product shapes: 8 waves (512 threads), 4 steps of loads in flight,
+// 1 to 4 row tiles per block (each activation load serves that many tiles).
+// Every block is resident at once, so the CU with the most blocks sets the
+// time: of the row-tile counts that leave at least one block per CU, the one
+// whose busiest CU is fullest is taken, the larger on a tie.  7B shapes: q/k/v
+// 256 blocks of three tiles (384 blocks of two left half the CUs with one:
+// 43.4 against 40.8 us with 768 blocks of one, and three tiles gained another
+// 1.5% of the step), w1/w3 688 of two, wo and w2 256 of one, the classifier
+// 500 of four.  Chosen on whole decode steps of 5, 8 and 16 sequences; within
+// 1%: 4 waves, 16 waves for the narrow products, 2 steps in flight; 2-7%
+// slower: 8 steps, 4 waves of one tile with 8 steps.
+constexpr int kTiledWaves = 8, kTiledSteps = 4;
+
+int cu_count() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            cus = c;
+        else
+            return 256;
+    }
+    return cus;
+}
+
+// fraction of the busiest CU's slots the blocks fill, in thousandths
+int tiled_balance(int blocks, int cus) {
+    const int per = (blocks + cus - 1) / cus;
+    return (int)(1000LL * blocks / ((long long)per * cus));
+}
+
+#ifndef LD_TILED_RT_MAX
+#define LD_TILED_RT_MAX 4
 #endif
-#ifndef LD_TILED_NARROW
-#define LD_TILED_NARROW 8, 1, 4
-#endif
-struct TiledShape {
-    int nw, rt, d;
-};
-constexpr TiledShape kTiledWide{LD_TILED_WIDE}, kTiledNarrow{LD_TILED_NARROW};
+template <int KIND, int XT, int RT>
+void tiled_go(const TiledParams& p, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((tiled_kernel<kTiledWaves, RT, kTiledSteps, KIND, XT>), dim3(blocks), dim3(kTiledWaves * 64), 0,
+                       s, p);
+}
 
 template <int KIND, int XT>
 void tiled_dispatch(const TiledParams& p, hipStream_t s) {
-    constexpr TiledShape W = kTiledWide, N = kTiledNarrow;
-    if (p.rows >= 8192 && (p.rows / 16) % W.rt == 0)
-        hipLaunchKernelGGL((tiled_kernel<W.nw, W.rt, W.d, KIND, XT>), dim3(p.rows / 16 / W.rt), dim3(W.nw * 64), 0, s,
-                           p);
-    else if ((p.rows / 16) % N.rt == 0)
-        hipLaunchKernelGGL((tiled_kernel<N.nw, N.rt, N.d, KIND, XT>), dim3(p.rows / 16 / N.rt), dim3(N.nw * 64), 0, s,
-                           p);
-    else
-        hipLaunchKernelGGL((tiled_kernel<N.nw, 1, N.d, KIND, XT>), dim3(p.rows / 16), dim3(N.nw * 64), 0, s, p);
+    const int tiles = p.rows / 16, cus = cu_count();
+    int rt = 1, best = tiled_balance(tiles, cus);
+    for (int r = 2; r <= LD_TILED_RT_MAX; ++r)
+        if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) >= best) {
+            rt = r;
+            best = tiled_balance(tiles / r, cus);
+        }
+    switch (rt) {
+        case 4: tiled_go<KIND, XT, 4>(p, tiles / 4, s); break;
+        case 3: tiled_go<KIND, XT, 3>(p, tiles / 3, s); break;
+        case 2: tiled_go<KIND, XT, 2>(p, tiles / 2, s); break;
+        default: tiled_go<KIND, XT, 1>(p, tiles, s); break;
+    }
 }
 
 hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s) {

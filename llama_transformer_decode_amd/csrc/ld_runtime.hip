@@ -210,7 +210,7 @@ struct ld_model {
     // the batch's residual and hidden vectors in the tiled layout
     bool tiled = false;
     float *t_qkv = nullptr, *t_wo = nullptr, *t_ffn = nullptr, *t_w2 = nullptr, *t_cls = nullptr;
-    float *bxt = nullptr, *bhbt = nullptr;
+    float *bxt = nullptr, *bhbt = nullptr, *batt_t = nullptr;
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
     hipGraph_t graph = nullptr;
@@ -619,8 +619,9 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
 }
 
 // Attention of layer l for sequences 0..n-1 of the batch (q rows in bq, each
-// sequence's own caches and position).
-hipError_t launch_batch_attention(ld_model* m, int n, int l) {
+// sequence's own caches and position); out_t: the outputs also in the tiled
+// layout there (the tiled products' batches).
+hipError_t launch_batch_attention(ld_model* m, int n, int l, float* out_t = nullptr) {
     const ld_config& c = m->cfg;
     const size_t cache_layer = (size_t)c.seq_len * m->kv_dim;
     AttnParams a{};
@@ -640,6 +641,7 @@ hipError_t launch_batch_attention(ld_model* m, int n, int l) {
     a.batch = n;
     a.q_stride = c.dim;
     a.seq_stride = (size_t)c.n_layers * cache_layer;
+    a.out_t = out_t;
     return attn_launch(m->hs, a, m->stream);
 }
 
@@ -742,8 +744,8 @@ int launch_batch_step_gemv(ld_model* m, int n) {
 
 // A decode step of kGemvBatch+1 .. kTiledBatch sequences with the tiled
 // matrix-core products: the single step's launches (each weight streamed once
-// for the batch, the RMSNorms fused), residual and hidden vectors handed on in
-// the tiled layout; attention as for the other batch paths.
+// for the batch, the RMSNorms fused), residual, attention and hidden vectors
+// handed on in the tiled layout.
 int launch_batch_step_tiled(ld_model* m, int n) {
     const ld_config& c = m->cfg;
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
@@ -779,9 +781,9 @@ int launch_batch_step_tiled(ld_model* m, int n) {
             p.seq_stride = seq_stride;
             HIP_TRY(tiled_launch(K_QKV, p, s));
         }
-        HIP_TRY(launch_batch_attention(m, n, l));
+        HIP_TRY(launch_batch_attention(m, n, l, m->batt_t));
         {
-            TiledParams p = base(m->t_wo + (size_t)l * d * d, m->batt, 0, c.dim, c.dim, 0);
+            TiledParams p = base(m->t_wo + (size_t)l * d * d, m->batt_t, 1, c.dim, c.dim, 0);
             p.x_resid = m->bx;
             p.ldr = c.dim;
             p.out_t = m->bxt;
@@ -1126,7 +1128,8 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
                 if ((rc = dalloc(m, &m->t_qkv, L * qkv)) || (rc = dalloc(m, &m->t_wo, L * d * d)) ||
                     (rc = dalloc(m, &m->t_ffn, L * ffn)) || (rc = dalloc(m, &m->t_w2, L * d * h)) ||
                     (rc = dalloc(m, &m->t_cls, V * d)) || (rc = dalloc(m, &m->bxt, (size_t)kTiledBatch * d)) ||
-                    (rc = dalloc(m, &m->bhbt, (size_t)kTiledBatch * h)))
+                    (rc = dalloc(m, &m->bhbt, (size_t)kTiledBatch * h)) ||
+                    (rc = dalloc(m, &m->batt_t, (size_t)kTiledBatch * d)))
                     break;
                 for (size_t l = 0; l < L && e == hipSuccess; ++l) {
                     e = tile_weights_launch(K_QKV, m->wq + l * d * d, m->wk + l * kv * d, m->wv + l * kv * d,
@@ -1148,6 +1151,7 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
                                             cfg->dim, m->t_cls, m->stream);
                 if (e == hipSuccess) e = hipMemsetAsync(m->bxt, 0, sizeof(float) * kTiledBatch * d, m->stream);
                 if (e == hipSuccess) e = hipMemsetAsync(m->bhbt, 0, sizeof(float) * kTiledBatch * h, m->stream);
+                if (e == hipSuccess) e = hipMemsetAsync(m->batt_t, 0, sizeof(float) * kTiledBatch * d, m->stream);
                 if (e == hipSuccess) e = hipStreamSynchronize(m->stream);
                 if (e != hipSuccess) { rc = fail_hip(e, "tiled weights"); break; }
                 m->tiled = true;
