@@ -146,15 +146,13 @@ struct AttnParams {
 // (both multiples of 16) form 16 x 16 tiles; tile (rt, kt) is 64 float4 at
 // float4 offset (rt * K/16 + kt) * 64, float4 l holding row 16 rt + l % 16 at
 // k = 16 kt + 4 (l / 16) + 0..3, times the gain of the product's RMSNorm at k.
-// Tiled activations: float4 (kt * 64 + l) = x[l % 16][16 kt + 4 (l / 16) + 0..3]
-// for sequences 0..15.
-constexpr int kTiledBatch = 16;
+// Tiled activations (vectors of n floats, planes of 16 sequences): float4
+// ((plane * n/16 + kt) * 64 + l) = x[16 plane + l % 16][16 kt + 4 (l / 16) + 0..3].
+constexpr int kTiledBatch = 32;
 
 struct TiledParams {
     const float* w;        // tiled weights (gain folded in)
-    const float* x;        // input: tiled (x_tiled) or row-major with stride ldx
-    int x_tiled;
-    int ldx;
+    const float* x;        // input, tiled
     int k;                 // input length
     int rows;              // output rows (K_SWIGLU: 2 x hidden, w1 and w3 rows interleaved)
     int nb;                // sequences, 1..kTiledBatch
@@ -164,7 +162,7 @@ struct TiledParams {
     int ldo;
     float* x_resid;        // K_RESID: x_resid[b * ldr + r] += C
     int ldr;
-    float* out_t;          // K_RESID: the new residual, K_SWIGLU: hb, tiled (NULL: none)
+    float* out_t;          // K_RESID: the new residual, K_SWIGLU: hb, tiled (K_RESID: may be NULL)
     int seg1, seg2;        // K_QKV as GemvParams
     float* kc;
     float* vc;

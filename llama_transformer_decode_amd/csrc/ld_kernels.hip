@@ -1000,9 +1000,10 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
 // sequence's sum of squares is accumulated from the same activations, so the
 // row scale multiplies the result.
 
-// float4 slot of x[b][k] (k a multiple of 4) in the tiled activations
-__host__ __device__ __forceinline__ size_t tiled_slot(int b, int k) {
-    return (size_t)(k >> 4) * 64 + ((k & 15) >> 2) * 16 + b;
+// float4 slot of x[b][k] (k a multiple of 4) in the tiled activations of
+// vectors of n floats (planes of 16 sequences)
+__host__ __device__ __forceinline__ size_t tiled_slot(int b, int k, int n) {
+    return ((size_t)(b >> 4) * (size_t)(n >> 4) + (size_t)(k >> 4)) * 64 + ((k & 15) >> 2) * 16 + (b & 15);
 }
 
 __device__ __forceinline__ float f4c(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
@@ -1035,39 +1036,49 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
     }
 }
 
-template <int NW, int RT, int D, int KIND, int XT>
+template <int NW, int RT, int D, int KIND, int NP>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     typedef float v4 __attribute__((ext_vector_type(4)));
-    __shared__ v4 red[NW][RT][64];
-    __shared__ float ss_s[NW][16];
+    constexpr int NE = RT * NP;                 // output tiles of the block
+    constexpr int EPT = (NE + NW - 1) / NW;     // epilogue entries per thread
+    __shared__ v4 red[NW][NE][64];
+    __shared__ float ss_s[NW][NP][16];
     const int KT = p.k >> 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, c = lane & 15;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rt0 = blockIdx.x * RT;
     const float4* wt = reinterpret_cast<const float4*>(p.w) + (size_t)rt0 * KT * 64 + lane;
-    const float* xbase = XT ? p.x + 4 * lane : p.x + (size_t)min(c, p.nb - 1) * p.ldx + 4 * q;
+    const float4* xt = reinterpret_cast<const float4*>(p.x) + lane;  // plane jb at + jb * KT * 64
     const int nsteps = (KT + NW - 1) / NW;  // this wave: tiles wave, wave + NW, ... below KT
-    // the residual rows this thread adds to in the epilogue (entry threadIdx.x
-    // of the block's RT x 64; NW * 64 >= RT * 64 threads) are loaded now, so
+    // the residual rows this thread adds to in the epilogue are loaded now, so
     // the epilogue does not wait on them
-    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (KIND == K_RESID) {
-        static_assert(NW >= RT, "one epilogue entry per thread");
-        const int e = threadIdx.x, b = e & 15, r0 = 16 * (rt0 + (e >> 6)) + 4 * ((e & 63) >> 4);
-        if (e < RT * 64 && b < p.nb && r0 < p.rows) res = *reinterpret_cast<const float4*>(p.x_resid + (size_t)b * p.ldr + r0);
+    float4 res[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        res[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (KIND == K_RESID) {
+            const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
+            const int b = 16 * (t % NP) + (l & 15), r0 = 16 * (rt0 + t / NP) + 4 * (l >> 4);
+            if (t < NE && b < p.nb && r0 < p.rows) res[i] = *reinterpret_cast<const float4*>(p.x_resid + (size_t)b * p.ldr + r0);
+        }
     }
 
-    v4 acc[RT];
+    v4 acc[RT][NP];
 #pragma unroll
-    for (int j = 0; j < RT; ++j) acc[j] = v4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-    float4 w[D][RT], xv[D];
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int jb = 0; jb < NP; ++jb) acc[j][jb] = v4{0.f, 0.f, 0.f, 0.f};
+    float ss[NP];
+#pragma unroll
+    for (int jb = 0; jb < NP; ++jb) ss[jb] = 0.f;
+    float4 w[D][RT], xv[D][NP];
     auto load = [&](int kk0) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int kt = min((kk0 + d) * NW + wave, KT - 1);  // past the end: re-read the last tile (not used)
 #pragma unroll
             for (int j = 0; j < RT; ++j) w[d][j] = wt[((size_t)j * KT + kt) * 64];
-            xv[d] = *reinterpret_cast<const float4*>(xbase + (XT ? (size_t)kt * 256 : (size_t)kt * 16));
+#pragma unroll
+            for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
         }
     };
     load(0);
@@ -1075,12 +1086,18 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             if ((kk + d) * NW + wave < KT) {  // wave-uniform
-                if (p.norm) ss = dot4(xv[d], xv[d], ss);
+                if (p.norm) {
+#pragma unroll
+                    for (int jb = 0; jb < NP; ++jb) ss[jb] = dot4(xv[d][jb], xv[d][jb], ss[jb]);
+                }
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int j = 0; j < RT; ++j)
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4c(w[d][j], t), f4c(xv[d], t), acc[j], 0, 0, 0);
+#pragma unroll
+                        for (int jb = 0; jb < NP; ++jb)
+                            acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4c(w[d][j], t), f4c(xv[d][jb], t),
+                                                                              acc[j][jb], 0, 0, 0);
             }
         }
         // keep the next loads after these products: hoisting them would hold
@@ -1090,33 +1107,43 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
         if (kk + D < nsteps) load(kk + D);
     }
 #pragma unroll
-    for (int j = 0; j < RT; ++j) red[wave][j][lane] = acc[j];
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int jb = 0; jb < NP; ++jb) red[wave][j * NP + jb][lane] = acc[j][jb];
     if (p.norm) {  // lanes c, c + 16, c + 32, c + 48 hold sequence c's k in parts
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        if (lane < 16) ss_s[wave][lane] = ss;
+#pragma unroll
+        for (int jb = 0; jb < NP; ++jb) {
+            float v = ss[jb];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (lane < 16) ss_s[wave][jb][lane] = v;
+        }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < RT * 64; e += NW * 64) {
-        const int j = e >> 6, l = e & 63, b = l & 15;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
+        if (t >= NE) break;
+        const int j = t / NP, jb = t % NP, b = 16 * jb + (l & 15);
         if (b >= p.nb) continue;
-        v4 sum = red[0][j][l];
+        v4 sum = red[0][t][l];
 #pragma unroll
-        for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][j][l];
+        for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][t][l];
         if (p.norm) {
-            float t = 0.f;
+            float q2 = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) t += ss_s[w2][b];
-            sum *= 1.0f / sqrtf(t / (float)p.k + p.eps);
+            for (int w2 = 0; w2 < NW; ++w2) q2 += ss_s[w2][jb][l & 15];
+            sum *= 1.0f / sqrtf(q2 / (float)p.k + p.eps);
         }
         const int r0 = 16 * (rt0 + j) + 4 * (l >> 4);  // rows r0 .. r0 + 3 of sequence b
         if (r0 >= p.rows) continue;
         if constexpr (KIND == K_PLAIN) {
             *reinterpret_cast<float4*>(p.out + (size_t)b * p.ldo + r0) = make_float4(sum[0], sum[1], sum[2], sum[3]);
         } else if constexpr (KIND == K_RESID) {
-            const float4 v = make_float4(res.x + sum[0], res.y + sum[1], res.z + sum[2], res.w + sum[3]);
+            const float4 o = res[i];
+            const float4 v = make_float4(o.x + sum[0], o.y + sum[1], o.z + sum[2], o.w + sum[3]);
             *reinterpret_cast<float4*>(p.x_resid + (size_t)b * p.ldr + r0) = v;
-            if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(b, r0)] = v;
+            if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(b, r0, p.rows)] = v;
         } else if constexpr (KIND == K_SWIGLU) {
             // rows (w1 u, w3 u, w1 u+1, w3 u+1), u = r0 / 2: hb = silu(w1 x) (w3 x)
             // ("run.c 逐行解讀" §4 step 2h)
@@ -1124,7 +1151,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
             const float h0 = a0 * (1.0f / (1.0f + expf(-a0))) * sum[1];
             const float h1 = a1 * (1.0f / (1.0f + expf(-a1))) * sum[3];
             const int u = r0 >> 1;  // even: the pair (u, u + 1) is half of a tiled float4
-            *reinterpret_cast<float2*>(p.out_t + 4 * tiled_slot(b, u & ~3) + (u & 3)) = make_float2(h0, h1);
+            *reinterpret_cast<float2*>(p.out_t + 4 * tiled_slot(b, u & ~3, p.rows >> 1) + (u & 3)) = make_float2(h0, h1);
         } else if constexpr (KIND == K_QKV) {
             // RoPE at the sequence's own position on q and k rows (pairs
             // (r0, r0+1) and (r0+2, r0+3)), k and v into its cache row
@@ -1215,7 +1242,7 @@ __global__ __launch_bounds__(256) void embed_state_kernel(const float* __restric
     for (int i = threadIdx.x; i < dim / 4; i += 256) {
         const float4 v = src[i];
         dst[i] = v;
-        if (xt) reinterpret_cast<float4*>(xt)[tiled_slot(b, 4 * i)] = v;
+        if (xt) reinterpret_cast<float4*>(xt)[tiled_slot(b, 4 * i, dim)] = v;
     }
 }
 
@@ -1321,11 +1348,12 @@ __device__ __forceinline__ AttnParams seq_view(const AttnParams& p) {
 }
 
 // Output float4 c of query head h; for a decode batch whose outputs go on to
-// the tiled products (out_t), also the tiled copy of sequence blockIdx.z.
+// the tiled products (out_t), also the tiled copy of sequence blockIdx.z (the
+// vectors are n_heads * HS floats).
 template <int HS>
 __device__ __forceinline__ void put_out(const AttnParams& p, int h, int c, float4 v) {
     reinterpret_cast<float4*>(p.out)[(size_t)h * (HS / 4) + c] = v;
-    if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(blockIdx.z, h * HS + 4 * c)] = v;
+    if (p.out_t) reinterpret_cast<float4*>(p.out_t)[tiled_slot(blockIdx.z, h * HS + 4 * c, p.n_heads * HS)] = v;
 }
 
 __device__ __forceinline__ float4 fma4(float a, float4 v, float4 acc) {
@@ -2335,59 +2363,66 @@ int tiled_balance(int blocks, int cus) {
     return (int)(1000LL * blocks / ((long long)per * cus));
 }
 
-#ifndef LD_TILED_RT_MAX
-#define LD_TILED_RT_MAX 4
-#endif
-template <int KIND, int XT, int RT>
+// Up to 16 sequences (one plane): 8 waves, 4 steps in flight, 1 to 4 row
+// tiles.  17-32 (two planes): 8 waves, 4 steps, 1 or 2 row tiles (registers
+// and LDS hold row tiles x planes partial tiles).  Four planes (33-64
+// sequences, 4 waves, 2 steps) ran at 13.5-13.9 ms per 7B-shaped step against
+// 10.8-11.1 ms with the split-K products, so the tiled path stops at 32: the
+// matrix cores are then about 38% busy, with twice as many activation bytes
+// read from L2 as weight bytes from HBM.
+template <int KIND, int NW, int D, int NP, int RT>
 void tiled_go(const TiledParams& p, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((tiled_kernel<kTiledWaves, RT, kTiledSteps, KIND, XT>), dim3(blocks), dim3(kTiledWaves * 64), 0,
-                       s, p);
+    hipLaunchKernelGGL((tiled_kernel<NW, RT, D, KIND, NP>), dim3(blocks), dim3(NW * 64), 0, s, p);
 }
 
-template <int KIND, int XT>
-void tiled_dispatch(const TiledParams& p, hipStream_t s) {
+template <int KIND, int NW, int D, int NP, int RT_MAX>
+void tiled_shape(const TiledParams& p, hipStream_t s) {
     const int tiles = p.rows / 16, cus = cu_count();
     int rt = 1, best = tiled_balance(tiles, cus);
-    for (int r = 2; r <= LD_TILED_RT_MAX; ++r)
+    for (int r = 2; r <= RT_MAX; ++r)
         if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) >= best) {
             rt = r;
             best = tiled_balance(tiles / r, cus);
         }
     switch (rt) {
-        case 4: tiled_go<KIND, XT, 4>(p, tiles / 4, s); break;
-        case 3: tiled_go<KIND, XT, 3>(p, tiles / 3, s); break;
-        case 2: tiled_go<KIND, XT, 2>(p, tiles / 2, s); break;
-        default: tiled_go<KIND, XT, 1>(p, tiles, s); break;
+        case 4: if constexpr (RT_MAX >= 4) tiled_go<KIND, NW, D, NP, 4>(p, tiles / 4, s); break;
+        case 3: if constexpr (RT_MAX >= 3) tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s); break;
+        case 2: tiled_go<KIND, NW, D, NP, 2>(p, tiles / 2, s); break;
+        default: tiled_go<KIND, NW, D, NP, 1>(p, tiles, s); break;
     }
+}
+
+template <int KIND>
+void tiled_dispatch(const TiledParams& p, hipStream_t s) {
+    if (p.nb <= 16)
+        tiled_shape<KIND, 8, 4, 1, 4>(p, s);
+    else
+        tiled_shape<KIND, 8, 4, 2, 2>(p, s);
 }
 
 hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s) {
     if (!p.w || !p.x || p.nb < 1 || p.nb > kTiledBatch || p.k <= 0 || p.k % 16 || p.rows <= 0 || p.rows % 16)
         return hipErrorInvalidValue;
-    if (!p.x_tiled && (p.ldx < p.k || p.ldx % 4)) return hipErrorInvalidValue;
     switch (kind) {
         case K_PLAIN:
             if (!p.out || p.ldo % 4) return hipErrorInvalidValue;
+            tiled_dispatch<K_PLAIN>(p, s);
             break;
         case K_RESID:
             if (!p.x_resid || p.ldr % 4) return hipErrorInvalidValue;
+            tiled_dispatch<K_RESID>(p, s);
             break;
         case K_SWIGLU:
-            if (!p.out_t) return hipErrorInvalidValue;
+            if (!p.out_t || p.rows % 32) return hipErrorInvalidValue;
+            tiled_dispatch<K_SWIGLU>(p, s);
             break;
         case K_QKV:
             if (!p.out || !p.kc || !p.vc || !p.rope || !p.row_state || p.head_size % 4 || p.seg1 % 4 || p.seg2 % 4 ||
                 p.ldo % 4 || p.kv_stride % 4 || p.seq_stride % 4)
                 return hipErrorInvalidValue;
+            tiled_dispatch<K_QKV>(p, s);
             break;
         default: return hipErrorInvalidValue;
-    }
-    const bool xt = p.x_tiled != 0;
-    switch (kind) {
-        case K_PLAIN: xt ? tiled_dispatch<K_PLAIN, 1>(p, s) : tiled_dispatch<K_PLAIN, 0>(p, s); break;
-        case K_RESID: xt ? tiled_dispatch<K_RESID, 1>(p, s) : tiled_dispatch<K_RESID, 0>(p, s); break;
-        case K_SWIGLU: xt ? tiled_dispatch<K_SWIGLU, 1>(p, s) : tiled_dispatch<K_SWIGLU, 0>(p, s); break;
-        case K_QKV: xt ? tiled_dispatch<K_QKV, 1>(p, s) : tiled_dispatch<K_QKV, 0>(p, s); break;
     }
     return hipGetLastError();
 }
@@ -2579,7 +2614,7 @@ hipError_t attn_launch(int hs, const AttnParams& p0, hipStream_t s, hipEvent_t s
 
 hipError_t embed_state_launch(const float* emb, const StepState* st, int batch, int dim, float* x, hipStream_t s,
                               float* xt) {
-    if (xt && (batch > kTiledBatch || dim % 16)) return hipErrorInvalidValue;
+    if (xt && (batch > kTiledBatch || dim % 16)) return hipErrorInvalidValue;  // (tiled_slot's planes)
     hipLaunchKernelGGL(embed_state_kernel, dim3(batch), dim3(256), 0, s, emb, st, dim, x, xt);
     return hipGetLastError();
 }

@@ -751,12 +751,10 @@ int launch_batch_step_tiled(ld_model* m, int n) {
     const size_t d = c.dim, h = c.hidden_dim, kv = m->kv_dim;
     const size_t cache_layer = (size_t)c.seq_len * kv, seq_stride = (size_t)c.n_layers * cache_layer;
     hipStream_t s = m->stream;
-    auto base = [&](const float* w, const float* x, int tiled_x, int k, int rows, int norm) {
+    auto base = [&](const float* w, const float* x, int k, int rows, int norm) {
         TiledParams p{};
         p.w = w;
         p.x = x;
-        p.x_tiled = tiled_x;
-        p.ldx = k;
         p.k = k;
         p.rows = rows;
         p.nb = n;
@@ -767,7 +765,7 @@ int launch_batch_step_tiled(ld_model* m, int n) {
     HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s, m->bxt));
     for (int l = 0; l < c.n_layers; ++l) {
         {
-            TiledParams p = base(m->t_qkv + (size_t)l * (d + 2 * kv) * d, m->bxt, 1, c.dim, c.dim + 2 * m->kv_dim, 1);
+            TiledParams p = base(m->t_qkv + (size_t)l * (d + 2 * kv) * d, m->bxt, c.dim, c.dim + 2 * m->kv_dim, 1);
             p.out = m->bq;
             p.ldo = c.dim;
             p.seg1 = c.dim;
@@ -783,19 +781,19 @@ int launch_batch_step_tiled(ld_model* m, int n) {
         }
         HIP_TRY(launch_batch_attention(m, n, l, m->batt_t));
         {
-            TiledParams p = base(m->t_wo + (size_t)l * d * d, m->batt_t, 1, c.dim, c.dim, 0);
+            TiledParams p = base(m->t_wo + (size_t)l * d * d, m->batt_t, c.dim, c.dim, 0);
             p.x_resid = m->bx;
             p.ldr = c.dim;
             p.out_t = m->bxt;
             HIP_TRY(tiled_launch(K_RESID, p, s));
         }
         {
-            TiledParams p = base(m->t_ffn + (size_t)l * 2 * h * d, m->bxt, 1, c.dim, 2 * c.hidden_dim, 1);
+            TiledParams p = base(m->t_ffn + (size_t)l * 2 * h * d, m->bxt, c.dim, 2 * c.hidden_dim, 1);
             p.out_t = m->bhbt;
             HIP_TRY(tiled_launch(K_SWIGLU, p, s));
         }
         {
-            TiledParams p = base(m->t_w2 + (size_t)l * d * h, m->bhbt, 1, c.hidden_dim, c.dim, 0);
+            TiledParams p = base(m->t_w2 + (size_t)l * d * h, m->bhbt, c.hidden_dim, c.dim, 0);
             p.x_resid = m->bx;
             p.ldr = c.dim;
             p.out_t = m->bxt;
@@ -803,7 +801,7 @@ int launch_batch_step_tiled(ld_model* m, int n) {
         }
     }
     {
-        TiledParams p = base(m->t_cls, m->bxt, 1, c.dim, c.vocab_size, 1);
+        TiledParams p = base(m->t_cls, m->bxt, c.dim, c.vocab_size, 1);
         p.out = m->blogits;
         p.ldo = c.vocab_size;
         HIP_TRY(tiled_launch(K_PLAIN, p, s));

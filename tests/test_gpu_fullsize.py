@@ -151,12 +151,14 @@ def test_long_prefill_equals_token_by_token_decode(big):
 @pytest.mark.parametrize("case", [0, 1, 2])
 def test_batch_step_at_full_size(big, case):
     # one batched step of several sequences at different installed prefixes, each row against the oracle;
-    # 7B-shaped: 4 sequences (the batch GEMV kernels), 6 and 5 (the tiled matrix-core products);
-    # 70B-layer: 2 and 3 sequences (the batch GEMV kernels, with the split-K product for the
-    # 28672-wide down projection, which has no batch GEMV shape) and 5 (the tiled products)
+    # 7B-shaped: 4 sequences (the batch GEMV kernels), 6 and 5 (the tiled matrix-core products, one
+    # plane of 16 sequences); 70B-layer: 2 and 3 sequences (the batch GEMV kernels, with the split-K
+    # product for the 28672-wide down projection, which has no batch GEMV shape) and 33 (the split-K
+    # matrix-core products)
     cfg, blob, w = big
     lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300], [1, 0, 63, 64, 65]],
-               "llama70b_8l": [[4000, 1500], [100, 4095, 2048], [0, 3000, 4095, 17, 1024]]}[cfg.name][case]
+               "llama70b_8l": [[4000, 1500], [100, 4095, 2048],
+                               [0, 3000, 4095, 17, 1024] + [31 * i + 1 for i in range(28)]]}[cfg.name][case]
     B = len(lengths)
     caches = [(_prefix(cfg, p, 900 + 50 * b) if p else oracle.KVCache(cfg)) for b, p in enumerate(lengths)]
     toks = synth.prefill_tokens(cfg, B)
@@ -168,8 +170,13 @@ def test_batch_step_at_full_size(big, case):
         m.write_kv_cache(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
         del k, v
         got = host(m.forward_batch(toks, lengths))
+    oracle.set_threads(8)  # bit-identical to one thread; 33 sequences of the 70B layer
+    try:
+        refs = [oracle.forward(cfg, blob, caches[b], int(toks[b]), lengths[b]) for b in range(B)]
+    finally:
+        oracle.set_threads(1)
     for b in range(B):
-        ref = oracle.forward(cfg, blob, caches[b], int(toks[b]), lengths[b])
+        ref = refs[b]
         ok, err, tol = logits_close(got[b], ref)
         print(f"[{cfg.name}] batch row {b} at {lengths[b]}: max |d logit| {err:.3g} (tolerance {tol:.3g})",
               flush=True)
