@@ -984,9 +984,10 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
 // (non-temporal 16-byte loads, 16 per thread in flight, like the weight
 // loads of the GEMVs) into sums[b]; the sums keep the loads live.
 // ---------------------------------------------------------------------------
-// Batch decode of up to 16 sequences on the matrix cores, weights pre-tiled
+// Batch decode of up to 32 sequences on the matrix cores, weights pre-tiled
 // (TiledParams): the q/k/v, wo, w1/w3, w2 and classifier products of a decode
-// step over the batch's vectors, C(rows x nb) = W x_b.  Each wave loads whole
+// step over the batch's vectors, C(rows x nb) = W x_b, in planes of 16
+// sequences (NP planes: each weight float4 feeds the MFMAs of every plane).  Each wave loads whole
 // 1 KB tiles (64 lanes x 16 contiguous bytes) and feeds each lane's float4 to
 // four v_mfma_f32_16x16x4f32 steps as the A operand (rows 16 rt + l % 16, k
 // 16 kt + 4 (l / 16) + t at step t), with the tiled activations as the B
