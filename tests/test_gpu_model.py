@@ -95,6 +95,22 @@ def test_graph_and_direct_launches_are_bit_identical(name):
         assert np.array_equal(host(kg), host(ke)) and np.array_equal(host(vg), host(ve))
 
 
+def test_fused_and_separate_attention_launches_agree():
+    # the tiny model runs q/k/v and attention as one launch at every position;
+    # with LD_OPT_NO_FUSE it launches them apart: both within the bar of the
+    # oracle, and of each other to the rounding of the attention's sums
+    cfg, b, w = blob_of("tiny")
+    toks, ref = oracle_run("tiny")
+    inputs = np.concatenate([[1], toks[:-1]])
+    with pkg.Model(cfg, w) as f, pkg.Model(cfg, w, fuse=False) as u:
+        for p in range(cfg.seq_len):
+            a, c = host(f.forward(int(inputs[p]), p)), host(u.forward(int(inputs[p]), p))
+            assert logits_close(c, ref[p])[0], p
+            assert np.max(np.abs(a - c)) <= 1e-5 * np.max(np.abs(ref[p])), p
+        stats = {s["name"]: s["launches"] for s in u.profile(1, 0, 2)}
+    assert stats["qkv_attention"] == 0 and stats["attention"] == 2 * cfg.n_layers
+
+
 @pytest.mark.parametrize("name", ["tiny", "gqa_small"])
 def test_kv_cache_rows_match_oracle(name):
     cfg, b, w = blob_of(name)
