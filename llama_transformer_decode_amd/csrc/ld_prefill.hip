@@ -75,6 +75,10 @@ constexpr int kBN = 128, kGemmThreads = 256;
 #ifndef LD_GEMM_BK_M64
 #define LD_GEMM_BK_M64 16
 #endif
+// 128-row tiles (prompts) take gemm_dtl_kernel (1) or gemm_kernel (0)
+#ifndef LD_GEMM_DTL
+#define LD_GEMM_DTL 1
+#endif
 #ifndef LD_GEMM_R_BATCH
 #define LD_GEMM_R_BATCH 2
 #endif
@@ -186,7 +190,8 @@ struct Mfma<16> {
     static __device__ __forceinline__ int row(int r, int g) { return g * 4 + r; }
 };
 
-// Tiles: BM = 128 rows (prompt prefill), 2 x 2 waves of 64 x 64 with MT = 32.
+// Tiles: BM = 128 rows (prompt prefill; gemm_dtl_kernel below runs these
+// unless LD_GEMM_DTL is 0), 2 x 2 waves of 64 x 64 with MT = 32.
 // A decode batch, where the weight stream is the cost, takes the smallest
 // tile that holds its rows: BM = 16 (1 x 4 waves of 16 x 32, MT = 16), 32
 // (1 x 4 waves of 32 x 32) or 64 (2 x 2 waves of 32 x 64).  The matrix-core
@@ -425,6 +430,270 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p) {
             }
 }
 
+// ---------------------------------------------------------------------------
+// Prompt products (128-row tiles) with the slabs loaded straight into LDS.
+//
+// The same 128 x 128 tile, 2 x 2 waves of 64 x 64 and v_mfma_f32_32x32x2f32
+// as gemm_kernel, but the K slabs (BK deep) go from global memory to LDS by
+// the load-to-LDS form of the global load (global_load_lds_dwordx4: each
+// lane's 16 bytes land at the wave's LDS base + 16 x lane), so no register
+// holds a slab on its way.  ST LDS buffers keep ST - 1 slabs in flight
+// behind the one being multiplied.  Built with BK = 32, ST = 2: 66 KB of LDS
+// and 142 registers, two blocks per CU (two waves per SIMD).  Measured on the
+// 7B-shaped prompt of 2048 tokens: 224.6 ms against 228.4 for gemm_kernel;
+// slabs of 16 with 2-4 buffers 228.6-229.9 ms; one block per CU (BK = 32,
+// ST = 3 or 4) 257-259 ms.
+//
+// Slab layout: row r, k quad c (4 floats) sits at quad position
+// c ^ ((r / SH) % QPR) of its row (QPR = BK / 4 quads; rows SH = 16 / QPR
+// apart share LDS banks).  A fragment read (one k quad of 16 consecutive
+// rows per 16 lanes) then covers every bank once.  A load instruction fills
+// 64 / QPR rows: lane l takes row l / QPR and position l % QPR.
+//
+// Per slab kt a wave runs its MFMAs in groups of 4 k per lane (16 each).
+// The LDS reads of the next group and the loads of slab kt + ST - 1 are
+// issued one at a time between the MFMAs (a wave issues in order, so a burst
+// of them would hold back its next MFMA).  Before the last group a wave
+// waits for its loads of slab kt + 1 (later slabs stay in flight) and its
+// LDS reads of slab kt, then the block barrier: slab kt + 1 is then visible
+// to every wave, and slab kt's buffer free for the loads of the next
+// iteration.  The last group, already in registers, covers the reads of
+// slab kt + 1's first group.
+//
+// NORM: the RMSNorm gain is staged per slab in LDS too (each wave its own
+// copies of the slab's gains, one 4-byte load per lane) and multiplies the A
+// fragments after they are read; the row sums of squares are taken from the
+// same fragments before the gain.
+
+#ifndef LD_GEMM_DTL_STAGES
+#define LD_GEMM_DTL_STAGES 2
+#endif
+#ifndef LD_GEMM_DTL_BK
+#define LD_GEMM_DTL_BK 32
+#endif
+
+__device__ __forceinline__ float f4c(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
+
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ unsigned lds_addr(const float* p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) float*)p;
+}
+
+// One load of 16 bytes per lane straight into LDS at lds + 16 x lane (lds
+// wave-uniform).  Inline assembly, so that the compiler does not take the
+// LDS write as pending at every later LDS read; the kernel counts these
+// loads itself before each barrier.  M0 is set here; nothing else in these
+// kernels uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(const void* g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+// the same with 4 bytes per lane (at lds + 4 x lane)
+__device__ __forceinline__ void lds_load4(const void* g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector memory loads are in flight and
+// all its LDS reads are done, then the block barrier.
+template <int N>
+__device__ __forceinline__ void slab_barrier() {
+    static_assert(N == 0 || N == 4 || N == 5 || N == 8 || N == 9 || N == 10 || N == 16 || N == 18, "load count");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int KIND, bool NORM, int BK, int ST>
+__global__ __launch_bounds__(kGemmThreads, ST * BK <= 64 ? 2 : 1) void gemm_dtl_kernel(GemmParams p) {
+    constexpr int MT = 32, TM = 2, TN = 2, NR = 16;
+    constexpr int QPR = BK / 4;          // k quads per slab row
+    constexpr int RPI = 64 / QPR;        // rows per load instruction
+    constexpr int NI = 128 / RPI / 4;    // load instructions per operand, wave and slab
+    constexpr int SH = 16 / QPR;         // rows apart that share LDS banks
+    constexpr int HK = BK / 2;           // k per lane group and slab
+    constexpr int NG = HK / 4;           // groups of 4 k per slab
+    constexpr int NL = 2 * NI + (NORM ? 1 : 0);  // loads per slab and lane
+    static_assert((BK == 16 || BK == 32) && ST >= 2 && ST <= 4, "shape");
+    typedef Mfma<MT>::acc acc_t;
+    __shared__ __attribute__((aligned(1024))) float As[ST][128 * BK];
+    __shared__ __attribute__((aligned(1024))) float Bs[ST][128 * BK];
+    __shared__ __attribute__((aligned(16))) float Gs[NORM ? ST : 1][NORM ? 256 : 4];
+    __shared__ float row_scale[NORM ? 128 : 1];
+
+    const int mtiles = (p.m + 127) / 128;
+    const int lb = xcd_local_block(blockIdx.x, gridDim.x);
+    const int ks = lb % p.splits, tile = lb / p.splits;
+    const int m0 = (tile % mtiles) * 128, n0 = (tile / mtiles) * kBN;
+    const int kbeg = ks * p.kchunk, kend = min(p.k, kbeg + p.kchunk);
+    const int nslab = (kend - kbeg + BK - 1) / BK;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, lg = lane >> 5;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+
+    // slab loads: instruction i of a wave fills rows 32 wave + RPI i ..; lane
+    // l takes row r = 32 wave + RPI i + l / QPR at position l % QPR, which
+    // holds k quad (l % QPR) ^ ((r / SH) % QPR)
+    int lq[NI];
+    const float* ga[NI];
+    const float* gb[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = 32 * wave + RPI * i + lane / QPR;
+        lq[i] = (lane % QPR) ^ ((r / SH) % QPR);
+        ga[i] = p.a + (size_t)min(m0 + r, p.m - 1) * p.lda + 4 * lq[i];
+        gb[i] = b_row<KIND>(p, min(n0 + r, p.n - 1)) + 4 * lq[i];
+    }
+    // load u of slab s (into buffer s % ST): u < NI the A rows of instruction
+    // u, u < 2 NI the B rows of instruction u - NI, u = 2 NI the gains (each
+    // wave its own copies: lane l takes gain k % BK); k past kend reads zeros
+    auto issue_one = [&](int s, int u) {
+        const int st = s % ST;
+        const int kk = kbeg + BK * s;
+        if (u < 2 * NI) {
+            const int i = u % NI;
+            const bool in = kk + 4 * lq[i] < kend;
+            const float* src = u < NI ? ga[i] + kk : gb[i] + kk;
+            const float* dst = u < NI ? &As[st][(32 * wave + RPI * i) * BK] : &Bs[st][(32 * wave + RPI * i) * BK];
+            lds_load16(in ? (const void*)src : (const void*)gemm_zero4, lds_addr(dst));
+        } else if constexpr (NORM) {
+            lds_load4(p.gain + min(kk + lane % BK, p.k - 1), lds_addr(&Gs[st][64 * wave]));
+        }
+    };
+
+    // fragment offsets (floats in a slab): rows wm + 32 i + li and
+    // wn + 32 j + li; group g reads k quad NG lg + g, at position
+    // (NG lg + g) ^ ((li / SH) % QPR)
+    const int xq = (NG * lg) ^ ((li / SH) % QPR);
+    int aoff[TM], boff[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) aoff[i] = (wm + 32 * i + li) * BK;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) boff[j] = (wn + 32 * j + li) * BK;
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
+    float sq[TM] = {};
+    float4 fa[2][TM], fb[2][TN], gv[2];  // two fragment sets (gains: NORM)
+
+    // LDS read r of group g of buffer st into a fragment set: r = 0, 1 the A
+    // tiles, 2, 3 the B tiles, 4 the gains
+    constexpr int NRD = NORM ? 5 : 4;
+    auto read_one = [&](int st, int g, int set, int r) {
+        const int q = (xq ^ g) << 2;
+        if (r < 2) fa[set][r] = *reinterpret_cast<const float4*>(&As[st][aoff[r] + q]);
+        else if (r < 4) fb[set][r - 2] = *reinterpret_cast<const float4*>(&Bs[st][boff[r - 2] + q]);
+        else if constexpr (NORM) gv[set] = *reinterpret_cast<const float4*>(&Gs[st][64 * wave + HK * lg + 4 * g]);
+    };
+    // NORM: A tile i's rows' sums of squares, then the gain
+    auto prep = [&](int set, int i) {
+        if constexpr (NORM) {
+            const float4 g = gv[set];
+            float4& a = fa[set][i];
+            sq[i] += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+            a = make_float4(a.x * g.x, a.y * g.y, a.z * g.z, a.w * g.w);
+        }
+    };
+    // product idx (0..15) of a group: k step idx / 4, tiles ((idx / 2) % 2, idx % 2)
+    auto mfma_one = [&](int set, int idx) {
+        const int s = idx >> 2, i = (idx >> 1) & 1, j = idx & 1;
+        acc[i][j] = Mfma<MT>::step(f4c(fa[set][i], s), f4c(fb[set][j], s), acc[i][j]);
+    };
+    // group g of slab kt from fragment set g % 2: the reads of (rst, rg) into
+    // the other set after its first products, and in the groups before the
+    // barrier the loads of slab kt + ST - 1 (if any) after every other product
+    auto group = [&](int kt, int g, int rst, int rg) {
+        const int set = g & 1;
+        const int ls = kt + ST - 1;
+        const bool more = ls < nslab;
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+            if (idx == 0) prep(set, 0);
+            mfma_one(set, idx);
+            if (idx == 0) prep(set, 1);
+            if (idx < NRD) read_one(rst, rg, set ^ 1, idx);
+            if (g < NG - 1 && (idx & 1)) {
+                const int u = 8 * g + (idx >> 1);
+                if (u < NL && more) issue_one(ls, u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    static_assert(8 * (NG - 1) >= NL, "load slots");
+    // waits for slab kt + 1 with the loads of later slabs in flight
+    auto end_slab = [&](int kt) {
+        int after = 0;
+#pragma unroll
+        for (int d = 2; d < ST; ++d) after += kt + d < nslab;
+        if (after == 2) slab_barrier<2 * NL>();
+        else if (after == 1) slab_barrier<NL>();
+        else slab_barrier<0>();
+    };
+
+    for (int s = 0; s < ST - 1 && s < nslab; ++s)
+        for (int u = 0; u < NL; ++u) issue_one(s, u);
+    end_slab(-1);
+#pragma unroll
+    for (int r = 0; r < NRD; ++r) read_one(0, 0, 0, r);
+    for (int kt = 0; kt < nslab; ++kt) {
+        const int st = kt % ST;
+#pragma unroll
+        for (int g = 0; g < NG - 1; ++g) group(kt, g, st, g + 1);
+        end_slab(kt);
+        group(kt, NG - 1, (kt + 1) % ST, 0);  // after the last slab the reads are stale and not used
+    }
+
+    if constexpr (NORM) {
+        // lanes li and li + 32 hold row wm + 32 i + li's sum in two halves;
+        // the waves of the first column half publish it
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const float v = sq[i] + __shfl_xor(sq[i], 32);
+            const int r = wm + 32 * i + li, gm = m0 + r;
+            if (wn == 0 && lg == 0) {
+                if (p.splits > 1) {
+                    if (n0 == 0 && gm < p.m) p.part[(size_t)p.splits * p.m * p.n + (size_t)ks * p.m + gm] = v;
+                } else {
+                    row_scale[r] = 1.0f / sqrtf(v / (float)p.k + p.eps);
+                }
+            }
+        }
+        if (p.splits == 1) __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const int gm = m0 + wm + i * MT + Mfma<MT>::row(r, lg);
+                const int gn = n0 + wn + j * MT + li;
+                float v = acc[i][j][r];
+                if constexpr (NORM) {
+                    if (p.splits == 1) v *= row_scale[gm - m0];
+                }
+                if (p.splits > 1) {
+                    if (gm < p.m && gn < p.n) p.part[((size_t)ks * p.m + gm) * p.n + gn] = v;
+                    continue;
+                }
+                const float other = (KIND == G_QKV || KIND == G_SWIGLU) ? __shfl_xor(v, 1) : 0.f;
+                if (gm < p.m && gn < p.n) epilogue<KIND>(p, gm, gn, v, other);
+            }
+}
+
 // Sum of the split partials of C, in split order, then the epilogue: one
 // thread per (row, column pair).  The loads of 8 splits are issued before
 // their sums.  With a norm gain the row's sum of squares is summed the same
@@ -629,6 +898,8 @@ hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim,
 
 namespace {
 
+hipError_t gemm_reduce_launch(int kind, const GemmParams& p, hipStream_t s);
+
 template <int BM, int BK, int MT, int R, bool NORM>
 void gemm_launch_kind(int kind, const GemmParams& p, dim3 grid, dim3 block, hipStream_t s) {
     switch (kind) {
@@ -649,6 +920,35 @@ hipError_t gemm_launch_bm(int kind, const GemmParams& p, hipStream_t s) {
         gemm_launch_kind<BM, BK, MT, R, true>(kind, p, grid, block, s);
     else
         gemm_launch_kind<BM, BK, MT, R, false>(kind, p, grid, block, s);
+    return gemm_reduce_launch(kind, p, s);
+}
+
+template <bool NORM>
+void gemm_dtl_kind(int kind, const GemmParams& p, dim3 grid, hipStream_t s) {
+    const dim3 block(kGemmThreads);
+    switch (kind) {
+        case G_PLAIN: hipLaunchKernelGGL((gemm_dtl_kernel<G_PLAIN, NORM, LD_GEMM_DTL_BK, LD_GEMM_DTL_STAGES>), grid, block, 0, s, p); break;
+        case G_RESID: hipLaunchKernelGGL((gemm_dtl_kernel<G_RESID, NORM, LD_GEMM_DTL_BK, LD_GEMM_DTL_STAGES>), grid, block, 0, s, p); break;
+        case G_QKV: hipLaunchKernelGGL((gemm_dtl_kernel<G_QKV, NORM, LD_GEMM_DTL_BK, LD_GEMM_DTL_STAGES>), grid, block, 0, s, p); break;
+        case G_SWIGLU: hipLaunchKernelGGL((gemm_dtl_kernel<G_SWIGLU, NORM, LD_GEMM_DTL_BK, LD_GEMM_DTL_STAGES>), grid, block, 0, s, p); break;
+    }
+}
+
+// 128-row tiles with direct-to-LDS slabs
+hipError_t gemm_dtl_launch(int kind, const GemmParams& p, hipStream_t s) {
+    const long long blocks = (long long)((p.m + 127) / 128) * ((p.n + kBN - 1) / kBN) * p.splits;
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    if (kind != G_PLAIN && kind != G_RESID && kind != G_QKV && kind != G_SWIGLU) return hipErrorInvalidValue;
+    if (p.gain)
+        gemm_dtl_kind<true>(kind, p, dim3((unsigned)blocks), s);
+    else
+        gemm_dtl_kind<false>(kind, p, dim3((unsigned)blocks), s);
+    return gemm_reduce_launch(kind, p, s);
+}
+
+// the sum of split partials and the epilogue (after either product kernel)
+hipError_t gemm_reduce_launch(int kind, const GemmParams& p, hipStream_t s) {
+    const dim3 block(kGemmThreads);
     if (p.splits > 1) {
         const long long threads = (long long)p.m * ((p.n + 1) / 2);
         const dim3 rgrid((unsigned)((threads + 255) / 256));
@@ -713,7 +1013,11 @@ hipError_t gemm_launch(int kind, const GemmParams& p0, hipStream_t s) {
         case 32: return gemm_launch_bm<32, LD_GEMM_BK_M32, 32, LD_GEMM_R_BATCH>(kind, p, s);
         case 64: return gemm_launch_bm<64, LD_GEMM_BK_M64, 32, LD_GEMM_R_BATCH>(kind, p, s);
     }
+#if LD_GEMM_DTL
+    return gemm_dtl_launch(kind, p, s);
+#else
     return gemm_launch_bm<128, LD_GEMM_BK128, 32, 1>(kind, p, s);
+#endif
 }
 
 bool attn_prefill_supported(int hs) {

@@ -45,7 +45,9 @@ def gemm(a, w):
 @pytest.mark.parametrize("m,n,k", [(1, 1, 4), (3, 5, 8), (128, 128, 16), (129, 130, 20), (200, 300, 100),
                                    (17, 1000, 36), (64, 1536, 288), (256, 1024, 4096), (5, 64, 176),
                                    # each row tile (16, 32, 64) with K split, ragged slabs and tails
-                                   (16, 1000, 1028), (32, 520, 2052), (33, 300, 1000), (63, 260, 772)])
+                                   (16, 1000, 1028), (32, 520, 2052), (33, 300, 1000), (63, 260, 772),
+                                   # 128-row tiles: ragged rows, columns and K (split), one-slab K
+                                   (300, 1000, 1028), (2048, 256, 64), (129, 128, 4), (1000, 130, 292)])
 def test_gemm_exact_on_small_integers(m, n, k):
     rng = np.random.default_rng(m * 1000 + n + k)
     a = rng.integers(-4, 5, (m, k)).astype(np.float32)
@@ -57,7 +59,8 @@ def test_gemm_exact_on_small_integers(m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(64, 4096, 4096), (64, 11008, 4096), (33, 4096, 11008), (16, 8192, 8192),
                                    (16, 1024, 8192), (8, 8192, 28672), (100, 288, 288), (100, 768, 288),
-                                   (100, 288, 768), (64, 176, 64), (64, 64, 176)])
+                                   (100, 288, 768), (64, 176, 64), (64, 64, 176),
+                                   (512, 4096, 4096), (2048, 1024, 4096), (200, 4096, 11008)])
 def test_gemm_within_the_fp32_summation_bound(m, n, k):
     rng = np.random.default_rng(m + n + k)
     a = rng.standard_normal((m, k)).astype(np.float32)
