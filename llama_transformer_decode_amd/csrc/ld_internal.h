@@ -272,6 +272,9 @@ int attn_chunk(int head_size);  // > 0 for a head size the attention kernels cov
 // grid.y of the attention kernel for a context of seq_len positions (the
 // splits of the longest context; shorter ones use fewer, the rest exit)
 int attn_splits(int head_size, int seq_len, int n_heads, int n_kv_heads);
+// grid.y for a decode batch of that many sequences (at most nsplit, the
+// model's attn_splits): the batch's sequences fill the grid themselves
+int attn_batch_splits(int nsplit, int n_kv_heads, int batch);
 // waves per attention block for a context of seq_len positions: 4, or more
 // where the whole grid would be small (few kv heads, short context)
 int attn_waves(int head_size, int seq_len, int n_heads, int n_kv_heads);

@@ -2539,6 +2539,18 @@ int attn_splits(int hs, int seq_len, int n_heads, int n_kv_heads) {
     return splits_for(hs, seq_len, n_heads, n_kv_heads, attn_waves(hs, seq_len, n_heads, n_kv_heads));
 }
 
+// Splits of a decode batch's attention: the batch brings its own blocks, so
+// about kAttnBlocks blocks over all sequences' kv heads.  A split grid sized
+// for one sequence would launch tens of thousands of blocks for a large
+// batch, and at a short context nearly all of them return at once, which
+// cost more than the attention (7B shape, 64 sequences at positions 0-31:
+// 26 us per layer with 16 splits).
+int attn_batch_splits(int nsplit, int n_kv_heads, int batch) {
+    const long long per = (long long)n_kv_heads * (batch > 1 ? batch : 1);
+    const int want = (int)((kAttnBlocks + per - 1) / per);
+    return want < 1 ? 1 : want < nsplit ? want : nsplit;
+}
+
 // Launch one attention kernel (and the merge after it): with events, through
 // hipExtLaunchKernelGGL so that `start` is taken by the attention kernel's own
 // dispatch and `stop` by the last kernel's, bracketing their execution alone.

@@ -636,7 +636,7 @@ hipError_t launch_batch_attention(ld_model* m, int n, int l, float* out_t = null
     a.n_heads = c.n_heads;
     a.n_kv_heads = c.n_kv_heads;
     a.kv_dim = m->kv_dim;
-    a.nsplit = m->nsplit;
+    a.nsplit = attn_batch_splits(m->nsplit, c.n_kv_heads, n);
     a.waves = m->attn_waves;
     a.batch = n;
     a.q_stride = c.dim;
