@@ -1037,6 +1037,24 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
     }
 }
 
+// waves per block and steps of tiles in flight: one plane (up to 16
+// sequences), two planes (17-32).  7B shape, 8 / 16 / 32 sequences: 8 waves
+// and 4 steps 5.05 / 5.07 / 6.47 ms per step; 3 steps 5.05 / 5.08 / 6.44-6.47;
+// 6 steps 5.16 / 5.20 / 6.72; 8 steps (one plane) 5.18 / 5.23; 4 waves
+// 5.44 / 5.49 / 6.70.
+#ifndef LD_TILED_NW1
+#define LD_TILED_NW1 8
+#endif
+#ifndef LD_TILED_D1
+#define LD_TILED_D1 4
+#endif
+#ifndef LD_TILED_NW2
+#define LD_TILED_NW2 8
+#endif
+#ifndef LD_TILED_D2
+#define LD_TILED_D2 4
+#endif
+
 template <int NW, int RT, int D, int KIND, int NP>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     typedef float v4 __attribute__((ext_vector_type(4)));
@@ -1072,17 +1090,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
 #pragma unroll
     for (int jb = 0; jb < NP; ++jb) ss[jb] = 0.f;
     float4 w[D][RT], xv[D][NP];
-    auto load = [&](int kk0) {
+    // step kk's tiles into slot d (past the end: re-read the last tile, not used)
+    auto load_one = [&](int kk, int d) {
+        const int kt = min(kk * NW + wave, KT - 1);
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int kt = min((kk0 + d) * NW + wave, KT - 1);  // past the end: re-read the last tile (not used)
+        for (int j = 0; j < RT; ++j) w[d][j] = wt[((size_t)j * KT + kt) * 64];
 #pragma unroll
-            for (int j = 0; j < RT; ++j) w[d][j] = wt[((size_t)j * KT + kt) * 64];
-#pragma unroll
-            for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
-        }
+        for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
     };
-    load(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_one(d, d);
     for (int kk = 0; kk < nsteps; kk += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -1100,12 +1117,16 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
                             acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4c(w[d][j], t), f4c(xv[d][jb], t),
                                                                               acc[j][jb], 0, 0, 0);
             }
+            // slot d refills with step kk + D + d as soon as its products are
+            // issued, so D steps of tiles stay in flight all the time in the
+            // same registers (7B shape: 16 sequences 5.18 -> 5.07 ms per step,
+            // 32 sequences 6.89 -> 6.49, against refilling all D slots after
+            // the D steps' products).  Unconditional: past the end it re-reads
+            // the last tile; a load that may not have been issued would make
+            // every later wait one for all loads in flight.
+            __builtin_amdgcn_sched_barrier(0);
+            load_one(kk + D + d, d);
         }
-        // keep the next loads after these products: hoisting them would hold
-        // two sets of tiles in registers at once (a second register set, loaded
-        // while the first is multiplied, measured no faster)
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + D < nsteps) load(kk + D);
     }
 #pragma unroll
     for (int j = 0; j < RT; ++j)
@@ -2396,9 +2417,9 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
 template <int KIND>
 void tiled_dispatch(const TiledParams& p, hipStream_t s) {
     if (p.nb <= 16)
-        tiled_shape<KIND, 8, 4, 1, 4>(p, s);
+        tiled_shape<KIND, LD_TILED_NW1, LD_TILED_D1, 1, 4>(p, s);
     else
-        tiled_shape<KIND, 8, 4, 2, 2>(p, s);
+        tiled_shape<KIND, LD_TILED_NW2, LD_TILED_D2, 2, 2>(p, s);
 }
 
 hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s) {
