@@ -741,18 +741,24 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
 // on the matrix cores with v_mfma_f32_16x16x4f32.
 //
 // A block (4 waves) takes two tiles of 64 consecutive queries of one head h,
-// one after the other (a short and a long one); each wave 16 of a tile's.  Key tiles of 32 rows of K and V (kv head g(h)) are staged in LDS
-// by the whole block.  Per 16 keys a wave computes the transposed score tile
-// S^T (16 keys x 16 queries) = K Q^T: lane l then holds 4 keys of query
+// one after the other (a short and a long one); each wave 16 of a tile's.
+// Key tiles of 32 rows of K (as rows) and V (transposed: Vt[d][key]) of kv
+// head g(h) are staged in LDS by the whole block.  Per 16 keys a wave
+// computes the transposed score tile S^T (16 keys x 16 queries) = K Q^T:
+// lane l then holds 4 keys of query
 // l % 16, so the online softmax statistics (m, l) of a query live in the four
 // lanes l % 16 + 16c and need two lane exchanges.  The same registers are
 // the B operand of O^T (hs x 16 queries) += V^T P^T, whose result keeps the
 // query in l % 16, so the rescale by e^(m_old - m_new) needs no exchange.
+// Scores are kept in base-2
+// units (q scaled by log2(e) / sqrt(hs)), so the weights come from the native
+// 2^x.
 // Q (hs/4 floats per lane) and O^T (hs/4) stay in registers.  The MFMA's four
 // k positions per step are k = (hs/4) c + s for lane quarter c in the score
 // product, and key 4c + s in the value product.
 
 constexpr int kAQ = 64;       // queries per block
+constexpr float kLog2eP = 1.4426950408889634f;  // log2(e)
 constexpr int kAK = 32;       // keys per LDS tile
 constexpr int kAPad = 4;
 
@@ -761,18 +767,24 @@ constexpr int kAPad = 4;
 #endif
 
 template <int HS>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) {
+// (three blocks per CU where the head fits: 126 registers at head size 128,
+// against 172 at two, which left the 70B layer's 1792 blocks a third fewer
+// slots: 951 against 1099 us per layer of its 3584-token prompt)
+__global__ __launch_bounds__(256, HS <= 128 ? 3 : 1) void attn_prefill_kernel(AttnPrefillParams p) {
     constexpr int Q4 = HS / 4;    // d per lane quarter
     constexpr int CT = HS / 16;   // 16-wide column tiles of the output
     constexpr int ROW = HS + kAPad;
+    constexpr int VROW = kAK + 4;  // keys per row of the transposed value tile (+4: no bank conflicts)
     __shared__ __attribute__((aligned(16))) float Ks[kAK][ROW];
-    __shared__ __attribute__((aligned(16))) float Vs[kAK][ROW];
+    __shared__ __attribute__((aligned(16))) float Vt[HS][VROW];
 
     const int h = blockIdx.y;
     const int g = (int)(((long long)h * p.n_kv_heads) / p.n_heads);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 15, lc = lane >> 4;
-    const float scale = 1.0f / sqrtf((float)HS);
+    // scores in base-2 units: q is scaled by log2(e) / sqrt(hs), so that
+    // e^(s - m) is 2^(s2 - m2) on the native exponential
+    const float scale = kLog2eP / sqrtf((float)HS);
     const float* kbase = p.kc + (size_t)g * HS;
     const float* vbase = p.vc + (size_t)g * HS;
     const int ntiles = (p.t + kAQ - 1) / kAQ;
@@ -789,7 +801,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
         const int tq = min(wq0 + lq, p.t - 1);  // this lane's query (clamped; results past T are not stored)
         const int qpos = p.pos0 + tq;
 
-        // Q row quarter: Q[tq][h*HS + lc*Q4 + s], pre-scaled by 1/sqrt(hs)
+        // Q row quarter: Q[tq][h*HS + lc*Q4 + s], pre-scaled
         float qv[Q4];
         {
             const float4* q4 = reinterpret_cast<const float4*>(p.q + (size_t)tq * p.ldq + (size_t)h * HS + lc * Q4);
@@ -812,13 +824,55 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
         const int wave_last_pos = p.pos0 + min(wq0 + 15, p.t - 1);
 
         for (int k0 = 0; k0 < n_keys; k0 += kAK) {
-            // stage keys k0 .. k0 + 31 (rows past the last key read the last key; they are masked)
+            // stage keys k0 .. k0 + 31 (rows past the last key read the last key;
+            // they are masked): K as rows, V transposed (Vt[d][key]), so that a
+            // lane's four values of one output column are one 16-byte read.
+            // All of a thread's loads go out before its LDS writes (one round
+            // trip per tile).  V item e: dims 4 c4 .. 4 c4 + 3 of keys 4 kg ..
+            // 4 kg + 3 (kg fastest across lanes: two-way bank conflicts at most).
             __syncthreads();
-            for (int e = tid; e < kAK * (HS / 4); e += 256) {
-                const int r = e / (HS / 4), c4 = e % (HS / 4);
-                const size_t row = (size_t)min(k0 + r, n_keys - 1) * p.kv_stride;
-                *reinterpret_cast<float4*>(&Ks[r][4 * c4]) = reinterpret_cast<const float4*>(kbase + row)[c4];
-                *reinterpret_cast<float4*>(&Vs[r][4 * c4]) = reinterpret_cast<const float4*>(vbase + row)[c4];
+            {
+                // items past the end are clamped to the last one: loaded and
+                // written twice with the same values, with no branch (a load
+                // behind a branch is waited for on its own)
+                constexpr int NKE = kAK * (HS / 4), NVE = (kAK / 4) * (HS / 4);
+                constexpr int NKI = (NKE + 255) / 256, NVI = (NVE + 255) / 256;
+                float4 kr[NKI], vr[NVI][4];
+#pragma unroll
+                for (int i = 0; i < NKI; ++i) {
+                    const int e = min(tid + 256 * i, NKE - 1);
+                    const int r = e / (HS / 4), c4 = e % (HS / 4);
+                    const size_t row = (size_t)min(k0 + r, n_keys - 1) * p.kv_stride;
+                    kr[i] = reinterpret_cast<const float4*>(kbase + row)[c4];
+                }
+#pragma unroll
+                for (int i = 0; i < NVI; ++i) {
+                    const int e = min(tid + 256 * i, NVE - 1);
+                    const int kg = e % (kAK / 4), c4 = e / (kAK / 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const size_t row = (size_t)min(k0 + 4 * kg + j, n_keys - 1) * p.kv_stride;
+                        vr[i][j] = reinterpret_cast<const float4*>(vbase + row)[c4];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NKI; ++i) {
+                    const int e = min(tid + 256 * i, NKE - 1);
+                    *reinterpret_cast<float4*>(&Ks[e / (HS / 4)][4 * (e % (HS / 4))]) = kr[i];
+                }
+#pragma unroll
+                for (int i = 0; i < NVI; ++i) {
+                    const int e = min(tid + 256 * i, NVE - 1);
+                    const int kg = e % (kAK / 4), c4 = e / (kAK / 4);
+                    *reinterpret_cast<float4*>(&Vt[4 * c4 + 0][4 * kg]) =
+                        make_float4(vr[i][0].x, vr[i][1].x, vr[i][2].x, vr[i][3].x);
+                    *reinterpret_cast<float4*>(&Vt[4 * c4 + 1][4 * kg]) =
+                        make_float4(vr[i][0].y, vr[i][1].y, vr[i][2].y, vr[i][3].y);
+                    *reinterpret_cast<float4*>(&Vt[4 * c4 + 2][4 * kg]) =
+                        make_float4(vr[i][0].z, vr[i][1].z, vr[i][2].z, vr[i][3].z);
+                    *reinterpret_cast<float4*>(&Vt[4 * c4 + 3][4 * kg]) =
+                        make_float4(vr[i][0].w, vr[i][1].w, vr[i][2].w, vr[i][3].w);
+                }
             }
             __syncthreads();
             if (k0 > wave_last_pos) continue;  // every key of the tile is after every query of this wave
@@ -848,25 +902,27 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillParams p) 
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
                 tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
                 const float m_new = fmaxf(m, tmax);  // finite: key 0 is in the first tile of every query
-                const float alpha = expf(m - m_new);
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
                 float psum = 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    sc[r] = expf(sc[r] - m_new);
+                    sc[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
                     psum += sc[r];
                 }
                 psum += __shfl_xor(psum, 16);
                 psum += __shfl_xor(psum, 32);
                 l = l * alpha + psum;
                 m = m_new;
-                // O^T(hs x 16 queries) += V^T P^T: A = V^T (column 16 c + lq, key 4 lc + r), B = P^T
+                // O^T(hs x 16 queries) += V^T P^T: A = V^T (column 16 c + lq,
+                // keys 4 lc + r, one 16-byte read), B = P^T
 #pragma unroll
                 for (int c = 0; c < CT; ++c) {
                     o[c] *= alpha;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(Vs[sub * 16 + lc * 4 + r][c * 16 + lq], sc[r],
-                                                                    o[c], 0, 0, 0);
+                    const float4 vv = *reinterpret_cast<const float4*>(&Vt[c * 16 + lq][sub * 16 + lc * 4]);
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.x, sc[0], o[c], 0, 0, 0);
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.y, sc[1], o[c], 0, 0, 0);
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.z, sc[2], o[c], 0, 0, 0);
+                    o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv.w, sc[3], o[c], 0, 0, 0);
                 }
             }
         }
