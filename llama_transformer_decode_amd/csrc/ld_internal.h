@@ -148,7 +148,10 @@ struct AttnParams {
 // k = 16 kt + 4 (l / 16) + 0..3, times the gain of the product's RMSNorm at k.
 // Tiled activations (vectors of n floats, planes of 16 sequences): float4
 // ((plane * n/16 + kt) * 64 + l) = x[16 plane + l % 16][16 kt + 4 (l / 16) + 0..3].
-constexpr int kTiledBatch = 32;
+#ifndef LD_TILED_BATCH
+#define LD_TILED_BATCH 64
+#endif
+constexpr int kTiledBatch = LD_TILED_BATCH;
 
 struct TiledParams {
     const float* w;        // tiled weights (gain folded in)

@@ -984,7 +984,7 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
 // (non-temporal 16-byte loads, 16 per thread in flight, like the weight
 // loads of the GEMVs) into sums[b]; the sums keep the loads live.
 // ---------------------------------------------------------------------------
-// Batch decode of up to 32 sequences on the matrix cores, weights pre-tiled
+// Batch decode of up to 64 sequences on the matrix cores, weights pre-tiled
 // (TiledParams): the q/k/v, wo, w1/w3, w2 and classifier products of a decode
 // step over the batch's vectors, C(rows x nb) = W x_b, in planes of 16
 // sequences (NP planes: each weight float4 feeds the MFMAs of every plane).  Each wave loads whole
@@ -1053,6 +1053,20 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
 #endif
 #ifndef LD_TILED_D2
 #define LD_TILED_D2 4
+#endif
+// three or four planes (33-48, 49-64 sequences): 4 waves, 2 steps in
+// flight, up to 4 row tiles.  7B shape, 40 / 64 sequences: 8.03 / 9.76 ms
+// per step, against 10.12 / 10.68 with the split-K products; four planes for
+// 40 as well 9.62; 8 waves 9.76-10.16 / 9.93-10.31 (3 steps 10.09, 1 step
+// 12.08); 2 waves 14.7.
+#ifndef LD_TILED_NW4
+#define LD_TILED_NW4 4
+#endif
+#ifndef LD_TILED_D4
+#define LD_TILED_D4 2
+#endif
+#ifndef LD_TILED_RT4
+#define LD_TILED_RT4 4
 #endif
 
 template <int NW, int RT, int D, int KIND, int NP>
@@ -2387,11 +2401,11 @@ int tiled_balance(int blocks, int cus) {
 
 // Up to 16 sequences (one plane): 8 waves, 4 steps in flight, 1 to 4 row
 // tiles.  17-32 (two planes): 8 waves, 4 steps, 1 or 2 row tiles (registers
-// and LDS hold row tiles x planes partial tiles).  Four planes (33-64
-// sequences, 4 waves, 2 steps) ran at 13.5-13.9 ms per 7B-shaped step against
-// 10.8-11.1 ms with the split-K products, so the tiled path stops at 32: the
-// matrix cores are then about 38% busy, with twice as many activation bytes
-// read from L2 as weight bytes from HBM.
+// and LDS hold row tiles x planes partial tiles).  33-48 and 49-64 (three and
+// four planes): 4 waves, 2 steps, 1 to 4 row tiles.  Before each step's slot
+// was refilled as soon as its products were issued, four planes ran at
+// 13.5-13.9 ms per 7B-shaped step against 10.8-11.1 ms with the split-K
+// products; with the refill, 9.8 against 10.7.
 template <int KIND, int NW, int D, int NP, int RT>
 void tiled_go(const TiledParams& p, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((tiled_kernel<NW, RT, D, KIND, NP>), dim3(blocks), dim3(NW * 64), 0, s, p);
@@ -2418,8 +2432,14 @@ template <int KIND>
 void tiled_dispatch(const TiledParams& p, hipStream_t s) {
     if (p.nb <= 16)
         tiled_shape<KIND, LD_TILED_NW1, LD_TILED_D1, 1, 4>(p, s);
-    else
+    else if (kTiledBatch <= 32 || p.nb <= 32)
         tiled_shape<KIND, LD_TILED_NW2, LD_TILED_D2, 2, 2>(p, s);
+#if LD_TILED_BATCH > 32
+    else if (p.nb <= 48)
+        tiled_shape<KIND, LD_TILED_NW4, LD_TILED_D4, 3, LD_TILED_RT4>(p, s);
+    else
+        tiled_shape<KIND, LD_TILED_NW4, LD_TILED_D4, 4, LD_TILED_RT4>(p, s);
+#endif
 }
 
 hipError_t tiled_launch(int kind, const TiledParams& p, hipStream_t s) {

@@ -9,8 +9,8 @@ the GPU caches and in the oracle's), so one batched step mixes positions; the
 appended cache rows must match the oracle's, and no other sequence's rows may
 change.  Greedy generation in lockstep must reproduce each sequence's oracle
 tokens up to its first tie.  Batches of up to 4 sequences take the batch
-GEMV kernels, 5 to 32 the tiled matrix-core products (in planes of 16
-sequences), more the split-K matrix-core products.
+GEMV kernels, 5 to 64 the tiled matrix-core products (in planes of 16
+sequences: one to four), more the split-K matrix-core products.
 """
 import numpy as np
 import pytest
@@ -73,8 +73,12 @@ def install(m, cfg, caches):
                                                          500, 507]),
                                           # 17-32 sequences: two planes of 16
                                           ("tiny", [3 * i for i in range(20)]),
-                                          # more than 32: the split-K matrix-core products
+                                          # 33-48: three planes; 49-64: four
                                           ("stories15m", [(37 * i) % 250 for i in range(40)]),
+                                          ("tiny", [(11 * i) % 60 for i in range(48)]),
+                                          ("gqa_small", [(97 * i) % 500 for i in range(49)]),
+                                          ("tiny", [(5 * i) % 60 for i in range(64)]),
+                                          # more than 64: the split-K matrix-core products
                                           ("tiny", [(7 * i) % 60 for i in range(65)])])
 def test_batch_steps_at_mixed_positions(name, lengths, graph):
     cfg, blob, w = blob_of(name)

@@ -153,8 +153,8 @@ def test_batch_step_at_full_size(big, case):
     # one batched step of several sequences at different installed prefixes, each row against the oracle;
     # 7B-shaped: 4 sequences (the batch GEMV kernels), 6 and 5 (the tiled matrix-core products, one
     # plane of 16 sequences); 70B-layer: 2 and 3 sequences (the batch GEMV kernels, with the split-K
-    # product for the 28672-wide down projection, which has no batch GEMV shape) and 33 (the split-K
-    # matrix-core products)
+    # product for the 28672-wide down projection, which has no batch GEMV shape) and 33 (the tiled
+    # matrix-core products, three planes of 16 sequences)
     cfg, blob, w = big
     lengths = {"llama7b": [[0, 700, 2000, 33], [5, 1200, 0, 2047, 64, 300], [1, 0, 63, 64, 65]],
                "llama70b_8l": [[4000, 1500], [100, 4095, 2048],
