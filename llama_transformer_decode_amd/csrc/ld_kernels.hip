@@ -2424,7 +2424,19 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
         case 4: if constexpr (RT_MAX >= 4) tiled_go<KIND, NW, D, NP, 4>(p, tiles / 4, s); break;
         case 3: if constexpr (RT_MAX >= 3) tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s); break;
         case 2: tiled_go<KIND, NW, D, NP, 2>(p, tiles / 2, s); break;
-        default: tiled_go<KIND, NW, D, NP, 1>(p, tiles, s); break;
+        default:
+            // three or four planes with one block per CU at most (wo and w2):
+            // 8 waves and 8 steps in flight instead of 4 and 2 (7B shape, 40 /
+            // 64 sequences: 8.07 / 9.78 -> 7.72 / 9.63 ms per step; for one or
+            // two planes the same change was 1-2% slower)
+            if constexpr (NP >= 3) {
+                if (tiles <= cus) {
+                    tiled_go<KIND, 8, 8, NP, 1>(p, tiles, s);
+                    break;
+                }
+            }
+            tiled_go<KIND, NW, D, NP, 1>(p, tiles, s);
+            break;
     }
 }
 
