@@ -234,6 +234,9 @@ struct AttnPrefillParams {
 };
 
 hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s);
+// out[t] = RMSNorm(x[t]) with the gain, for t rows of dim floats (dim % 4 == 0)
+hipError_t rmsnorm_rows_launch(const float* x, const float* gain, float eps, int t, int dim, float* out,
+                               hipStream_t s);
 // a decode batch: x[b] = E[st[b].token]; the greedy token of every logits row,
 // tokens_out[b * tokens_stride + pos_b], and each sequence's state advances
 // xt (optional): the same rows in the tiled layout of TiledParams (batch <= kTiledBatch)

@@ -41,6 +41,31 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ em
 }
 
 
+// RMSNorm of every token row ("run.c 逐行解讀" §4 rmsnorm): out = g * (x *
+// 1/sqrt(mean(x^2) + eps)), one block per row, for the prompt products that
+// read a normalised copy of the residual stream.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, const float* __restrict__ gain,
+                                                           float eps, int dim, float* __restrict__ out) {
+    __shared__ float part[4];
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)blockIdx.x * dim);
+    const float4* g4 = reinterpret_cast<const float4*>(gain);
+    float4* o = reinterpret_cast<float4*>(out + (size_t)blockIdx.x * dim);
+    const int n4 = dim / 4;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        const float4 v = xr[i];
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)dim + eps);
+    for (int i = threadIdx.x; i < n4; i += 256) {
+        const float4 v = xr[i], g = g4[i];
+        o[i] = make_float4(g.x * (r * v.x), g.y * (r * v.y), g.z * (r * v.z), g.w * (r * v.w));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // C = A * B^T on the matrix cores.
 //
@@ -942,6 +967,13 @@ __global__ __launch_bounds__(256, HS <= 128 ? 3 : 1) void attn_prefill_kernel(At
 
 hipError_t embed_launch(const float* emb, const int32_t* tokens, int t, int dim, float* x, hipStream_t s) {
     hipLaunchKernelGGL(embed_kernel, dim3(t), dim3(256), 0, s, emb, tokens, dim, x);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm_rows_launch(const float* x, const float* gain, float eps, int t, int dim, float* out,
+                               hipStream_t s) {
+    if (t <= 0 || dim <= 0 || dim % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(t), dim3(256), 0, s, x, gain, eps, dim, out);
     return hipGetLastError();
 }
 

@@ -502,6 +502,10 @@ int run_step(ld_model* m, long long pos) {
     return launch_step(m, nullptr, fused);
 }
 
+#ifndef LD_PREFILL_NORM_ROWS
+#define LD_PREFILL_NORM_ROWS 1
+#endif
+
 // Tokens per prefill chunk: chunks run one after another, each attending to
 // the cache rows the earlier ones wrote.
 constexpr int kPrefillChunk = 2048;
@@ -538,9 +542,15 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
     for (int l = 0; l < c.n_layers; ++l) {
         {
             GemmParams g{};
+#if LD_PREFILL_NORM_ROWS
+            // the normalised rows go to pf_att (free until the attention writes it)
+            HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_att + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_att, s));
+            g.a = m->pf_att;
+#else
             g.a = m->pf_x;
             g.gain = m->rms_att + (size_t)l * d;
             g.eps = m->opt.norm_eps;
+#endif
             g.lda = c.dim;
             g.m = T;
             g.n = c.dim + 2 * m->kv_dim;
@@ -589,9 +599,15 @@ int prefill_chunk(ld_model* m, int seq, int p0, int T) {
         }
         {
             GemmParams g{};
+#if LD_PREFILL_NORM_ROWS
+            // pf_att is free again once wo has read it
+            HIP_TRY(rmsnorm_rows_launch(m->pf_x, m->rms_ffn + (size_t)l * d, m->opt.norm_eps, T, c.dim, m->pf_att, s));
+            g.a = m->pf_att;
+#else
             g.a = m->pf_x;
             g.gain = m->rms_ffn + (size_t)l * d;
             g.eps = m->opt.norm_eps;
+#endif
             g.lda = c.dim;
             g.m = T;
             g.n = 2 * c.hidden_dim;
