@@ -1007,6 +1007,28 @@ __host__ __device__ __forceinline__ size_t tiled_slot(int b, int k, int n) {
     return ((size_t)(b >> 4) * (size_t)(n >> 4) + (size_t)(k >> 4)) * 64 + ((k & 15) >> 2) * 16 + (b & 15);
 }
 
+// The 1 KB weight tiles of a product sit in groups of LD_TILED_KG k tiles:
+// group g holds k tiles 8g .. 8g + 7 of row tile 0, then of row tile 1, and so
+// on, so the blocks, which all walk K at about the same pace, read one
+// contiguous stretch of the copy at a time.  With each row tile's K contiguous
+// instead (LD_TILED_KG 0), the blocks' streams sit one row tile (256-688 KB)
+// apart and the batch step is 3-4% slower (7B shape, 8 / 16 / 32 sequences
+// 5.03 / 5.08 / 6.58 -> 4.81 / 4.87 / 6.38 ms per step; groups of 4 or 16
+// within 0.5% of 8).
+#ifndef LD_TILED_KG
+#define LD_TILED_KG 8
+#endif
+// 1 KB weight tile (row tile rt of rtn, k tile kt of KT) in the tiled weights
+__host__ __device__ __forceinline__ size_t tiled_wtile(int rt, int kt, int rtn, int KT) {
+    if constexpr (LD_TILED_KG == 0) {
+        return (size_t)rt * KT + kt;
+    } else {
+        const int g = kt / LD_TILED_KG, g0 = g * LD_TILED_KG;
+        const int width = KT - g0 < LD_TILED_KG ? KT - g0 : LD_TILED_KG;
+        return (size_t)g0 * rtn + (size_t)rt * width + (kt - g0);
+    }
+}
+
 __device__ __forceinline__ float f4c(const float4& v, int t) { return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w; }
 
 __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float* __restrict__ w0,
@@ -1022,6 +1044,7 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
         const int rt = (int)(tile / kt_n), kt = (int)(tile % kt_n);
         const int row = 16 * rt + (l & 15), col = 16 * kt + 4 * (l >> 4);
         const float* src;
+        const size_t di = tiled_wtile(rt, kt, rows / 16, kt_n) * 64 + l;
         if (kind == K_QKV)
             src = row < seg1 ? w0 + (size_t)row * k : row < seg2 ? w1 + (size_t)(row - seg1) * k : w2 + (size_t)(row - seg2) * k;
         else if (kind == K_SWIGLU)
@@ -1033,7 +1056,7 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
             const float4 g = *reinterpret_cast<const float4*>(gain + col);
             v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
         }
-        dst[i] = v;
+        dst[di] = v;
     }
 }
 
@@ -1059,6 +1082,18 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
 // per step, against 10.12 / 10.68 with the split-K products; four planes for
 // 40 as well 9.62; 8 waves 9.76-10.16 / 9.93-10.31 (3 steps 10.09, 1 step
 // 12.08); 2 waves 14.7.
+#ifndef LD_TILED_TIE
+#define LD_TILED_TIE 1
+#endif
+#ifndef LD_TILED_ONE8
+#define LD_TILED_ONE8 0
+#endif
+#ifndef LD_TILED_NWS
+#define LD_TILED_NWS 0
+#endif
+#ifndef LD_TILED_DS
+#define LD_TILED_DS 4
+#endif
 #ifndef LD_TILED_NW4
 #define LD_TILED_NW4 4
 #endif
@@ -1079,7 +1114,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     const int KT = p.k >> 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rt0 = blockIdx.x * RT;
-    const float4* wt = reinterpret_cast<const float4*>(p.w) + (size_t)rt0 * KT * 64 + lane;
+    const float4* wt = reinterpret_cast<const float4*>(p.w) + lane;
+    const int rtn = p.rows >> 4;
     const float4* xt = reinterpret_cast<const float4*>(p.x) + lane;  // plane jb at + jb * KT * 64
     const int nsteps = (KT + NW - 1) / NW;  // this wave: tiles wave, wave + NW, ... below KT
     // the residual rows this thread adds to in the epilogue are loaded now, so
@@ -1108,7 +1144,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     auto load_one = [&](int kk, int d) {
         const int kt = min(kk * NW + wave, KT - 1);
 #pragma unroll
-        for (int j = 0; j < RT; ++j) w[d][j] = wt[((size_t)j * KT + kt) * 64];
+        for (int j = 0; j < RT; ++j) w[d][j] = wt[tiled_wtile(rt0 + j, kt, rtn, KT) * 64];
 #pragma unroll
         for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
     };
@@ -2416,13 +2452,23 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
     const int tiles = p.rows / 16, cus = cu_count();
     int rt = 1, best = tiled_balance(tiles, cus);
     for (int r = 2; r <= RT_MAX; ++r)
-        if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) >= best) {
+        if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) + LD_TILED_TIE >= best + 1) {
             rt = r;
             best = tiled_balance(tiles / r, cus);
         }
     switch (rt) {
         case 4: if constexpr (RT_MAX >= 4) tiled_go<KIND, NW, D, NP, 4>(p, tiles / 4, s); break;
-        case 3: if constexpr (RT_MAX >= 3) tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s); break;
+        case 3:
+            if constexpr (RT_MAX >= 3) {
+#if LD_TILED_ONE8
+                if (NP >= 3 && tiles / 3 <= cus) {
+                    tiled_go<KIND, 8, LD_TILED_ONE8, NP, 3>(p, tiles / 3, s);
+                    break;
+                }
+#endif
+                tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s);
+            }
+            break;
         case 2: tiled_go<KIND, NW, D, NP, 2>(p, tiles / 2, s); break;
         default:
             // three or four planes with one block per CU at most (wo and w2):
@@ -2435,6 +2481,14 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
                     break;
                 }
             }
+#if LD_TILED_NWS
+            if constexpr (NP <= 2) {
+                if (tiles <= cus) {
+                    tiled_go<KIND, LD_TILED_NWS, LD_TILED_DS, NP, 1>(p, tiles, s);
+                    break;
+                }
+            }
+#endif
             tiled_go<KIND, NW, D, NP, 1>(p, tiles, s);
             break;
     }
