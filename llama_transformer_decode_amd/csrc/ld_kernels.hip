@@ -619,6 +619,16 @@ __device__ __forceinline__ float4 load_w(const float4* p) {
 #endif
 }
 
+// Row groups of a GEMV go to the blocks round robin (block b: groups b, b +
+// grid, ...), so at any time the blocks read one contiguous stretch of the
+// matrix.  With a contiguous range of groups per block (LD_GEMV_STRIDE 0) the
+// 7B-shaped decode runs at 232.0 tok/s, with round robin 235.5-235.9; the
+// plain streaming read is the other way round (contiguous shares 7.07 TB/s,
+// 64 KB chunks round robin 6.59).
+#ifndef LD_GEMV_STRIDE
+#define LD_GEMV_STRIDE 1
+#endif
+
 constexpr bool is_qkv_kind(int kind) { return kind == K_QKV || kind == K_QKV_ATT; }
 
 // Rows of row group u.  K_SWIGLU interleaves w1 and w3 rows of the same
@@ -673,9 +683,13 @@ __device__ void gemv_body(const GemvParams& p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n4 = p.n >> 2;
 
-    // row groups of this block (an even split of p.units over the grid)
-    const int u0 = (int)(((long long)blockIdx.x * p.units) / gridDim.x);
-    const int u1 = (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    // row groups of this block: round robin over the grid, or (the q/k/v
+    // kernel with fused attention, whose blocks report the rows they wrote)
+    // an even split of p.units into contiguous ranges
+    constexpr bool kStride = LD_GEMV_STRIDE && KIND != K_QKV_ATT;
+    const int u0 = kStride ? (int)blockIdx.x : (int)(((long long)blockIdx.x * p.units) / gridDim.x);
+    const int u1 = kStride ? p.units : (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    const int ustep = kStride ? (int)gridDim.x : 1;
     float4 w[RPI][NX];
     if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
 
@@ -744,7 +758,7 @@ __device__ void gemv_body(const GemvParams& p) {
     float bv = -INFINITY;
     int bi = INT_MAX;
     int buf = 0;
-    for (int u = u0; u < u1; ++u) {
+    for (int u = u0; u < u1; u += ustep) {
         float acc[RPI];
 #pragma unroll
         for (int r = 0; r < RPI; ++r) {
@@ -755,9 +769,9 @@ __device__ void gemv_body(const GemvParams& p) {
         // keep the next group's loads after these products: hoisting them
         // would hold two groups of weights in registers at once
         __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < u1) {
-            load_group<NT, NX, RPI, KIND>(p, u + 1, n4, w);
-            if constexpr (KIND == K_RESID) res_nxt = res_load(u + 1);
+        if (u + ustep < u1) {
+            load_group<NT, NX, RPI, KIND>(p, u + ustep, n4, w);
+            if constexpr (KIND == K_RESID) res_nxt = res_load(u + ustep);
         }
 #pragma unroll
         for (int r = 0; r < RPI; ++r) acc[r] = wave_sum(acc[r]);
@@ -858,8 +872,10 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n4 = p.n >> 2;
 
-    const int u0 = (int)(((long long)blockIdx.x * p.units) / gridDim.x);
-    const int u1 = (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    constexpr bool kStride = LD_GEMV_STRIDE;
+    const int u0 = kStride ? (int)blockIdx.x : (int)(((long long)blockIdx.x * p.units) / gridDim.x);
+    const int u1 = kStride ? p.units : (int)(((long long)(blockIdx.x + 1) * p.units) / gridDim.x);
+    const int ustep = kStride ? (int)gridDim.x : 1;
     float4 w[RPI][NX];
     if (u0 < u1) load_group<NT, NX, RPI, KIND>(p, u0, n4, w);
 
@@ -908,7 +924,7 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
     const int vb = tid / RPI, vr = tid % RPI;
     const bool mine = tid < V && vb < p.nb;
     int buf = 0;
-    for (int u = u0; u < u1; ++u) {
+    for (int u = u0; u < u1; u += ustep) {
         float acc[NB][RPI];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -919,7 +935,7 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
                 for (int k = 0; k < NX; ++k) acc[b][r] = dot4(w[r][k], xr[b][k], acc[b][r]);
             }
         __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < u1) load_group<NT, NX, RPI, KIND>(p, u + 1, n4, w);
+        if (u + ustep < u1) load_group<NT, NX, RPI, KIND>(p, u + ustep, n4, w);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -1260,9 +1276,9 @@ constexpr int kStreamThreads = 256, kStreamU = 16;
 __global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const float4* __restrict__ src, long long n4,
                                                                      long long per, float* __restrict__ sums) {
     __shared__ float part[kStreamThreads / 64];
+    float acc = 0.f;
     const long long b0 = (long long)blockIdx.x * per;
     const long long b1 = min(n4, b0 + per);
-    float acc = 0.f;
     long long i = b0 + threadIdx.x;
     for (; i + (long long)(kStreamU - 1) * kStreamThreads < b1; i += (long long)kStreamThreads * kStreamU) {
         float4 v[kStreamU];
@@ -2092,6 +2108,16 @@ struct Tpl {
 #ifndef LD_GEMV_28672
 #define LD_GEMV_28672 {512, 14, 1}
 #endif
+// Per-kind shapes for 1024 < n <= 4096, chosen on whole greedy decodes of the
+// 7B shape with the round-robin row groups: the q/k/v product 256 x 4 x 2
+// (31.9 -> 31.1 us; the same shape for wo was 11.1 -> 11.6 us), the
+// classifier one row per group (84.7 -> 83.7 us).
+#ifndef LD_GEMV_QKV4096
+#define LD_GEMV_QKV4096 {256, 4, 2}
+#endif
+#ifndef LD_GEMV_CLS4096
+#define LD_GEMV_CLS4096 {512, 2, 1}
+#endif
 constexpr Tpl kTpl[] = {
     LD_GEMV_256,       // n <= 256
     LD_GEMV_512,       // n <= 512
@@ -2101,8 +2127,16 @@ constexpr Tpl kTpl[] = {
     LD_GEMV_12288,     // n <= 12288
     LD_GEMV_28672,     // n <= 28672
     {512, 16, 1},      // n <= 32768
+    LD_GEMV_QKV4096,   // K_QKV in place of entry 3
+    LD_GEMV_CLS4096,   // K_CLS in place of entry 3
 };
 constexpr int kNumTpl = sizeof(kTpl) / sizeof(kTpl[0]);
+constexpr int kNumWidthTpl = 8;  // entries chosen by input width
+
+// the entry a kind uses in place of width entry t
+constexpr int kind_template(int kind, int t) {
+    return t == 3 && kind == K_QKV ? 8 : t == 3 && kind == K_CLS ? 9 : t;
+}
 
 constexpr int rows_per_group(int t, int kind) {
     return (is_qkv_kind(kind) || kind == K_SWIGLU) && kTpl[t].rpi < 2 ? 2 : kTpl[t].rpi;
@@ -2126,6 +2160,8 @@ GemvFn gemv_fn(int t) {
         case 5: return gemv_fn_t<KIND, 5>();
         case 6: return gemv_fn_t<KIND, 6>();
         case 7: return gemv_fn_t<KIND, 7>();
+        case 8: return gemv_fn_t<KIND, 8>();
+        case 9: return gemv_fn_t<KIND, 9>();
     }
     return nullptr;
 }
@@ -2257,8 +2293,9 @@ hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan) {
     if (kind == K_QKV_ATT) return hipErrorInvalidValue;  // qkv_attention_plan
     const int n4 = n / 4;
     int t = 0;
-    while (t < kNumTpl && kTpl[t].nt * kTpl[t].nx < n4) ++t;
-    if (t == kNumTpl) return hipErrorInvalidValue;
+    while (t < kNumWidthTpl && kTpl[t].nt * kTpl[t].nx < n4) ++t;
+    if (t == kNumWidthTpl) return hipErrorInvalidValue;
+    t = kind_template(kind, t);
     const Tpl tp = kTpl[t];
     const int rpi = rows_per_group(t, kind);
     const int per_iter = kind == K_SWIGLU ? rpi / 2 : rpi;
