@@ -174,7 +174,14 @@ struct TiledParams {
     const float2* rope;
     const StepState* row_state;  // K_QKV: sequence b at row_state[b].pos
     size_t seq_stride;
+    float* part;           // products whose row tiles do not fill the CUs: K split over blocks,
+    size_t part_floats;    //   partial tiles here (NULL: no split; tiled_part_floats() suffice)
+    unsigned* arrive;      //   and arrival counts (tiled_arrive_count(), kept at zero between launches)
 };
+
+// workspace of the tiled products' K split on a device with `cus` compute units
+size_t tiled_part_floats(int cus);
+int tiled_arrive_count(int cus);
 
 // Pack rows x k weights into the tiled layout: kind K_PLAIN (w0), K_QKV (w0 |
 // w1 | w2 with the row segments seg1, seg2), K_SWIGLU (row 2u = w0 row u, 2u+1

@@ -1120,7 +1120,14 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
 #define LD_TILED_RT4 4
 #endif
 
-template <int NW, int RT, int D, int KIND, int NP>
+// KS > 1: K in KS parts, blocks KS g .. KS g + KS - 1 take row tiles RT g ..
+// RT g + RT - 1 over one part each (so each activation load serves RT row
+// tiles even where the row tiles do not fill the CUs).  Each stores its
+// partial tiles (coherent stores) to p.part and counts its arrival in
+// p.arrive[g]; the block that completes the count resets it, adds the KS
+// partials in part order and runs the epilogue.  No block waits for another.
+// Not with p.norm.
+template <int NW, int RT, int D, int KIND, int NP, int KS = 1>
 __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     typedef float v4 __attribute__((ext_vector_type(4)));
     constexpr int NE = RT * NP;                 // output tiles of the block
@@ -1129,11 +1136,14 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     __shared__ float ss_s[NW][NP][16];
     const int KT = p.k >> 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rt0 = blockIdx.x * RT;
+    const int grp = KS > 1 ? (int)blockIdx.x / KS : (int)blockIdx.x;
+    const int part = KS > 1 ? (int)blockIdx.x % KS : 0;
+    const int rt0 = grp * RT;
+    const int kb0 = KS > 1 ? part * KT / KS : 0, kb1 = KS > 1 ? (part + 1) * KT / KS : KT;  // k tiles of this block
     const float4* wt = reinterpret_cast<const float4*>(p.w) + lane;
     const int rtn = p.rows >> 4;
     const float4* xt = reinterpret_cast<const float4*>(p.x) + lane;  // plane jb at + jb * KT * 64
-    const int nsteps = (KT + NW - 1) / NW;  // this wave: tiles wave, wave + NW, ... below KT
+    const int nsteps = (kb1 - kb0 + NW - 1) / NW;  // this wave: tiles kb0 + wave, kb0 + wave + NW, ... below kb1
     // the residual rows this thread adds to in the epilogue are loaded now, so
     // the epilogue does not wait on them
     float4 res[EPT];
@@ -1158,9 +1168,9 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     float4 w[D][RT], xv[D][NP];
     // step kk's tiles into slot d (past the end: re-read the last tile, not used)
     auto load_one = [&](int kk, int d) {
-        const int kt = min(kk * NW + wave, KT - 1);
+        const int kt = min(kb0 + kk * NW + wave, kb1 - 1);
 #pragma unroll
-        for (int j = 0; j < RT; ++j) w[d][j] = wt[tiled_wtile(rt0 + j, kt, rtn, KT) * 64];
+        for (int j = 0; j < RT; ++j) w[d][j] = wt[tiled_wtile(min(rt0 + j, rtn - 1), kt, rtn, KT) * 64];
 #pragma unroll
         for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
     };
@@ -1169,7 +1179,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     for (int kk = 0; kk < nsteps; kk += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if ((kk + d) * NW + wave < KT) {  // wave-uniform
+            if (kb0 + (kk + d) * NW + wave < kb1) {  // wave-uniform
                 if (p.norm) {
 #pragma unroll
                     for (int jb = 0; jb < NP; ++jb) ss[jb] = dot4(xv[d][jb], xv[d][jb], ss[jb]);
@@ -1208,21 +1218,62 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
         }
     }
     __syncthreads();
+    v4 sums[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
+        sums[i] = v4{0.f, 0.f, 0.f, 0.f};
         if (t >= NE) break;
-        const int j = t / NP, jb = t % NP, b = 16 * jb + (l & 15);
-        if (b >= p.nb) continue;
         v4 sum = red[0][t][l];
 #pragma unroll
         for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][t][l];
         if (p.norm) {
             float q2 = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) q2 += ss_s[w2][jb][l & 15];
+            for (int w2 = 0; w2 < NW; ++w2) q2 += ss_s[w2][t % NP][l & 15];
             sum *= 1.0f / sqrtf(q2 / (float)p.k + p.eps);
         }
+        sums[i] = sum;
+    }
+    if constexpr (KS > 1) {
+        __shared__ int last_s;
+        float4* pt = reinterpret_cast<float4*>(p.part) + (size_t)grp * KS * NE * 64;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * NW * 64;
+            if (e >= NE * 64) break;
+            store_coherent(pt + (size_t)part * NE * 64 + e, make_float4(sums[i][0], sums[i][1], sums[i][2], sums[i][3]));
+        }
+        wait_vector_memory();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned before = atomicAdd(p.arrive + grp, 1u);
+            const int last = before + 1 == (unsigned)KS;
+            if (last) atomicExch(p.arrive + grp, 0u);
+            last_s = last;
+        }
+        __syncthreads();
+        if (!last_s) return;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * NW * 64;
+            if (e >= NE * 64) break;
+            v4 sum = v4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+                const float4 v = load_coherent(pt + (size_t)q * NE * 64 + e);
+                sum += v4{v.x, v.y, v.z, v.w};
+            }
+            sums[i] = sum;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
+        if (t >= NE) break;
+        const int j = t / NP, jb = t % NP, b = 16 * jb + (l & 15);
+        if (b >= p.nb) continue;
+        const v4 sum = sums[i];
         const int r0 = 16 * (rt0 + j) + 4 * (l >> 4);  // rows r0 .. r0 + 3 of sequence b
         if (r0 >= p.rows) continue;
         if constexpr (KIND == K_PLAIN) {
@@ -2484,6 +2535,58 @@ void tiled_go(const TiledParams& p, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((tiled_kernel<NW, RT, D, KIND, NP>), dim3(blocks), dim3(NW * 64), 0, s, p);
 }
 
+#ifndef LD_TILED_OB
+#define LD_TILED_OB 1
+#endif
+#ifndef LD_TILED_OB_NW1
+#define LD_TILED_OB_NW1 8
+#endif
+#ifndef LD_TILED_OB_D1
+#define LD_TILED_OB_D1 2
+#endif
+#ifndef LD_TILED_OB_NW2
+#define LD_TILED_OB_NW2 4
+#endif
+#ifndef LD_TILED_OB_D2
+#define LD_TILED_OB_D2 2
+#endif
+#ifndef LD_TILED_OB_NW4
+#define LD_TILED_OB_NW4 4
+#endif
+#ifndef LD_TILED_OB_D4
+#define LD_TILED_OB_D4 2
+#endif
+// K split where the row tiles do not outnumber the CUs (wo and w2; not with
+// the RMSNorm): KS row tiles per block and K in KS parts, so there are about
+// as many blocks as before and each activation load serves KS row tiles.  KS
+// is 2 for one plane and 4 for more (7B shape, 8 / 16 / 32 / 64 sequences:
+// without the split 4.64 / 4.66 / 5.49 / 8.78 ms per step, KS 2 4.59 / 4.62 /
+// 5.50 / 8.39, KS 4 4.73 / 4.76 / 5.25-5.27 / 8.40-8.41).
+#ifndef LD_TILED_KS1
+#define LD_TILED_KS1 2
+#endif
+#ifndef LD_TILED_KS
+#define LD_TILED_KS 4
+#endif
+constexpr int kTiledKsMax = 4;
+template <int KIND, int NP>
+bool tiled_split(const TiledParams& p, hipStream_t s) {
+    constexpr int KS = NP == 1 ? LD_TILED_KS1 : LD_TILED_KS, RT = KS;
+    if constexpr (KS <= 1) return false;
+    static_assert(KS <= kTiledKsMax, "workspace");
+    constexpr int NW = NP == 1 ? LD_TILED_OB_NW1 : NP == 2 ? LD_TILED_OB_NW2 : LD_TILED_OB_NW4;
+    constexpr int D = NP == 1 ? LD_TILED_OB_D1 : NP == 2 ? LD_TILED_OB_D2 : 2;
+    const int tiles = p.rows / 16, cus = cu_count();
+    const int groups = (tiles + RT - 1) / RT;
+    if (p.norm || !p.part || !p.arrive || tiles > cus || (p.k >> 4) < KS * NW) return false;
+    if ((size_t)groups * KS * RT * NP * 256 > p.part_floats || groups > tiled_arrive_count(cus)) return false;
+    hipLaunchKernelGGL((tiled_kernel<NW, RT, D, KIND, NP, KS>), dim3(groups * KS), dim3(NW * 64), 0, s, p);
+    return true;
+}
+
+size_t tiled_part_floats(int cus) { return (size_t)cus * kTiledKsMax * 4 * 256; }
+int tiled_arrive_count(int cus) { return cus; }
+
 template <int KIND, int NW, int D, int NP, int RT_MAX>
 void tiled_shape(const TiledParams& p, hipStream_t s) {
     const int tiles = p.rows / 16, cus = cu_count();
@@ -2512,6 +2615,7 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
             // 8 waves and 8 steps in flight instead of 4 and 2 (7B shape, 40 /
             // 64 sequences: 8.07 / 9.78 -> 7.72 / 9.63 ms per step; for one or
             // two planes the same change was 1-2% slower)
+            if (tiled_split<KIND, NP>(p, s)) break;
             if constexpr (NP >= 3) {
                 if (tiles <= cus) {
                     tiled_go<KIND, 8, 8, NP, 1>(p, tiles, s);
@@ -2531,8 +2635,42 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
     }
 }
 
+// One block per CU holding ceil(row tiles / CUs) row tiles (rounded up to 2,
+// 3, 4, 6 or 8; the last block's surplus tiles re-read the last tile and
+// store nothing).  Returns false where every row tile has a CU of its own.
+template <int KIND, int NW, int D, int NP>
+bool tiled_one_block(const TiledParams& p, hipStream_t s) {
+    const int tiles = p.rows / 16, cus = cu_count();
+    const int need = (tiles + cus - 1) / cus;
+    if (need <= 1) return false;
+    const int rt = need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
+    const int blocks = (tiles + rt - 1) / rt;
+    switch (rt) {
+        case 2: tiled_go<KIND, NW, D, NP, 2>(p, blocks, s); break;
+        case 3: tiled_go<KIND, NW, D, NP, 3>(p, blocks, s); break;
+        case 4: tiled_go<KIND, NW, D, NP, 4>(p, blocks, s); break;
+        case 6: tiled_go<KIND, NW, D, NP, 6>(p, blocks, s); break;
+        default: tiled_go<KIND, NW, (D < 2 ? D : 2), NP, 8>(p, blocks, s); break;
+    }
+    return true;
+}
+
 template <int KIND>
 void tiled_dispatch(const TiledParams& p, hipStream_t s) {
+#if LD_TILED_OB
+    if (p.nb <= 16) {
+        if (tiled_one_block<KIND, LD_TILED_OB_NW1, LD_TILED_OB_D1, 1>(p, s)) return;
+    } else if (kTiledBatch <= 32 || p.nb <= 32) {
+        if (tiled_one_block<KIND, LD_TILED_OB_NW2, LD_TILED_OB_D2, 2>(p, s)) return;
+    }
+#if LD_TILED_BATCH > 32
+    else if (p.nb <= 48) {
+        if (tiled_one_block<KIND, LD_TILED_OB_NW4, LD_TILED_OB_D4, 3>(p, s)) return;
+    } else {
+        if (tiled_one_block<KIND, LD_TILED_OB_NW4, LD_TILED_OB_D4, 4>(p, s)) return;
+    }
+#endif
+#endif
     if (p.nb <= 16)
         tiled_shape<KIND, LD_TILED_NW1, LD_TILED_D1, 1, 4>(p, s);
     else if (kTiledBatch <= 32 || p.nb <= 32)

@@ -211,6 +211,9 @@ struct ld_model {
     bool tiled = false;
     float *t_qkv = nullptr, *t_wo = nullptr, *t_ffn = nullptr, *t_w2 = nullptr, *t_cls = nullptr;
     float *bxt = nullptr, *bhbt = nullptr, *batt_t = nullptr;
+    float* t_part = nullptr;       // K-split partials of the tiled products (tiled_part_floats)
+    size_t t_part_floats = 0;
+    unsigned* t_arrive = nullptr;  // their arrival counts, kept at zero between launches
     hipStream_t stream = nullptr, user = nullptr;
     hipEvent_t ev_in = nullptr, ev_out = nullptr;
     hipGraph_t graph = nullptr;
@@ -776,6 +779,9 @@ int launch_batch_step_tiled(ld_model* m, int n) {
         p.nb = n;
         p.norm = norm;
         p.eps = m->opt.norm_eps;
+        p.part = m->t_part;
+        p.part_floats = m->t_part_floats;
+        p.arrive = m->t_arrive;
         return p;
     };
     HIP_TRY(embed_state_launch(m->emb, m->bstate, n, c.dim, m->bx, s, m->bxt));
@@ -1145,6 +1151,16 @@ int ld_create(const ld_config* cfg, const ld_options* opt, const void* d_weights
                     (rc = dalloc(m, &m->bhbt, (size_t)kTiledBatch * h)) ||
                     (rc = dalloc(m, &m->batt_t, (size_t)kTiledBatch * d)))
                     break;
+                int dev = 0, cus = 0;
+                e = hipGetDevice(&dev);
+                if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+                if (e != hipSuccess) { rc = fail_hip(e, "device attributes"); break; }
+                m->t_part_floats = tiled_part_floats(cus);
+                if ((rc = dalloc(m, &m->t_part, m->t_part_floats)) ||
+                    (rc = dalloc(m, &m->t_arrive, (size_t)tiled_arrive_count(cus))))
+                    break;
+                e = hipMemset(m->t_arrive, 0, sizeof(unsigned) * (size_t)tiled_arrive_count(cus));
+                if (e != hipSuccess) { rc = fail_hip(e, "hipMemset"); break; }
                 for (size_t l = 0; l < L && e == hipSuccess; ++l) {
                     e = tile_weights_launch(K_QKV, m->wq + l * d * d, m->wk + l * kv * d, m->wv + l * kv * d,
                                             cfg->dim, cfg->dim + m->kv_dim, m->rms_att + l * d,

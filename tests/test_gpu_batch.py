@@ -10,7 +10,9 @@ appended cache rows must match the oracle's, and no other sequence's rows may
 change.  Greedy generation in lockstep must reproduce each sequence's oracle
 tokens up to its first tie.  Batches of up to 4 sequences take the batch
 GEMV kernels, 5 to 64 the tiled matrix-core products (in planes of 16
-sequences: one to four), more the split-K matrix-core products.
+sequences: one to four; products with no more row tiles than compute units and
+no RMSNorm split K over blocks and merge in the last one), more the split-K
+matrix-core products.
 """
 import numpy as np
 import pytest
@@ -71,8 +73,10 @@ def install(m, cfg, caches):
                                           ("tiny", [0, 1, 2, 3, 4, 5, 6, 7, 20, 30, 40, 59]),
                                           ("gqa_small", [0, 9, 18, 27, 36, 45, 54, 63, 100, 200, 300, 400, 450, 480,
                                                          500, 507]),
-                                          # 17-32 sequences: two planes of 16
+                                          # 17-32 sequences: two planes of 16 (gqa_small: wo and w2
+                                          # with K split over blocks, 18 row tiles in groups of 4)
                                           ("tiny", [3 * i for i in range(20)]),
+                                          ("gqa_small", [(41 * i) % 500 for i in range(24)]),
                                           # 33-48: three planes; 49-64: four
                                           ("stories15m", [(37 * i) % 250 for i in range(40)]),
                                           ("tiny", [(11 * i) % 60 for i in range(48)]),
