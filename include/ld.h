@@ -64,7 +64,8 @@ typedef struct ld_config {
  * calls use sequence 0.  With max_batch > 4, and dim, hidden_dim, kv_dim and
  * vocab_size multiples of 16, ld_create also keeps a second copy of the
  * weight matrices and the classifier in device memory (about the size of the
- * blob), laid out for the matrix-core products of 5 to 64 sequences. */
+ * blob), laid out for the matrix-core products of 5 to 64 sequences, and a
+ * 4 MB workspace with one counter per compute unit for their K split. */
 typedef struct ld_options {
     float norm_eps;
     float rope_theta;

@@ -1098,18 +1098,6 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
 // per step, against 10.12 / 10.68 with the split-K products; four planes for
 // 40 as well 9.62; 8 waves 9.76-10.16 / 9.93-10.31 (3 steps 10.09, 1 step
 // 12.08); 2 waves 14.7.
-#ifndef LD_TILED_TIE
-#define LD_TILED_TIE 1
-#endif
-#ifndef LD_TILED_ONE8
-#define LD_TILED_ONE8 0
-#endif
-#ifndef LD_TILED_NWS
-#define LD_TILED_NWS 0
-#endif
-#ifndef LD_TILED_DS
-#define LD_TILED_DS 4
-#endif
 #ifndef LD_TILED_NW4
 #define LD_TILED_NW4 4
 #endif
@@ -2491,18 +2479,21 @@ hipError_t tile_weights_launch(int kind, const float* w0, const float* w1, const
     return hipGetLastError();
 }
 
-// Tiled product shapes: 8 waves (512 threads), 4 steps of loads in flight,
-// 1 to 4 row tiles per block (each activation load serves that many tiles).
-// Every block is resident at once, so the CU with the most blocks sets the
-// time: of the row-tile counts that leave at least one block per CU, the one
-// whose busiest CU is fullest is taken, the larger on a tie.  7B shapes: q/k/v
-// 256 blocks of three tiles (384 blocks of two left half the CUs with one:
-// 43.4 against 40.8 us with 768 blocks of one, and three tiles gained another
-// 1.5% of the step), w1/w3 688 of two, wo and w2 256 of one, the classifier
-// 500 of four.  Chosen on whole decode steps of 5, 8 and 16 sequences; within
-// 1%: 4 waves, 16 waves for the narrow products, 2 steps in flight; 2-7%
-// slower: 8 steps, 4 waves of one tile with 8 steps.
-constexpr int kTiledWaves = 8, kTiledSteps = 4;
+// Tiled product shapes, in this order:
+// - more row tiles than CUs (tiled_one_block): one block per CU holding
+//   ceil(row tiles / CUs) row tiles, so each activation load serves that many
+//   tiles and no CU runs two blocks (7B shape: q/k/v 256 blocks of 3 tiles,
+//   w1/w3 230 of 6, the classifier 250 of 8);
+// - otherwise, without the RMSNorm (wo and w2): K split over blocks
+//   (tiled_split);
+// - otherwise (the narrow products of small models): tiled_shape, the row
+//   tiles per block whose busiest CU is fullest.
+// Against the earlier rule (tiled_shape for every product: w1/w3 688 blocks of
+// two tiles, wo and w2 256 of one), the first two took the 7B-shaped batch
+// step of 8 / 16 / 32 / 64 sequences from 4.83 / 4.88 / 6.47 / 9.74 to 4.59 /
+// 4.62 / 5.25 / 8.39 ms.  A probe of the w1/w3 product alone at 64 sequences:
+// 171 us with 688 blocks of two tiles, 146 with 459 of three, 116 with 230 of
+// six.
 
 int cu_count() {
     static int cus = 0;
@@ -2592,23 +2583,13 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
     const int tiles = p.rows / 16, cus = cu_count();
     int rt = 1, best = tiled_balance(tiles, cus);
     for (int r = 2; r <= RT_MAX; ++r)
-        if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) + LD_TILED_TIE >= best + 1) {
+        if (tiles % r == 0 && tiles / r >= cus && tiled_balance(tiles / r, cus) >= best) {
             rt = r;
             best = tiled_balance(tiles / r, cus);
         }
     switch (rt) {
         case 4: if constexpr (RT_MAX >= 4) tiled_go<KIND, NW, D, NP, 4>(p, tiles / 4, s); break;
-        case 3:
-            if constexpr (RT_MAX >= 3) {
-#if LD_TILED_ONE8
-                if (NP >= 3 && tiles / 3 <= cus) {
-                    tiled_go<KIND, 8, LD_TILED_ONE8, NP, 3>(p, tiles / 3, s);
-                    break;
-                }
-#endif
-                tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s);
-            }
-            break;
+        case 3: if constexpr (RT_MAX >= 3) tiled_go<KIND, NW, D, NP, 3>(p, tiles / 3, s); break;
         case 2: tiled_go<KIND, NW, D, NP, 2>(p, tiles / 2, s); break;
         default:
             // three or four planes with one block per CU at most (wo and w2):
@@ -2622,14 +2603,6 @@ void tiled_shape(const TiledParams& p, hipStream_t s) {
                     break;
                 }
             }
-#if LD_TILED_NWS
-            if constexpr (NP <= 2) {
-                if (tiles <= cus) {
-                    tiled_go<KIND, LD_TILED_NWS, LD_TILED_DS, NP, 1>(p, tiles, s);
-                    break;
-                }
-            }
-#endif
             tiled_go<KIND, NW, D, NP, 1>(p, tiles, s);
             break;
     }
