@@ -1126,10 +1126,12 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = KS > 1 ? (int)blockIdx.x / KS : (int)blockIdx.x;
     const int part = KS > 1 ? (int)blockIdx.x % KS : 0;
-    const int rt0 = grp * RT;
+    // row tiles rt0 .. rt0 + cnt - 1; the last block's surplus tiles (j >=
+    // cnt) re-read its first tile, which stays in the cache, and store nothing
+    const int rtn = p.rows >> 4;
+    const int rt0 = grp * RT, cnt = min(RT, rtn - rt0);
     const int kb0 = KS > 1 ? part * KT / KS : 0, kb1 = KS > 1 ? (part + 1) * KT / KS : KT;  // k tiles of this block
     const float4* wt = reinterpret_cast<const float4*>(p.w) + lane;
-    const int rtn = p.rows >> 4;
     const float4* xt = reinterpret_cast<const float4*>(p.x) + lane;  // plane jb at + jb * KT * 64
     const int nsteps = (kb1 - kb0 + NW - 1) / NW;  // this wave: tiles kb0 + wave, kb0 + wave + NW, ... below kb1
     // the residual rows this thread adds to in the epilogue are loaded now, so
@@ -1141,7 +1143,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
         if constexpr (KIND == K_RESID) {
             const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
             const int b = 16 * (t % NP) + (l & 15), r0 = 16 * (rt0 + t / NP) + 4 * (l >> 4);
-            if (t < NE && b < p.nb && r0 < p.rows) res[i] = *reinterpret_cast<const float4*>(p.x_resid + (size_t)b * p.ldr + r0);
+            if (t < NE && t / NP < cnt && b < p.nb && r0 < p.rows) res[i] = *reinterpret_cast<const float4*>(p.x_resid + (size_t)b * p.ldr + r0);
         }
     }
 
@@ -1158,7 +1160,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
     auto load_one = [&](int kk, int d) {
         const int kt = min(kb0 + kk * NW + wave, kb1 - 1);
 #pragma unroll
-        for (int j = 0; j < RT; ++j) w[d][j] = wt[tiled_wtile(min(rt0 + j, rtn - 1), kt, rtn, KT) * 64];
+        for (int j = 0; j < RT; ++j) w[d][j] = wt[tiled_wtile(rt0 + (j < cnt ? j : 0), j < cnt ? kt : kb0, rtn, KT) * 64];
 #pragma unroll
         for (int jb = 0; jb < NP; ++jb) xv[d][jb] = xt[((size_t)jb * KT + kt) * 64];
     };
@@ -1260,7 +1262,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(TiledParams p) {
         const int e = threadIdx.x + i * NW * 64, t = e >> 6, l = e & 63;
         if (t >= NE) break;
         const int j = t / NP, jb = t % NP, b = 16 * jb + (l & 15);
-        if (b >= p.nb) continue;
+        if (b >= p.nb || j >= cnt) continue;
         const v4 sum = sums[i];
         const int r0 = 16 * (rt0 + j) + 4 * (l >> 4);  // rows r0 .. r0 + 3 of sequence b
         if (r0 >= p.rows) continue;
@@ -2565,6 +2567,7 @@ bool tiled_split(const TiledParams& p, hipStream_t s) {
     constexpr int KS = NP == 1 ? LD_TILED_KS1 : LD_TILED_KS, RT = KS;
     if constexpr (KS <= 1) return false;
     static_assert(KS <= kTiledKsMax, "workspace");
+    // (three or four planes: 8 waves 3-5% slower, 3 steps in flight 0.5%)
     constexpr int NW = NP == 1 ? LD_TILED_OB_NW1 : NP == 2 ? LD_TILED_OB_NW2 : LD_TILED_OB_NW4;
     constexpr int D = NP == 1 ? LD_TILED_OB_D1 : NP == 2 ? LD_TILED_OB_D2 : 2;
     const int tiles = p.rows / 16, cus = cu_count();
@@ -2617,6 +2620,8 @@ bool tiled_one_block(const TiledParams& p, hipStream_t s) {
     const int need = (tiles + cus - 1) / cus;
     if (need <= 1) return false;
     const int rt = need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
+    // (a block on every CU instead, the row tiles shared out evenly, need or
+    // need - 1 per block, was 1.5-2% slower for one plane, 0-2% for more)
     const int blocks = (tiles + rt - 1) / rt;
     switch (rt) {
         case 2: tiled_go<KIND, NW, D, NP, 2>(p, blocks, s); break;
