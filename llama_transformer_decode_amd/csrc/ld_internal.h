@@ -68,6 +68,7 @@ struct GemvPlan {
     int units;
     int grid;
     int nb;                // 0: one vector; else the batch kernel for up to nb vectors
+    int grid_nb[2];        // batch: the grids of its instances for 1 and 2 vectors (grid: nb)
 };
 
 struct GemvParams {
@@ -144,8 +145,10 @@ struct AttnParams {
 // Batch decode of up to kTiledBatch sequences on the matrix cores with
 // pre-tiled weights (tiled_launch).  Tiled weights: a product's rows and K
 // (both multiples of 16) form 16 x 16 tiles; tile (rt, kt) is 64 float4 at
-// float4 offset (rt * K/16 + kt) * 64, float4 l holding row 16 rt + l % 16 at
-// k = 16 kt + 4 (l / 16) + 0..3, times the gain of the product's RMSNorm at k.
+// float4 offset tiled_wtile(rt, kt, rows / 16, K / 16) * 64 (groups of 8 k
+// tiles, row tile after row tile within a group), float4 l holding row
+// 16 rt + l % 16 at k = 16 kt + 4 (l / 16) + 0..3, times the gain of the
+// product's RMSNorm at k.
 // Tiled activations (vectors of n floats, planes of 16 sequences): float4
 // ((plane * n/16 + kt) * 64 + l) = x[16 plane + l % 16][16 kt + 4 (l / 16) + 0..3].
 #ifndef LD_TILED_BATCH

@@ -2243,31 +2243,39 @@ constexpr int rows_per_group_b(int t, int kind) {
     return (kind == K_QKV || kind == K_SWIGLU) && kTplB[t].rpi < 2 ? 2 : kTplB[t].rpi;
 }
 
-template <int KIND, int T>
+// Instances for 1, 2 and kGemvBatch vectors: a batch of one or two
+// sequences does not pay for the registers and products of four.
+template <int KIND, int T, int NB>
 GemvFn gemv_batch_fn_t() {
-    return gemv_batch_kernel<kTplB[T].nt, kTplB[T].nx, rows_per_group_b(T, KIND), KIND, kGemvBatch>;
+    return gemv_batch_kernel<kTplB[T].nt, kTplB[T].nx, rows_per_group_b(T, KIND), KIND, NB>;
 }
 
-template <int KIND>
+template <int KIND, int NB>
 GemvFn gemv_batch_fn(int t) {
     switch (t) {
-        case 0: return gemv_batch_fn_t<KIND, 0>();
-        case 1: return gemv_batch_fn_t<KIND, 1>();
-        case 2: return gemv_batch_fn_t<KIND, 2>();
-        case 3: return gemv_batch_fn_t<KIND, 3>();
-        case 4: return gemv_batch_fn_t<KIND, 4>();
+        case 0: return gemv_batch_fn_t<KIND, 0, NB>();
+        case 1: return gemv_batch_fn_t<KIND, 1, NB>();
+        case 2: return gemv_batch_fn_t<KIND, 2, NB>();
+        case 3: return gemv_batch_fn_t<KIND, 3, NB>();
+        case 4: return gemv_batch_fn_t<KIND, 4, NB>();
     }
     return nullptr;
 }
 
-GemvFn gemv_batch_fn_kind(int kind, int t) {
+template <int NB>
+GemvFn gemv_batch_fn_nb(int kind, int t) {
     switch (kind) {
-        case K_PLAIN: return gemv_batch_fn<K_PLAIN>(t);
-        case K_RESID: return gemv_batch_fn<K_RESID>(t);
-        case K_QKV: return gemv_batch_fn<K_QKV>(t);
-        case K_SWIGLU: return gemv_batch_fn<K_SWIGLU>(t);
+        case K_PLAIN: return gemv_batch_fn<K_PLAIN, NB>(t);
+        case K_RESID: return gemv_batch_fn<K_RESID, NB>(t);
+        case K_QKV: return gemv_batch_fn<K_QKV, NB>(t);
+        case K_SWIGLU: return gemv_batch_fn<K_SWIGLU, NB>(t);
     }
     return nullptr;
+}
+
+// nb: the batch's vectors (1, 2, or up to kGemvBatch)
+GemvFn gemv_batch_fn_kind(int kind, int t, int nb = kGemvBatch) {
+    return nb <= 1 ? gemv_batch_fn_nb<1>(kind, t) : nb <= 2 ? gemv_batch_fn_nb<2>(kind, t) : gemv_batch_fn_nb<kGemvBatch>(kind, t);
 }
 
 // The fused q/k/v + attention kernels: GEMV shapes up to n = 4096 (kTpl[0..3]),
@@ -2385,15 +2393,24 @@ hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_batch_fn_kind(kind, t), tp.nt, 0);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    const int slots = cus * occ;
-    if (plan->units <= slots) {
-        plan->grid = plan->units;
-    } else {
-        const int even = divisor_in(plan->units, (slots + 1) / 2, slots);
-        plan->grid = even ? even : slots;
+    // one grid per instance (kGemvBatch, 1 and 2 vectors): each fills its own slots
+    for (int i = 0; i < 3; ++i) {
+        const int nbi = i == 0 ? kGemvBatch : i;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemv_batch_fn_kind(kind, t, nbi), tp.nt, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+        const int slots = cus * occ;
+        int grid;
+        if (plan->units <= slots) {
+            grid = plan->units;
+        } else {
+            const int even = divisor_in(plan->units, (slots + 1) / 2, slots);
+            grid = even ? even : slots;
+        }
+        if (i == 0)
+            plan->grid = grid;
+        else
+            plan->grid_nb[i - 1] = grid;
     }
     return hipSuccess;
 }
@@ -2696,7 +2713,8 @@ hipError_t gemv_launch(const GemvPlan& plan, const GemvParams& p0, hipStream_t s
     p.units = plan.units;
     if (plan.nb) {
         if (p.nb < 1 || p.nb > plan.nb) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(gemv_batch_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, p);
+        const int grid = p.nb <= 2 && plan.grid_nb[p.nb - 1] > 0 ? plan.grid_nb[p.nb - 1] : plan.grid;
+        hipLaunchKernelGGL(gemv_batch_fn_kind(plan.kind, t, p.nb), dim3(grid), dim3(plan.nt), 0, s, p);
     } else if (start || stop) {
         // events taken by the dispatch itself: they bracket the kernel's execution
         hipExtLaunchKernelGGL(gemv_fn_kind(plan.kind, t), dim3(plan.grid), dim3(plan.nt), 0, s, start, stop, 0, p);

@@ -68,6 +68,8 @@ def install(m, cfg, caches):
 
 @pytest.mark.parametrize("graph", [True, False])
 @pytest.mark.parametrize("name,lengths", [("tiny", [0, 5, 17, 40]), ("tiny", [60, 0, 59]),
+                                          # one and two sequences: the batch GEMV's 1- and 2-vector instances
+                                          ("stories15m", [37]), ("gqa_small", [5, 300]),
                                           ("stories15m", [3, 0, 100, 31, 64]), ("gqa_small", [200, 7, 0, 508]),
                                           # 5..16 sequences: the tiled matrix-core products
                                           ("tiny", [0, 1, 2, 3, 4, 5, 6, 7, 20, 30, 40, 59]),
@@ -100,6 +102,8 @@ def test_batch_steps_at_mixed_positions(name, lengths, graph):
                 ok, err, tol = logits_close(got[b], ref)
                 assert ok, (s, b, err, tol)
         k, v = (host(t) for t in m.read_kv_cache())
+    if B == 1:  # a one-sequence model's caches have no batch axis
+        k, v = k[None], v[None]
     for b in range(B):
         n = lengths[b] + 4
         for g, r in ((k[b], caches[b].k), (v[b], caches[b].v)):
