@@ -113,6 +113,29 @@ def test_batch_steps_at_mixed_positions(name, lengths, graph):
             assert np.all(g[:, n:] == 0)
 
 
+@pytest.mark.parametrize("hidden,B", [(5120, 24), (5120, 64), (11008, 20), (11008, 50)])
+def test_batch_step_with_wide_products(hidden, B):
+    # products with more row tiles than compute units take one block per CU of
+    # ceil(row tiles / CUs) row tiles (the 7B shape's q/k/v, w1/w3 and
+    # classifier); a one-layer model with dim 256 and a wide hidden layer puts
+    # w1/w3 there with 3 (hidden 5120) and 6 (hidden 11008) row tiles per
+    # block, the classifier with 8, at two to four planes of 16 sequences,
+    # beside the K split of wo and w2
+    cfg = synth.Config(f"wide{hidden}", 256, hidden, 1, 4, 4, 32000, 64, 0, 1011)
+    blob = synth.make_blob(cfg)
+    lengths = [(7 * b) % 60 for b in range(B)]
+    caches = prefixes(cfg, lengths, 800)
+    toks = synth.prefill_tokens(cfg, B)
+    with pkg.Model(cfg, dev(blob), max_batch=B) as m:
+        install(m, cfg, caches)
+        got = host(m.forward_batch(toks, lengths))
+    assert got.shape == (B, cfg.vocab_size)
+    for b in range(B):
+        ref = oracle.forward(cfg, blob, caches[b], int(toks[b]), lengths[b])
+        ok, err, tol = logits_close(got[b], ref)
+        assert ok, (b, err, tol)
+
+
 @pytest.mark.parametrize("name,B", [("tiny", 2), ("stories15m", 8), ("gqa_small", 33)])
 def test_greedy_generation_in_lockstep(name, B):
     cfg, blob, w = blob_of(name)
