@@ -481,6 +481,24 @@ def main() -> int:
                "seconds_per_step": per_step,
                "GBps": round(sum(bytes_per_token(cfg, p) for p in cpu_pos) / dt / 1e9, 2),
                "host_cores_available": os.cpu_count(), "pinned_core": min(allowed), "cpu_model": cpu_model}
+        # the same sample with the rows of every matrix-vector product (and the
+        # heads of every attention call) shared out over the host's cores in
+        # contiguous ranges, the row-parallel matmul of the "run.c" page; the
+        # results are bit-identical to one thread's
+        n_thr = max(1, min(len(allowed), 16))
+        oracle.set_threads(n_thr)
+        try:
+            per_mt = {}
+            for p in cpu_pos:
+                t0 = time.perf_counter()
+                oracle.forward(cfg, blob, cache, 1, p)
+                per_mt[str(p)] = time.perf_counter() - t0
+        finally:
+            oracle.set_threads(1)
+        dt_mt = sum(per_mt.values())
+        cpu["all_cores"] = {"value": round(n_cpu / dt_mt, 5), "unit": "tokens/s", "cores": n_thr,
+                            "seconds_per_step": {k: float(f"{v:.4g}") for k, v in per_mt.items()},
+                            "GBps": round(sum(bytes_per_token(cfg, p) for p in cpu_pos) / dt_mt / 1e9, 2)}
 
     # ---- the long-context workload: the 70B-layer model, decode from 3584 to 4095 ----
     long_ctx = None
