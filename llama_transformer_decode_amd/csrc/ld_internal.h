@@ -264,7 +264,8 @@ hipError_t attn_prefill_launch(int head_size, const AttnPrefillParams& p, hipStr
 // shape outside the compiled kernels.
 hipError_t gemv_plan(int kind, int rows, int n, GemvPlan* plan);
 // the batch kernel for up to kGemvBatch vectors (hipErrorInvalidValue when n
-// is beyond its shapes); K_PLAIN, K_RESID, K_QKV, K_SWIGLU
+// is beyond its shapes); K_PLAIN, K_RESID, K_QKV, K_SWIGLU.  gemv_launch
+// takes its instance for 1, 2 or kGemvBatch vectors by GemvParams.nb.
 constexpr int kGemvBatch = 4;
 hipError_t gemv_plan_batch(int kind, int rows, int n, GemvPlan* plan);
 // start / stop (optional): events recorded by the kernel's own dispatch, so that

@@ -1008,10 +1008,11 @@ __global__ __launch_bounds__(NT) void gemv_batch_kernel(GemvParams p) {
 // four v_mfma_f32_16x16x4f32 steps as the A operand (rows 16 rt + l % 16, k
 // 16 kt + 4 (l / 16) + t at step t), with the tiled activations as the B
 // operand (sequence l % 16 at the same k).  Weights stream once for the whole
-// batch without an LDS stage.  A block takes RT row tiles over all of K: its
-// NW waves take the k tiles round robin (wave w: tiles w, w + NW, ..., so the
-// block reads NW consecutive tiles per step), then add their partial tiles
-// through LDS in wave order.  The output lane l holds rows 16 rt + 4 (l / 16)
+// batch without an LDS stage.  A block takes RT row tiles over all of K (or,
+// with the K split, over one of KS parts of K): its NW waves take the k tiles
+// round robin (wave w: tiles w, w + NW, ..., so the block reads NW
+// consecutive tiles per step), then add their partial tiles through LDS in
+// wave order.  The output lane l holds rows 16 rt + 4 (l / 16)
 // + 0..3 of sequence l % 16: RoPE pairs and SwiGLU (w1, w3) pairs sit in one
 // lane.  RMSNorm: the gain is folded into the tiled weights, and each
 // sequence's sum of squares is accumulated from the same activations, so the
@@ -1076,8 +1077,11 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(int kind, const float
     }
 }
 
-// waves per block and steps of tiles in flight: one plane (up to 16
-// sequences), two planes (17-32).  7B shape, 8 / 16 / 32 sequences: 8 waves
+// Shapes of tiled_shape (the products that take neither the one-block shapes
+// nor the K split: row tiles no more than CUs, with the RMSNorm; the figures
+// below were measured when every product took tiled_shape).  Waves per block
+// and steps of tiles in flight: one plane (up to 16 sequences), two planes
+// (17-32).  7B shape, 8 / 16 / 32 sequences: 8 waves
 // and 4 steps 5.05 / 5.07 / 6.47 ms per step; 3 steps 5.05 / 5.08 / 6.44-6.47;
 // 6 steps 5.16 / 5.20 / 6.72; 8 steps (one plane) 5.18 / 5.23; 4 waves
 // 5.44 / 5.49 / 6.70.
