@@ -113,15 +113,16 @@ def test_batch_steps_at_mixed_positions(name, lengths, graph):
             assert np.all(g[:, n:] == 0)
 
 
-@pytest.mark.parametrize("hidden,B", [(5120, 24), (5120, 64), (11008, 20), (11008, 50)])
-def test_batch_step_with_wide_products(hidden, B):
+@pytest.mark.parametrize("dim,heads,hidden,B", [(256, 4, 5120, 24), (256, 4, 5120, 64), (256, 4, 11008, 20),
+                                                (256, 4, 11008, 50), (3072, 24, 1024, 20), (3072, 24, 1024, 64)])
+def test_batch_step_with_wide_products(dim, heads, hidden, B):
     # products with more row tiles than compute units take one block per CU of
     # ceil(row tiles / CUs) row tiles (the 7B shape's q/k/v, w1/w3 and
-    # classifier); a one-layer model with dim 256 and a wide hidden layer puts
-    # w1/w3 there with 3 (hidden 5120) and 6 (hidden 11008) row tiles per
-    # block, the classifier with 8, at two to four planes of 16 sequences,
-    # beside the K split of wo and w2
-    cfg = synth.Config(f"wide{hidden}", 256, hidden, 1, 4, 4, 32000, 64, 0, 1011)
+    # classifier); one-layer models put w1/w3 there with 3 (dim 256, hidden
+    # 5120) and 6 (hidden 11008) row tiles per block, the q/k/v product with 3
+    # (dim 3072: 576 row tiles), the classifier with 8, at two to four planes
+    # of 16 sequences, beside the K split of wo and w2
+    cfg = synth.Config(f"wide{dim}x{hidden}", dim, hidden, 1, heads, heads, 32000, 64, 0, 1011)
     blob = synth.make_blob(cfg)
     lengths = [(7 * b) % 60 for b in range(B)]
     caches = prefixes(cfg, lengths, 800)
